@@ -1,0 +1,436 @@
+"""Plain, slow fp64 CPU oracle for OAL causal attention -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this module.  It shares no code with the HIP path and imports nothing from it.
+
+Sources (cited by title and section/equation, never by file position):
+  [OAL]     "Not All Dimensions Are Equal: Outlier-Aware Attention Linearization
+            with Grouped Quadratic Kernels" (arXiv 2610.13674).
+  [Slides]  the research discussion deck on the same paper.
+  [ReBased] "Linear Transformers with Learnable Kernel Functions" (blog post).
+
+What is computed (restated, not quoted):
+  For a query head h reading KV head h // (Hq/Hkv), a query q and key k:
+    x_r   = q_r k_r / sqrt(d_h)                          [OAL] sec. 4.1
+    s_g   = sum of x_r over the dimensions r of group g   [OAL] sec. 4.2
+    kappa = a + sum_g b_g s_g + sum_{g,h} c_gh s_g s_h    grouped form of the
+            dimension-aware kernel ([Slides] "Relax sharing ...", Eq. (3)) with
+            b_r = b_g(r) and C_rt = c_g(r)g(t) ([Slides] "A squared quadratic
+            form guarantees positive weights").
+  Causal normalised output ([OAL] sec. 2, linear attention; causal pair set of
+  Eq. (2) includes j = i):
+    y_i = sum_{j<=i} kappa(q_i,k_j) v_j / sum_{j<=i} kappa(q_i,k_j)
+
+Forms provided:
+  * ``attention_direct``: the definition above, O(N^2) per head (the direct
+    pairwise evaluation of [OAL] sec. 4.4).  This is the reference.
+  * ``attention_recurrent_packed``: prefix states of [OAL] Eq. (5) stored
+    symmetric-packed ([OAL] App. D, "Exact state and parameter counts") and
+    read out with Eq. (6).
+  * ``attention_recurrent_ordered``: the same with ordered-pair states (full
+    d_h x d_h second moment), Eq. (5)-(6) literally.
+  * ``chi_bruteforce`` / ``chi_separable``: the contribution score of Eq. (2).
+
+Readings of the pages (listed with reasons in the design notes):
+  * The score is scaled by 1/sqrt(d_h) everywhere; the Based polynomial
+    1 + t + t^2/2 of [ReBased] is the G = 1 case evaluated at s = t.
+  * ReBased's norm(x) is LayerNorm over d_h without its own affine, biased
+    variance, epsilon 1e-5, followed by ReBased's gamma/beta.
+  * Packed feature order (also the library's state layout): feature 0 is the
+    constant, feature 1 + r the linear term r, then the pairs r <= t in
+    row-major upper-triangle order.  The state keeps raw Eq. (5) moments;
+    multiplicity 2 for r < t and the coefficients belong to the query side.
+
+Parity pins: see tests/test_oracle_pins.py.  Every public function here is
+pinned by at least one check that does not reuse this module's arithmetic.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "coeffs_from_factor",
+    "premap",
+    "group_scores",
+    "kappa_from_scores",
+    "kappa",
+    "attention_direct",
+    "feature_count",
+    "packed_pairs",
+    "phi_k_packed",
+    "phi_q_packed",
+    "attention_recurrent_packed",
+    "attention_recurrent_ordered",
+    "state_from_prefix",
+    "decode_step",
+    "chi_bruteforce",
+    "chi_separable",
+    "abi_state_from_matrix",
+    "matrix_from_abi_state",
+]
+
+
+# --------------------------------------------------------------------------
+# coefficients
+# --------------------------------------------------------------------------
+
+def coeffs_from_factor(eps, L):
+    """(epsilon, L) -> (a, b_g, c_gh) for the positive group-aware kernel.
+
+    [OAL] sec. 4.3, Eq. (7): kappa = eps + sbar^T L L^T sbar with
+    sbar = [1, s_1..s_G]; [Slides] "A squared quadratic form guarantees
+    positive weights": with M = L L^T, a = eps + M_00, b_g = 2 M_0g and
+    c_gh = M_gh.  ``L`` is [H, G+1, G+1] (or [G+1, G+1]).
+    """
+    L = np.asarray(L, dtype=np.float64)
+    single = L.ndim == 2
+    if single:
+        L = L[None]
+    M = np.matmul(L, np.transpose(L, (0, 2, 1)))
+    a = eps + M[:, 0, 0]
+    b = 2.0 * M[:, 0, 1:]
+    c = M[:, 1:, 1:].copy()
+    if single:
+        return a[0], b[0], c[0]
+    return a, b, c
+
+
+# --------------------------------------------------------------------------
+# kernel evaluation
+# --------------------------------------------------------------------------
+
+def premap(x, gamma, beta, ln_eps=1e-5):
+    """ReBased pre-map gamma * norm(x) + beta along the last axis.
+
+    [ReBased] section "Let training place the parabola": the feature map is
+    (gamma * norm(x) + beta) squared elementwise; this returns the part inside
+    the square.  norm is LayerNorm (mean and biased variance over d_h).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return np.asarray(gamma, np.float64) * (x - mu) / np.sqrt(var + ln_eps) + np.asarray(beta, np.float64)
+
+
+def group_scores(q, k, group_of_dim, n_groups):
+    """Group-restricted scaled dot products s_g for all (query, key) pairs.
+
+    [OAL] sec. 4.2: s_g is the sum over r in group g of q_r k_r / sqrt(d_h).
+    q: [n, d], k: [m, d] -> [G, n, m].
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    d = q.shape[-1]
+    g = np.asarray(group_of_dim)
+    out = np.zeros((n_groups, q.shape[0], k.shape[0]))
+    for gi in range(n_groups):
+        dims = np.nonzero(g == gi)[0]
+        if dims.size:
+            out[gi] = (q[:, dims] @ k[:, dims].T) / math.sqrt(d)
+    return out
+
+
+def kappa_from_scores(s, a, b, c):
+    """kappa = a + sum_g b_g s_g + sum_g sum_h c_gh s_g s_h for score stacks s [G, ...]."""
+    G = s.shape[0]
+    out = np.full(s.shape[1:], float(a))
+    for g in range(G):
+        out = out + float(b[g]) * s[g]
+    for g in range(G):
+        for h in range(G):
+            out = out + float(c[g][h]) * s[g] * s[h]
+    return out
+
+
+def kappa(q, k, group_of_dim, a, b, c):
+    """Kernel value for one query/key pair (vectors of length d_h)."""
+    s = group_scores(np.atleast_2d(q), np.atleast_2d(k), group_of_dim, len(b))
+    return float(kappa_from_scores(s, a, b, c)[0, 0])
+
+
+def _kv_head(h, n_q_heads, n_kv_heads):
+    # query heads share KV heads in consecutive blocks (GQA, [OAL] App. B)
+    return h // (n_q_heads // n_kv_heads)
+
+
+def attention_direct(Q, K, V, group_of_dim, a, b, c, premap_params=None, rows=None,
+                     return_parts=False):
+    """Causal normalised OAL attention by the O(N^2) definition.
+
+    Q: [B, Hq, N, d]; K: [B, Hkv, N, d]; V: [B, Hkv, N, dv]; group_of_dim:
+    [Hq, d]; a: [Hq]; b: [Hq, G]; c: [Hq, G, G]; premap_params: None or the
+    ReBased affine {"gamma_q", "beta_q", "gamma_k", "beta_k", "ln_eps"}.
+    ``rows``: optional sorted array of output positions (0-based) to evaluate;
+    each y_i is computed from its own definition, so any subset is exact.
+    Returns y [B, Hq, R, dv] (and num [.., dv], den [..] if return_parts).
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    dv = V.shape[-1]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    R = rows.size
+    y = np.zeros((B, Hq, R, dv))
+    num = np.zeros((B, Hq, R, dv))
+    den = np.zeros((B, Hq, R))
+    causal = (np.arange(N)[None, :] <= rows[:, None])  # j <= i, [R, N]
+    for bi in range(B):
+        for h in range(Hq):
+            kh = _kv_head(h, Hq, Hkv)
+            q = Q[bi, h, rows]
+            k = K[bi, kh]
+            if premap_params is not None:
+                p = premap_params
+                q = premap(q, p["gamma_q"][h], p["beta_q"][h], p["ln_eps"])
+                k = premap(k, p["gamma_k"][kh], p["beta_k"][kh], p["ln_eps"])
+            G = len(b[h])
+            s = group_scores(q, k, group_of_dim[h], G)
+            w = kappa_from_scores(s, a[h], b[h], c[h]) * causal
+            num[bi, h] = w @ V[bi, kh]
+            den[bi, h] = w.sum(axis=1)
+            y[bi, h] = num[bi, h] / den[bi, h][:, None]
+    if return_parts:
+        return y, num, den
+    return y
+
+
+# --------------------------------------------------------------------------
+# feature-space (HD state) forms
+# --------------------------------------------------------------------------
+
+def feature_count(d):
+    """Packed feature count 1 + d + d(d+1)/2 ([OAL] App. D)."""
+    return 1 + d + d * (d + 1) // 2
+
+
+def packed_pairs(d):
+    """List of (r, t), r <= t, in row-major upper-triangle order."""
+    return [(r, t) for r in range(d) for t in range(r, d)]
+
+
+def phi_k_packed(k):
+    """Key features [1, k_r, k_r k_t (r <= t)] ([OAL] Eq. (5) moments, packed)."""
+    k = np.asarray(k, np.float64)
+    d = k.shape[-1]
+    f = [np.ones(k.shape[:-1])]
+    f += [k[..., r] for r in range(d)]
+    f += [k[..., r] * k[..., t] for (r, t) in packed_pairs(d)]
+    return np.stack(f, axis=-1)
+
+
+def phi_q_packed(q, group_of_dim, a, b, c):
+    """Query features carrying the coefficients of [OAL] Eq. (6).
+
+    [a, b_g(r) q_r / sqrt(d), m_rt c_g(r)g(t) q_r q_t / d] with multiplicity
+    m_rt = 1 on the diagonal and 2 off it ([OAL] App. D, packed readout).
+    """
+    q = np.asarray(q, np.float64)
+    d = q.shape[-1]
+    g = np.asarray(group_of_dim)
+    sd = math.sqrt(d)
+    f = [np.full(q.shape[:-1], float(a))]
+    f += [float(b[g[r]]) * q[..., r] / sd for r in range(d)]
+    for (r, t) in packed_pairs(d):
+        m = 1.0 if r == t else 2.0
+        f.append(m * float(c[g[r]][g[t]]) * q[..., r] * q[..., t] / d)
+    return np.stack(f, axis=-1)
+
+
+def attention_recurrent_packed(Q, K, V, group_of_dim, a, b, c, premap_params=None,
+                               state_in=None, return_state=False):
+    """Causal attention through packed prefix states, token by token.
+
+    State per (batch, KV head): S [D, dv+1] = sum_j phi_k(k_j) [v_j, 1]^T
+    ([OAL] Eq. (5) with u_j = [v_j; 1]); readout u~_i = phi_q(q_i)^T S_i and
+    y_i = u~_i[:dv] / u~_i[dv] ([OAL] Eq. (6)).  ``state_in``: [B, Hkv, D, dv+1]
+    initial states (zeros if None).
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    dv = V.shape[-1]
+    D = feature_count(d)
+    S = np.zeros((B, Hkv, D, dv + 1)) if state_in is None else np.array(state_in, np.float64)
+    y = np.zeros((B, Hq, N, dv))
+    for bi in range(B):
+        for kh in range(Hkv):
+            heads = [h for h in range(Hq) if _kv_head(h, Hq, Hkv) == kh]
+            k = K[bi, kh]
+            if premap_params is not None:
+                p = premap_params
+                k = premap(k, p["gamma_k"][kh], p["beta_k"][kh], p["ln_eps"])
+            fk = phi_k_packed(k)
+            fq = {}
+            for h in heads:
+                q = Q[bi, h]
+                if premap_params is not None:
+                    q = premap(q, premap_params["gamma_q"][h], premap_params["beta_q"][h],
+                               premap_params["ln_eps"])
+                fq[h] = phi_q_packed(q, group_of_dim[h], a[h], b[h], c[h])
+            st = S[bi, kh]
+            for i in range(N):
+                u = np.concatenate([V[bi, kh, i], [1.0]])
+                st += np.outer(fk[i], u)
+                for h in heads:
+                    ut = fq[h][i] @ st
+                    y[bi, h, i] = ut[:dv] / ut[dv]
+    if return_state:
+        return y, S
+    return y
+
+
+def attention_recurrent_ordered(Q, K, V, group_of_dim, a, b, c):
+    """Eq. (5)-(6) of [OAL] with ordered-pair states (no packing).
+
+    H0 = sum u_j, H1_r = sum k_jr u_j, H2_rt = sum k_jr k_jt u_j over j <= i;
+    u~_i = a H0 + (1/sqrt d) sum_r b_r q_r H1_r + (1/d) sum_{r,t} C_rt q_r q_t H2_rt
+    with b_r = b_g(r), C_rt = c_g(r)g(t).
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    dv = V.shape[-1]
+    y = np.zeros((B, Hq, N, dv))
+    for bi in range(B):
+        for h in range(Hq):
+            kh = _kv_head(h, Hq, Hkv)
+            g = np.asarray(group_of_dim[h])
+            br = np.array([b[h][g[r]] for r in range(d)], dtype=np.float64)
+            C = np.array([[c[h][g[r]][g[t]] for t in range(d)] for r in range(d)], dtype=np.float64)
+            H0 = np.zeros(dv + 1)
+            H1 = np.zeros((d, dv + 1))
+            H2 = np.zeros((d, d, dv + 1))
+            for i in range(N):
+                kk = K[bi, kh, i]
+                u = np.concatenate([V[bi, kh, i], [1.0]])
+                H0 += u
+                H1 += np.outer(kk, u)
+                H2 += np.einsum("r,t,l->rtl", kk, kk, u)
+                q = Q[bi, h, i]
+                ut = a[h] * H0
+                ut = ut + np.einsum("r,rl->l", br * q, H1) / math.sqrt(d)
+                ut = ut + np.einsum("rt,r,t,rtl->l", C, q, q, H2) / d
+                y[bi, h, i] = ut[:dv] / ut[dv]
+    return y
+
+
+def state_from_prefix(K, V, premap_k=None, ln_eps=1e-5):
+    """Packed state sum_j phi_k(k_j) [v_j, 1]^T of one (sequence, KV head).
+
+    K: [n, d], V: [n, dv]; premap_k: optional (gamma_k, beta_k) for the
+    ReBased pre-map.  Returns [D, dv+1].
+    """
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    if premap_k is not None:
+        K = premap(K, premap_k[0], premap_k[1], ln_eps)
+    fk = phi_k_packed(K)
+    U = np.concatenate([V, np.ones((V.shape[0], 1))], axis=1)
+    return fk.T @ U
+
+
+def decode_step(state, q, k, v, group_of_dim, a, b, c, n_q_heads, premap_params=None):
+    """One recurrent decode step ([OAL] Eq. (5)-(6) for a single new token).
+
+    state: [S, Hkv, D, dv+1] (fp64, updated copy returned); q: [S, Hq, d];
+    k: [S, Hkv, d]; v: [S, Hkv, dv].  The new token is part of its own causal
+    prefix (j <= i), so the state is updated before the readout.
+    Returns (y [S, Hq, dv], new_state).
+    """
+    st = np.array(state, np.float64)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    S, Hkv = k.shape[0], k.shape[1]
+    dv = v.shape[-1]
+    y = np.zeros((S, n_q_heads, dv))
+    for s in range(S):
+        for kh in range(Hkv):
+            kk = k[s, kh]
+            if premap_params is not None:
+                p = premap_params
+                kk = premap(kk, p["gamma_k"][kh], p["beta_k"][kh], p["ln_eps"])
+            st[s, kh] += np.outer(phi_k_packed(kk), np.concatenate([v[s, kh], [1.0]]))
+        for h in range(n_q_heads):
+            kh = _kv_head(h, n_q_heads, Hkv)
+            qq = q[s, h]
+            if premap_params is not None:
+                p = premap_params
+                qq = premap(qq, p["gamma_q"][h], p["beta_q"][h], p["ln_eps"])
+            ut = phi_q_packed(qq, group_of_dim[h], a[h], b[h], c[h]) @ st[s, kh]
+            y[s, h] = ut[:dv] / ut[dv]
+    return y, st
+
+
+def abi_state_from_matrix(S):
+    """[..., D, dv+1] -> flat library layout [..., D*dv + D]: H rows then z."""
+    S = np.asarray(S)
+    H = S[..., :-1]
+    z = S[..., -1]
+    return np.concatenate([H.reshape(H.shape[:-2] + (-1,)), z], axis=-1)
+
+
+def matrix_from_abi_state(flat, D, dv):
+    """Inverse of abi_state_from_matrix."""
+    flat = np.asarray(flat)
+    H = flat[..., : D * dv].reshape(flat.shape[:-1] + (D, dv))
+    z = flat[..., D * dv:]
+    return np.concatenate([H, z[..., None]], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# contribution score (Eq. (2))
+# --------------------------------------------------------------------------
+
+def chi_bruteforce(Q, K, lengths=None):
+    """chi_{p,r} and chi_r by the definition of [OAL] Eq. (2).
+
+    chi_{p,r} = mean over causal pairs j <= i < N_p of |q_ir k_jr| / sqrt(d);
+    chi_r = equal-weight mean over prompts p.  Query head h uses KV head
+    h // (Hq/Hkv) (the native GQA map, [OAL] App. B).  Q: [P, Hq, N, d],
+    K: [P, Hkv, N, d]; lengths: [P] (default N).  O(N^2 d): tiny inputs only.
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    P, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    lengths = np.full(P, N) if lengths is None else np.asarray(lengths)
+    per = np.zeros((P, Hq, d))
+    for p in range(P):
+        n = int(lengths[p])
+        pairs = [(i, j) for i in range(n) for j in range(i + 1)]
+        for h in range(Hq):
+            kh = _kv_head(h, Hq, Hkv)
+            for r in range(d):
+                tot = 0.0
+                for (i, j) in pairs:
+                    tot += abs(Q[p, h, i, r] * K[p, kh, j, r]) / math.sqrt(d)
+                per[p, h, r] = tot / len(pairs)
+    return per, per.mean(axis=0)
+
+
+def chi_separable(Q, K, lengths=None):
+    """Same quantity as chi_bruteforce, summed as sum_i |q_ir| * sum_{j<=i} |k_jr|."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    P, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    lengths = np.full(P, N) if lengths is None else np.asarray(lengths)
+    per = np.zeros((P, Hq, d))
+    for p in range(P):
+        n = int(lengths[p])
+        npairs = n * (n + 1) / 2.0
+        for h in range(Hq):
+            kh = _kv_head(h, Hq, Hkv)
+            pre = np.cumsum(np.abs(K[p, kh, :n]), axis=0)
+            per[p, h] = (np.abs(Q[p, h, :n]) * pre).sum(axis=0) / (math.sqrt(d) * npairs)
+    return per, per.mean(axis=0)

@@ -1,0 +1,378 @@
+"""Pins for the fp64 oracle: checks against what the pages and mathematics fix.
+
+None of these re-types the oracle's own formula: each compares it with a
+printed value, a closed-form special case, an independent exact computation
+(rational arithmetic) or an invariant that a plausible mistake (dropped term,
+wrong sign, wrong index, transposed operand, wrong head map) would break.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+
+def _rand(rng, *shape, std=1.0):
+    return rng.standard_normal(shape) * std
+
+
+# ---------------------------------------------------------------- counts
+
+def test_state_entry_count_matches_pages(golden):
+    g = golden("state_counts.json")
+    d, dv = 64, 64
+    D = O.feature_count(d)
+    assert D * (dv + 1) == g["state_entries_d64_dv64"]
+    # the oracle's own feature maps have exactly D entries
+    rng = np.random.default_rng(0)
+    assert O.phi_k_packed(_rand(rng, d)).shape[-1] == D
+    assert O.state_from_prefix(_rand(rng, 3, d), _rand(rng, 3, dv)).shape == (D, dv + 1)
+    # d_h = 16 workload: (1 + 16 + 136) features
+    assert O.feature_count(16) == 153
+    # ordered-pair count of App. D
+    assert (1 + d + d * d) * (dv + 1) == 1 + d + d * d + (1 + d + d * d) * dv
+
+
+def test_factor_parameter_count(golden):
+    for G, n in golden("state_counts.json")["params"]:
+        L = np.tril(np.ones((G + 1, G + 1)))
+        assert int(L.sum()) == n
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_taylor_special_case_single_group():
+    """One group with a=1, b=1, c=1/2 is the second-order Taylor polynomial of s."""
+    rng = np.random.default_rng(1)
+    d = 64
+    for _ in range(20):
+        q, k = _rand(rng, d), _rand(rng, d)
+        s = float(np.dot(q, k)) / math.sqrt(d)
+        want = 1.0 + s + 0.5 * s * s
+        got = O.kappa(q, k, np.zeros(d, int), 1.0, [1.0], [[0.5]])
+        assert got == pytest.approx(want, rel=1e-14, abs=1e-14)
+
+
+def test_taylor_with_uniform_coefficients_over_any_partition():
+    """Equal b_g and c_gh over any partition reduce to the global polynomial
+    (OAL App. D, positive global reference: s is the sum of the s_g)."""
+    rng = np.random.default_rng(2)
+    d = 16
+    for G in (2, 3, 5, 16):
+        gmap = rng.integers(0, G, size=d)
+        gmap[:G] = np.arange(G)  # every group non-empty
+        rng.shuffle(gmap)
+        b = np.full(G, 1.0)
+        c = np.full((G, G), 0.5)
+        q, k = _rand(rng, d), _rand(rng, d)
+        s = float(np.dot(q, k)) / math.sqrt(d)
+        assert O.kappa(q, k, gmap, 1.0, b, c) == pytest.approx(1 + s + 0.5 * s * s, rel=1e-13)
+
+
+def test_based_parabola_floor(golden):
+    pts = golden("taylor_parabola.json")["points"]
+    d = 16
+    for t, want in pts:
+        # q = 2 e_0 and k = (t * 2) e_0 give s = 4t / sqrt(16) = t exactly
+        q = np.zeros(d); q[0] = 2.0
+        k = np.zeros(d); k[0] = 2.0 * t
+        assert O.kappa(q, k, np.zeros(d, int), 1.0, [1.0], [[0.5]]) == want
+    rng = np.random.default_rng(3)
+    vals = [O.kappa(_rand(rng, d), _rand(rng, d), np.zeros(d, int), 1.0, [1.0], [[0.5]]) for _ in range(200)]
+    assert min(vals) >= 0.5
+
+
+def test_grouped_kernel_hand_example(golden):
+    g = golden("grouped_kernel_example.json")
+    got = O.kappa(np.array(g["q"]), np.array(g["k"]), np.array(g["group_of_dim"]), g["a"], g["b"], g["c"])
+    want = g["kappa_rational_part"] + g["kappa_coefficient_of_inv_sqrt2"] / math.sqrt(2.0)
+    assert got == pytest.approx(want, rel=1e-15)
+
+
+def test_asymmetric_group_pair_terms_enter_with_both_orders():
+    """c_gh and c_hg are both summed: an off-diagonal-only c gives 2 c s_1 s_2."""
+    d = 2
+    q, k = np.array([1.0, 1.0]), np.array([2.0, 3.0])
+    s1, s2 = 2.0 / math.sqrt(2), 3.0 / math.sqrt(2)
+    c = [[0.0, 0.25], [0.25, 0.0]]
+    got = O.kappa(q, k, np.array([0, 1]), 0.0, [0.0, 0.0], c)
+    assert got == pytest.approx(2 * 0.25 * s1 * s2, rel=1e-15)
+    # a linear-only kernel picks the right group for each b
+    got = O.kappa(q, k, np.array([0, 1]), 0.0, [1.0, -2.0], [[0, 0], [0, 0]])
+    assert got == pytest.approx(s1 - 2 * s2, rel=1e-15)
+
+
+# ---------------------------------------------------------------- positivity
+
+def test_eq7_positivity_and_denominator_floor():
+    rng = np.random.default_rng(4)
+    d, G, eps = 8, 3, 1e-3
+    gmap = np.array([0, 1, 2, 2, 1, 0, 2, 2])
+    for trial in range(5):
+        L = np.tril(rng.uniform(-1, 1, size=(G + 1, G + 1)))
+        a, b, c = O.coeffs_from_factor(eps, L)
+        for _ in range(50):
+            assert O.kappa(_rand(rng, d, std=3), _rand(rng, d, std=3), gmap, a, b, c) >= eps * (1 - 1e-12)
+    # den_i >= (i+1) eps along a sequence
+    B, H, N, dv = 1, 1, 40, 3
+    Q, K, V = _rand(rng, B, H, N, d, std=2), _rand(rng, B, H, N, d, std=2), _rand(rng, B, H, N, dv)
+    _, _, den = O.attention_direct(Q, K, V, [gmap], [a], [b], [c], return_parts=True)
+    assert np.all(den[0, 0] >= (np.arange(N) + 1) * eps * (1 - 1e-12))
+
+
+def test_psd_c_alone_does_not_give_nonnegative_kernel():
+    """The positivity needs the full M = [[a, b/2], [b/2, c]] PSD, not c alone."""
+    d = 4
+    q = np.array([1.0, 0, 0, 0]); k = np.array([-1.0, 0, 0, 0])  # s = -1/2
+    val = O.kappa(q, k, np.zeros(d, int), 0.1, [1.0], [[1.0]])
+    assert val == pytest.approx(-0.15, rel=1e-14)
+
+
+def test_global_embedding_is_psd_and_matches():
+    """OAL App. D: M_00 = m00, M_0g = m01, M_gh = m11 embeds a PSD global
+    quadratic into any partition, stays PSD and gives the same kernel."""
+    rng = np.random.default_rng(5)
+    d, G = 12, 4
+    gmap = np.array([0, 1, 2, 3] * 3)
+    for _ in range(5):
+        Lg = np.tril(rng.uniform(-1, 1, size=(2, 2)))
+        Mg = Lg @ Lg.T
+        M = np.empty((G + 1, G + 1))
+        M[0, 0] = Mg[0, 0]
+        M[0, 1:] = M[1:, 0] = Mg[0, 1]
+        M[1:, 1:] = Mg[1, 1]
+        assert np.linalg.eigvalsh(M).min() >= -1e-12
+        eps = 0.01
+        a, b, c = eps + M[0, 0], 2 * M[0, 1:], M[1:, 1:]
+        q, k = _rand(rng, d), _rand(rng, d)
+        s = float(np.dot(q, k)) / math.sqrt(d)
+        want = eps + Mg[0, 0] + 2 * Mg[0, 1] * s + Mg[1, 1] * s * s
+        assert O.kappa(q, k, gmap, a, b, c) == pytest.approx(want, rel=1e-12)
+
+
+# ---------------------------------------------------------------- worked example
+
+def test_mercer_counterexample(golden):
+    g = golden("mercer_counterexample.json")
+    eps = 0.25
+    a, b, c = O.coeffs_from_factor(eps, np.array(g["L_factor"]))
+    assert np.allclose(np.array(g["L_factor"]) @ np.array(g["L_factor"]).T, g["M"])
+    assert (a, b[0], c[0][0]) == (eps + 1.0, -2.0, 1.0)
+    xs = g["inputs"]
+    gram = np.array([[O.kappa(np.array([x]), np.array([z]), np.zeros(1, int), a, b, c) for z in xs] for x in xs])
+    want = eps * np.array(g["gram_eps_coefficient"]) + np.array(g["gram_constant"])
+    assert np.array_equal(gram, want)
+    ev = sorted(np.linalg.eigvalsh(gram))
+    want_ev = sorted(ec * eps + cst for ec, cst in g["eigenvalues_as_eps_coeff_and_constant"])
+    assert np.allclose(ev, want_ev, rtol=0, atol=1e-14)
+    # derived causal output at position 2
+    v = np.array([[3.0, -1.0], [0.5, 2.0]])
+    Q = np.array([0.0, -1.0]).reshape(1, 1, 2, 1)
+    K = np.array([1.0, -1.0]).reshape(1, 1, 2, 1)
+    y = O.attention_direct(Q, K, v.reshape(1, 1, 2, 2), [np.zeros(1, int)], [a], [b], [c])
+    want_y2 = ((eps + 4) * v[0] + eps * v[1]) / (2 * eps + 4)
+    assert np.allclose(y[0, 0, 1], want_y2, rtol=1e-15, atol=0)
+
+
+def test_coeffs_from_factor_hand_example():
+    # L = [[1, 0], [0.5, 2]] -> M = [[1, 0.5], [0.5, 4.25]]
+    a, b, c = O.coeffs_from_factor(0.125, np.array([[1.0, 0.0], [0.5, 2.0]]))
+    assert a == 1.125 and b[0] == 1.0 and c[0][0] == 4.25
+
+
+# ---------------------------------------------------------------- exact brute force
+
+def _fraction_attention(Q, K, V, gmap, a, b, c, sqrt_d):
+    """Definition in exact rational arithmetic; sqrt(d) must be an integer."""
+    N, d = len(Q), len(Q[0])
+    G = len(b)
+    out = []
+    for i in range(N):
+        num = [Fraction(0)] * len(V[0])
+        den = Fraction(0)
+        for j in range(i + 1):
+            s = [Fraction(0)] * G
+            for r in range(d):
+                s[gmap[r]] += Fraction(Q[i][r]) * Fraction(K[j][r]) / sqrt_d
+            kap = Fraction(a) + sum(Fraction(b[g]) * s[g] for g in range(G))
+            kap += sum(Fraction(c[g][h]) * s[g] * s[h] for g in range(G) for h in range(G))
+            den += kap
+            num = [num[l] + kap * Fraction(V[j][l]) for l in range(len(V[0]))]
+        out.append([x / den for x in num])
+    return out
+
+
+def test_direct_form_matches_exact_rational_bruteforce():
+    rng = np.random.default_rng(6)
+    d, dv, N, G = 4, 3, 6, 2
+    gmap = [1, 0, 1, 0]
+    Q = np.round(_rand(rng, N, d) * 8) / 8
+    K = np.round(_rand(rng, N, d) * 8) / 8
+    V = np.round(_rand(rng, N, dv) * 8) / 8
+    a, b, c = 0.75, [0.5, -0.25], [[0.5, 0.125], [0.125, 0.375]]
+    want = np.array(_fraction_attention(Q.tolist(), K.tolist(), V.tolist(), gmap, a, b, c, 2), dtype=float)
+    got = O.attention_direct(Q[None, None], K[None, None], V[None, None], [gmap], [a], [b], [c])[0, 0]
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- forms agree
+
+def _small_case(rng, B=2, Hq=4, Hkv=2, N=11, d=4, dv=3, G=3):
+    Q, K, V = _rand(rng, B, Hq, N, d), _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, dv)
+    groups = np.stack([rng.permutation(np.arange(d) % G) for _ in range(Hq)])
+    Ls = [np.tril(rng.uniform(0.1, 1.0, size=(G + 1, G + 1))) for _ in range(Hq)]
+    abc = [O.coeffs_from_factor(1e-3, L) for L in Ls]
+    a = np.array([x[0] for x in abc]); b = np.array([x[1] for x in abc]); c = np.array([x[2] for x in abc])
+    return Q, K, V, groups, a, b, c
+
+
+def test_direct_equals_packed_and_ordered_recurrences():
+    rng = np.random.default_rng(7)
+    Q, K, V, groups, a, b, c = _small_case(rng)
+    yd = O.attention_direct(Q, K, V, groups, a, b, c)
+    yp = O.attention_recurrent_packed(Q, K, V, groups, a, b, c)
+    yo = O.attention_recurrent_ordered(Q, K, V, groups, a, b, c)
+    assert np.allclose(yp, yd, rtol=1e-11, atol=1e-12)
+    assert np.allclose(yo, yd, rtol=1e-11, atol=1e-12)
+
+
+def test_row_subset_is_exact():
+    rng = np.random.default_rng(8)
+    Q, K, V, groups, a, b, c = _small_case(rng, N=17)
+    rows = np.array([0, 5, 16])
+    assert np.allclose(O.attention_direct(Q, K, V, groups, a, b, c, rows=rows),
+                       O.attention_direct(Q, K, V, groups, a, b, c)[:, :, rows], rtol=1e-14, atol=1e-15)
+
+
+def test_gqa_head_map_is_consecutive_blocks():
+    rng = np.random.default_rng(9)
+    Q, K, V, groups, a, b, c = _small_case(rng, Hq=6, Hkv=2)
+    y = O.attention_direct(Q, K, V, groups, a, b, c)
+    for h in range(6):
+        kh = h // 3
+        yh = O.attention_direct(Q[:, h:h + 1], K[:, kh:kh + 1], V[:, kh:kh + 1], groups[h:h + 1],
+                                a[h:h + 1], b[h:h + 1], c[h:h + 1])
+        assert np.allclose(yh[:, 0], y[:, h], rtol=1e-14, atol=1e-15)
+
+
+def test_invariants():
+    rng = np.random.default_rng(10)
+    Q, K, V, groups, a, b, c = _small_case(rng, B=1, Hq=2, Hkv=1)
+    y = O.attention_direct(Q, K, V, groups, a, b, c)
+    # first position returns its own value
+    assert np.allclose(y[:, :, 0], V[:, [0, 0], 0], rtol=1e-14)
+    # constant values are reproduced everywhere
+    Vc = np.broadcast_to(np.array([1.5, -2.0, 0.25]), V.shape).copy()
+    assert np.allclose(O.attention_direct(Q, K, Vc, groups, a, b, c), 1.5 * 0 + Vc[:, [0, 0]], rtol=1e-13)
+    # positive rescaling of (a, b, c)
+    assert np.allclose(O.attention_direct(Q, K, V, groups, 3 * a, 3 * b, 3 * c), y, rtol=1e-12)
+    # joint permutation of the dimensions and the group map
+    perm = rng.permutation(Q.shape[-1])
+    yp = O.attention_direct(Q[..., perm], K[..., perm], V, groups[:, perm], a, b, c)
+    assert np.allclose(yp, y, rtol=1e-12)
+    # identical query heads give identical outputs
+    Q2 = Q.copy(); Q2[:, 1] = Q2[:, 0]
+    g2 = groups.copy(); g2[1] = g2[0]
+    y2 = O.attention_direct(Q2, K, V, g2, a[[0, 0]], b[[0, 0]], c[[0, 0]])
+    assert np.array_equal(y2[:, 0], y2[:, 1])
+
+
+def test_decode_step_matches_direct_last_row_and_state():
+    rng = np.random.default_rng(11)
+    d, dv, G, Hq, Hkv, n = 4, 3, 2, 4, 2, 9
+    Q, K, V, groups, a, b, c = _small_case(rng, B=1, Hq=Hq, Hkv=Hkv, N=n + 1, d=d, dv=dv, G=G)
+    state = np.stack([O.state_from_prefix(K[0, kh, :n], V[0, kh, :n]) for kh in range(Hkv)])[None]
+    y, st = O.decode_step(state, Q[:, :, n], K[:, :, n], V[:, :, n], groups, a, b, c, Hq)
+    yd = O.attention_direct(Q, K, V, groups, a, b, c, rows=np.array([n]))
+    assert np.allclose(y, yd[:, :, 0], rtol=1e-12)
+    full = np.stack([O.state_from_prefix(K[0, kh], V[0, kh]) for kh in range(Hkv)])[None]
+    assert np.allclose(st, full, rtol=1e-13)
+    # the packed state holds raw moments: entry for pair (r, t) is sum k_r k_t v
+    D = O.feature_count(d)
+    pairs = O.packed_pairs(d)
+    f = 1 + d + pairs.index((1, 3))
+    assert np.isclose(full[0, 0, f, 0], np.sum(K[0, 0, :, 1] * K[0, 0, :, 3] * V[0, 0, :, 0]))
+    assert full.shape[2] == D
+
+
+def test_state_resume_equals_full_run():
+    rng = np.random.default_rng(12)
+    Q, K, V, groups, a, b, c = _small_case(rng, B=1, N=14)
+    y_full, S_full = O.attention_recurrent_packed(Q, K, V, groups, a, b, c, return_state=True)
+    y1, S1 = O.attention_recurrent_packed(Q[:, :, :6], K[:, :, :6], V[:, :, :6], groups, a, b, c, return_state=True)
+    y2, S2 = O.attention_recurrent_packed(Q[:, :, 6:], K[:, :, 6:], V[:, :, 6:], groups, a, b, c,
+                                          state_in=S1, return_state=True)
+    assert np.allclose(np.concatenate([y1, y2], axis=2), y_full, rtol=1e-12)
+    assert np.allclose(S2, S_full, rtol=1e-13)
+
+
+def test_abi_state_layout_roundtrip():
+    rng = np.random.default_rng(13)
+    S = _rand(rng, 2, 3, 15, 5)
+    flat = O.abi_state_from_matrix(S)
+    assert flat.shape == (2, 3, 15 * 4 + 15)
+    assert np.array_equal(flat[..., :4], S[..., 0, :4])  # first H row
+    assert np.array_equal(flat[..., 60:], S[..., :, 4])  # z column at the end
+    assert np.array_equal(O.matrix_from_abi_state(flat, 15, 4), S)
+
+
+# ---------------------------------------------------------------- ReBased readings
+
+def test_rebased_premap_and_feature_readings():
+    rng = np.random.default_rng(14)
+    d = 16
+    x = _rand(rng, 5, d, std=3)
+    z = O.premap(x, np.ones(d), np.zeros(d), 1e-5)
+    assert np.allclose(z.mean(-1), 0, atol=1e-12)
+    var = x.var(-1)
+    assert np.allclose((z ** 2).mean(-1), var / (var + 1e-5), rtol=1e-12)
+    gq, bq = 1 + 0.3 * _rand(rng, d), 0.3 * _rand(rng, d)
+    gk, bk = 1 + 0.3 * _rand(rng, d), 0.3 * _rand(rng, d)
+    q, k = _rand(rng, d), _rand(rng, d)
+    qt, kt = O.premap(q, gq, bq), O.premap(k, gk, bk)
+    # elementwise-square reading: d singleton groups, c = d I, a = b = 0
+    val = O.kappa(qt, kt, np.arange(d), 0.0, np.zeros(d), d * np.eye(d))
+    assert val == pytest.approx(float(np.dot(qt ** 2, kt ** 2)), rel=1e-12)
+    # squared-dot-product reading: one group, c = d
+    val = O.kappa(qt, kt, np.zeros(d, int), 0.0, [0.0], [[float(d)]])
+    assert val == pytest.approx(float(np.dot(qt, kt)) ** 2, rel=1e-12)
+
+
+# ---------------------------------------------------------------- contribution score
+
+def test_chi_bruteforce_equals_separable_varlen_gqa():
+    rng = np.random.default_rng(15)
+    P, Hq, Hkv, N, d = 3, 4, 2, 9, 5
+    Q, K = _rand(rng, P, Hq, N, d), _rand(rng, P, Hkv, N, d)
+    lens = np.array([9, 4, 1])
+    pb, mb = O.chi_bruteforce(Q, K, lens)
+    ps, ms = O.chi_separable(Q, K, lens)
+    assert np.allclose(pb, ps, rtol=1e-12) and np.allclose(mb, ms, rtol=1e-12)
+    # equal-weight average over prompts, not over pairs
+    assert np.allclose(mb, pb.mean(0))
+
+
+def test_chi_closed_forms():
+    P, Hq, Hkv, N, d = 2, 2, 1, 7, 4
+    ones = np.ones((P, Hq, N, d))
+    _, m = O.chi_bruteforce(ones, np.ones((P, Hkv, N, d)))
+    assert np.allclose(m, 1 / math.sqrt(d), rtol=1e-14)
+    rng = np.random.default_rng(16)
+    Q, K = _rand(rng, P, Hq, N, d), _rand(rng, P, Hkv, N, d)
+    _, m0 = O.chi_bruteforce(Q, K)
+    Q2, K2 = Q.copy(), K.copy()
+    Q2[..., 2] *= -3.0
+    K2[..., 2] *= 0.5
+    _, m1 = O.chi_bruteforce(Q2, K2)
+    assert np.allclose(m1[:, 2], 1.5 * m0[:, 2], rtol=1e-13)
+    assert np.allclose(m1[:, [0, 1, 3]], m0[:, [0, 1, 3]], rtol=1e-14)
+
+
+def test_chi_gaussian_expectation():
+    rng = np.random.default_rng(17)
+    P, H, N, d = 4, 2, 400, 16
+    _, m = O.chi_separable(_rand(rng, P, H, N, d), _rand(rng, P, H, N, d))
+    assert abs(m.mean() - (2 / math.pi) / math.sqrt(d)) < 0.03 * (2 / math.pi) / math.sqrt(d)
