@@ -1,0 +1,23 @@
+"""OAL causal grouped-quadratic linear attention for MI355X (gfx950).
+
+The compute path is the HIP library ``liboal.so`` (C ABI in include/oal.h);
+this package is its thin torch binding plus host-side grouping utilities.
+"""
+
+from ._lib import OalError, lib  # noqa: F401
+from .grouping import groups_from_contribution  # noqa: F401
+from .ops import (  # noqa: F401
+    Coeffs,
+    Prep,
+    coeffs_from_factor,
+    contrib,
+    decode_step,
+    feature_count,
+    fwd,
+    fwd_workspace_bytes,
+    state_floats,
+)
+
+
+def version() -> str:
+    return lib().oal_version().decode()

@@ -1,0 +1,241 @@
+// Recurrent single-token decode for OAL attention on gfx950.
+//
+// Per (sequence, KV head) the fp32 state S = [H | z] of the OAL paper's
+// Eq. (5) (packed as in App. D) is streamed once from HBM: each row f gets the
+// rank-1 update H[f] += phi_k(k)_f v and z[f] += phi_k(k)_f, is written back,
+// and is read by every query head of the group, num_h += phi_q,h(q_h)_f H[f]
+// and den_h += phi_q,h(q_h)_f z[f] (Eq. (6)); y_h = num_h / den_h.  The new
+// token therefore belongs to its own causal prefix.
+//
+// One 256-thread CTA per (sequence, KV head).  The feature values phi_k and
+// phi_q,h of all D rows are computed once into LDS; the streaming loop reads
+// 16 rows per pass as float4 (16 threads per 256-byte row), fully coalesced.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "oal_device.h"
+#include "oal_internal.h"
+
+namespace oal {
+
+namespace {
+constexpr int DV = 64;
+
+template <int DH>
+__device__ __forceinline__ void premap_vec(float* x, const float* __restrict__ gamma,
+                                           const float* __restrict__ beta, float eps) {
+  float mu = 0.f;
+  for (int c = 0; c < DH; ++c) mu += x[c];
+  mu *= 1.f / DH;
+  float var = 0.f;
+  for (int c = 0; c < DH; ++c) {
+    const float t = x[c] - mu;
+    var += t * t;
+  }
+  var *= 1.f / DH;
+  const float inv = 1.f / sqrtf(var + eps);
+  for (int c = 0; c < DH; ++c) x[c] = gamma[c] * (x[c] - mu) * inv + beta[c];
+}
+}  // namespace
+
+template <typename T, int DH, int RMAX, bool PREMAP>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ group_of_dim, const float* __restrict__ ca,
+    const float* __restrict__ cb, const float* __restrict__ cc, int G,
+    const float* __restrict__ gamma_q, const float* __restrict__ beta_q,
+    const float* __restrict__ gamma_k, const float* __restrict__ beta_k, float ln_eps,
+    float* __restrict__ state, T* __restrict__ y, int Hq, int Hkv) {
+  constexpr int D = (int)packed_features(DH);
+  extern __shared__ float smem[];
+  float* phik = smem;                 // [D]
+  float* phiq = smem + D;             // [RMAX][D]
+  __shared__ float khat[DH + 1];
+  __shared__ float qhat[RMAX][DH + 1];
+  __shared__ float vv[DV];
+  __shared__ float red[16][RMAX][DV];
+  __shared__ float dred[RMAX][256 / kWave];
+  __shared__ int bad;
+
+  const int bh = blockIdx.x;
+  const int b = bh / Hkv, kvh = bh % Hkv;
+  const int R = Hq / Hkv;
+  const int tid = threadIdx.x;
+
+  if (tid == 0) bad = 0;
+  if (tid < DH) khat[tid] = to_f32(k[(long)bh * DH + tid]);
+  if (tid == DH) khat[DH] = 1.f;
+  if (tid < DV) vv[tid] = to_f32(v[(long)bh * DV + tid]);
+  for (int idx = tid; idx < R * (DH + 1); idx += blockDim.x) {
+    const int hh = idx / (DH + 1), r = idx % (DH + 1);
+    qhat[hh][r] = r < DH ? to_f32(q[((long)b * Hq + kvh * R + hh) * DH + r]) : 1.f;
+  }
+  __syncthreads();
+  if (PREMAP) {
+    if (tid == 0) premap_vec<DH>(khat, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
+    if (tid >= 64 && tid - 64 < R) {
+      const int hh = tid - 64, h = kvh * R + hh;
+      premap_vec<DH>(qhat[hh], gamma_q + h * DH, beta_q + h * DH, ln_eps);
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < R * DH; idx += blockDim.x) {
+    const int g = group_of_dim[(kvh * R + idx / DH) * DH + idx % DH];
+    if (g < 0 || g >= G) atomicOr(&bad, 1);
+  }
+
+  // feature values of every packed row: const, linear r, pairs r <= t
+  const float inv_sqrt_d = 1.f / sqrtf((float)DH);
+  for (int f = tid; f < D; f += blockDim.x) {
+    int r, t;
+    if (f == 0) {
+      r = DH; t = DH;
+    } else if (f <= DH) {
+      r = f - 1; t = DH;
+    } else {
+      int p = f - 1 - DH;
+      r = 0;
+      while (p >= DH - r) { p -= DH - r; ++r; }
+      t = r + p;
+    }
+    phik[f] = khat[r] * khat[t];
+    for (int hh = 0; hh < RMAX; ++hh) {
+      if (hh >= R) break;
+      const int h = kvh * R + hh;
+      float cf;
+      if (r == DH) {
+        cf = ca[h];
+      } else if (t == DH) {
+        const int g = min(max(group_of_dim[h * DH + r], 0), G - 1);
+        cf = cb[h * G + g] * inv_sqrt_d;
+      } else {
+        const int g1 = min(max(group_of_dim[h * DH + r], 0), G - 1);
+        const int g2 = min(max(group_of_dim[h * DH + t], 0), G - 1);
+        const float m = r == t ? 1.f : 2.f;
+        cf = m * 0.5f * (cc[(h * G + g1) * G + g2] + cc[(h * G + g2) * G + g1]) / DH;
+      }
+      phiq[hh * D + f] = cf * qhat[hh][r] * qhat[hh][t];
+    }
+  }
+  __syncthreads();
+
+  // ---- stream H rows: 16 threads per row, float4 each ----
+  float* sp = state + (long)bh * D * (DV + 1);
+  const int c4 = tid % 16, rg = tid / 16;
+  const float4 v4 = make_float4(vv[4 * c4], vv[4 * c4 + 1], vv[4 * c4 + 2], vv[4 * c4 + 3]);
+  float acc[RMAX][4];
+#pragma unroll
+  for (int hh = 0; hh < RMAX; ++hh) acc[hh][0] = acc[hh][1] = acc[hh][2] = acc[hh][3] = 0.f;
+
+  constexpr int U = 4;
+  for (int f0 = rg; f0 < D; f0 += 16 * U) {
+    float4 hv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = f0 + 16 * u;
+      if (f < D) hv[u] = *reinterpret_cast<const float4*>(&sp[(long)f * DV + 4 * c4]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = f0 + 16 * u;
+      if (f >= D) continue;
+      const float pk = phik[f];
+      float4 x = hv[u];
+      x.x += pk * v4.x; x.y += pk * v4.y; x.z += pk * v4.z; x.w += pk * v4.w;
+      *reinterpret_cast<float4*>(&sp[(long)f * DV + 4 * c4]) = x;
+#pragma unroll
+      for (int hh = 0; hh < RMAX; ++hh) {
+        if (hh < R) {
+          const float pq = phiq[hh * D + f];
+          acc[hh][0] += pq * x.x; acc[hh][1] += pq * x.y;
+          acc[hh][2] += pq * x.z; acc[hh][3] += pq * x.w;
+        }
+      }
+    }
+  }
+  // ---- z column ----
+  float dacc[RMAX];
+#pragma unroll
+  for (int hh = 0; hh < RMAX; ++hh) dacc[hh] = 0.f;
+  float* zp = sp + (long)D * DV;
+  for (int f = tid; f < D; f += blockDim.x) {
+    const float zn = zp[f] + phik[f];
+    zp[f] = zn;
+#pragma unroll
+    for (int hh = 0; hh < RMAX; ++hh)
+      if (hh < R) dacc[hh] += phiq[hh * D + f] * zn;
+  }
+
+  // ---- reductions ----
+#pragma unroll
+  for (int hh = 0; hh < RMAX; ++hh) {
+    if (hh >= R) break;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[rg][hh][4 * c4 + e] = acc[hh][e];
+    float dsum = dacc[hh];
+    for (int off = 32; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off);
+    if (tid % kWave == 0) dred[hh][tid / kWave] = dsum;
+  }
+  __syncthreads();
+  const float nanv = __builtin_nanf("");
+  for (int idx = tid; idx < R * DV; idx += blockDim.x) {
+    const int hh = idx / DV, n = idx % DV;
+    float num = 0.f;
+    for (int g = 0; g < 16; ++g) num += red[g][hh][n];
+    const float den = dred[hh][0] + dred[hh][1] + dred[hh][2] + dred[hh][3];
+    store_elem(&y[((long)b * Hq + kvh * R + hh) * DV + n], bad ? nanv : num / den);
+  }
+}
+
+template <typename T, int DH, int RMAX>
+static hipError_t launch_decode_r(const DecodeLaunch& a, hipStream_t stream) {
+  constexpr int D = (int)packed_features(DH);
+  const size_t shm = (size_t)(1 + RMAX) * D * sizeof(float);
+  dim3 grid(a.B * a.Hkv);
+  const T* qq = reinterpret_cast<const T*>(a.q);
+  const T* kk = reinterpret_cast<const T*>(a.k);
+  const T* vv = reinterpret_cast<const T*>(a.v);
+  T* yy = reinterpret_cast<T*>(a.y);
+  hipError_t err = a.premap
+      ? hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, DH, RMAX, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm)
+      : hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, DH, RMAX, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (err != hipSuccess) return err;
+  if (a.premap)
+    hipLaunchKernelGGL((decode_kernel<T, DH, RMAX, true>), grid, dim3(256), shm, stream, qq, kk, vv,
+                       a.group_of_dim, a.ca, a.cb, a.cc, a.G, a.gamma_q, a.beta_q, a.gamma_k, a.beta_k,
+                       a.ln_eps, a.state, yy, a.Hq, a.Hkv);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, DH, RMAX, false>), grid, dim3(256), shm, stream, qq, kk, vv,
+                       a.group_of_dim, a.ca, a.cb, a.cc, a.G, nullptr, nullptr, nullptr, nullptr, 0.f,
+                       a.state, yy, a.Hq, a.Hkv);
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+static hipError_t launch_decode_d(const DecodeLaunch& a, hipStream_t stream) {
+  const int R = a.Hq / a.Hkv;
+  if (R <= 1) return launch_decode_r<T, DH, 1>(a, stream);
+  if (R <= 2) return launch_decode_r<T, DH, 2>(a, stream);
+  if (R <= 4) return launch_decode_r<T, DH, 4>(a, stream);
+  return launch_decode_r<T, DH, 8>(a, stream);
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
+  if (a.dtype == 1) {
+    switch (a.d_h) {
+      case 16: return launch_decode_d<uint16_t, 16>(a, stream);
+      case 32: return launch_decode_d<uint16_t, 32>(a, stream);
+      default: return launch_decode_d<uint16_t, 64>(a, stream);
+    }
+  }
+  switch (a.d_h) {
+    case 16: return launch_decode_d<float, 16>(a, stream);
+    case 32: return launch_decode_d<float, 32>(a, stream);
+    default: return launch_decode_d<float, 64>(a, stream);
+  }
+}
+
+}  // namespace oal

@@ -1,0 +1,125 @@
+// Device helpers shared by the OAL HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "oal_layout.h"
+
+namespace oal {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---- element access: activations are float or bfloat16 bit patterns ----
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
+__device__ __forceinline__ void store_elem(uint16_t* p, float x) { *p = bf16_bits(x); }
+
+template <typename T>
+struct IsBf16 {
+  static constexpr bool value = false;
+};
+template <>
+struct IsBf16<uint16_t> {
+  static constexpr bool value = true;
+};
+
+// ---- MFMA operand fragments: 8 elements per lane ----
+// bf16 path: one v_mfma_f32_16x16x32_bf16 per fragment pair.
+// fp32 path: eight v_mfma_f32_16x16x4_f32, element e of lane group lg being
+// the same K index in A and B, so the contraction covers the same 32 indices.
+template <bool BF16>
+struct Frag;
+template <>
+struct Frag<true> {
+  bf16x8 v;
+};
+template <>
+struct Frag<false> {
+  float v[8];
+};
+
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> frag_from(const float (&x)[8]);
+template <>
+__device__ __forceinline__ Frag<true> frag_from<true>(const float (&x)[8]) {
+  Frag<true> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (__bf16)x[e];
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<false> frag_from<false>(const float (&x)[8]) {
+  Frag<false> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = x[e];
+  return f;
+}
+
+template <bool BF16>
+__device__ __forceinline__ Frag<BF16> frag_zero() {
+  float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  return frag_from<BF16>(z);
+}
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<true>& a, const Frag<true>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<false>& a, const Frag<false>& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// Fragment loads from memory holding the fragment's element type
+// (bf16 bits or float), 8 consecutive elements.
+__device__ __forceinline__ Frag<true> frag_load(const uint16_t* p) {
+  Frag<true> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag<false> frag_load(const float* p) {
+  Frag<false> f;
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+  return f;
+}
+
+// Storage type of snapshot / fragment memory for an activation type.
+template <typename T>
+struct FragStore {
+  typedef float type;
+};
+template <>
+struct FragStore<uint16_t> {
+  typedef uint16_t type;
+};
+
+__device__ __forceinline__ void store4(uint16_t* p, const f32x4& x) {
+  uint2 w;
+  w.x = (uint32_t)bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
+  w.y = (uint32_t)bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+__device__ __forceinline__ void store4(float* p, const f32x4& x) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// LayerNorm + affine of one row held by `n` consecutive lanes of a wave
+// (each lane holds `per` elements).  Used for the ReBased pre-map.
+__device__ __forceinline__ float wave_sum_width(float x, int width) {
+  for (int off = width / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, width);
+  return x;
+}
+
+}  // namespace oal

@@ -1,0 +1,55 @@
+// Launch descriptors shared by the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oal {
+
+// Tokens per prefill chunk.
+constexpr int kChunk = 64;
+
+struct FwdLaunch {
+  int B, Hq, Hkv, N, d_h, G, dtype;
+  const void *q, *k, *v;
+  const int32_t* group_of_dim;
+  const float *ca, *cb, *cc;
+  bool premap;
+  const float *gamma_q, *beta_q, *gamma_k, *beta_k;
+  float ln_eps;
+  const float* state_in;
+  float* state_out;
+  void* y;
+  void* workspace;
+};
+
+struct DecodeLaunch {
+  int B, Hq, Hkv, d_h, G, dtype;
+  const void *q, *k, *v;
+  const int32_t* group_of_dim;
+  const float *ca, *cb, *cc;
+  bool premap;
+  const float *gamma_q, *beta_q, *gamma_k, *beta_k;
+  float ln_eps;
+  float* state;
+  void* y;
+};
+
+struct ContribLaunch {
+  int P, Hq, Hkv, N, d_h, dtype;
+  const void *q, *k;
+  const int32_t* seq_lens;
+  float* chi_per_prompt;
+  float* chi_mean;
+  void* workspace;
+};
+
+size_t fwd_workspace_bytes(int B, int Hkv, int N, int d_h, int dtype);
+hipError_t launch_fwd(const FwdLaunch& a, hipStream_t stream);
+hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h);
+hipError_t launch_contrib(const ContribLaunch& a, hipStream_t stream);
+
+}  // namespace oal

@@ -1,0 +1,199 @@
+"""Torch-facing binding of the OAL C ABI (argument marshalling only).
+
+Every computation happens in the HIP kernels of ``liboal.so``; this module
+checks tensor placement/shape/dtype, allocates outputs and workspaces with
+torch (device memory plumbing) and passes raw pointers plus the current HIP
+stream to the library.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.OAL_F32, torch.bfloat16: L.OAL_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.is_cuda, f"{name} must be on the GPU")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None:
+        _need(t.dim() == ndim, f"{name} must have {ndim} dims")
+    return t
+
+
+class Coeffs:
+    """Device copies of the grouped-kernel coefficients of every query head.
+
+    group_of_dim [Hq, d_h] int32 in [0, G), a [Hq], b [Hq, G], c [Hq, G, G]
+    float32.  Host copies are checked with the library's validator before
+    upload.
+    """
+
+    def __init__(self, group_of_dim, a, b, c, device="cuda"):
+        g = np.ascontiguousarray(np.asarray(group_of_dim, dtype=np.int32))
+        a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+        b = np.ascontiguousarray(np.asarray(b, dtype=np.float32))
+        c = np.ascontiguousarray(np.asarray(c, dtype=np.float32))
+        Hq, d = g.shape
+        G = b.shape[1]
+        _need(a.shape == (Hq,) and b.shape == (Hq, G) and c.shape == (Hq, G, G), "coefficient shapes")
+        dims = L.OalDims(1, Hq, 1, 1, d, 64, G, 0)
+        L.check(L.lib().oal_check_coeffs(ctypes.byref(dims), g.ctypes.data_as(ctypes.c_void_p),
+                                         c.ctypes.data_as(ctypes.c_void_p)), "oal_check_coeffs")
+        self.n_heads, self.d_h, self.n_groups = Hq, d, G
+        self.group_of_dim = torch.from_numpy(g).to(device)
+        self.a = torch.from_numpy(a).to(device)
+        self.b = torch.from_numpy(b).to(device)
+        self.c = torch.from_numpy(c).to(device)
+
+    def struct(self):
+        return L.OalCoeffs(self.group_of_dim.data_ptr(), self.a.data_ptr(), self.b.data_ptr(),
+                           self.c.data_ptr())
+
+
+class Prep:
+    """ReBased pre-map parameters (device float32)."""
+
+    def __init__(self, gamma_q, beta_q, gamma_k, beta_k, ln_eps=1e-5, device="cuda"):
+        conv = lambda x: torch.as_tensor(np.asarray(x, dtype=np.float32)).contiguous().to(device)
+        self.gamma_q, self.beta_q = conv(gamma_q), conv(beta_q)
+        self.gamma_k, self.beta_k = conv(gamma_k), conv(beta_k)
+        self.ln_eps = float(ln_eps)
+
+    def struct(self):
+        return L.OalPrep(self.gamma_q.data_ptr(), self.beta_q.data_ptr(), self.gamma_k.data_ptr(),
+                         self.beta_k.data_ptr(), self.ln_eps)
+
+
+def coeffs_from_factor(eps: float, Lf) -> tuple:
+    """(eps, L [H, G+1, G+1]) -> (a [H], b [H, G], c [H, G, G]) float32, host side."""
+    Lf = np.ascontiguousarray(np.asarray(Lf, dtype=np.float64))
+    H, n, _ = Lf.shape
+    G = n - 1
+    a = np.zeros(H, np.float32)
+    b = np.zeros((H, G), np.float32)
+    c = np.zeros((H, G, G), np.float32)
+    vp = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+    L.check(L.lib().oal_coeffs_from_factor(H, G, float(eps), vp(Lf), vp(a), vp(b), vp(c)),
+            "oal_coeffs_from_factor")
+    return a, b, c
+
+
+def feature_count(d_h: int) -> int:
+    return int(L.lib().oal_feature_count(d_h))
+
+
+def state_floats(d_h: int, d_v: int) -> int:
+    return int(L.lib().oal_state_floats(d_h, d_v))
+
+
+def _dims(B, Hq, Hkv, N, d, dv, G, dtype):
+    return L.OalDims(B, Hq, Hkv, N, d, dv, G, _DT[dtype])
+
+
+def fwd_workspace_bytes(B, Hq, Hkv, N, d_h, d_v, G, dtype) -> int:
+    dims = _dims(B, Hq, Hkv, N, d_h, d_v, G, dtype)
+    return int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def fwd(q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None, return_state=False,
+        y=None, state_out=None, workspace=None):
+    """Causal OAL prefill.  q [B, Hq, N, d], k [B, Hkv, N, d], v [B, Hkv, N, 64].
+
+    Returns y (and the final state [B, Hkv, state_floats] when return_state).
+    """
+    _dev(q, "q", ndim=4)
+    _need(q.dtype in _DT, "q must be float32 or bfloat16")
+    _dev(k, "k", q.dtype, 4)
+    _dev(v, "v", q.dtype, 4)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dv = v.shape[3]
+    _need(k.shape == (B, Hkv, N, d) and v.shape == (B, Hkv, N, dv), "k/v shapes")
+    _need(coeffs.n_heads == Hq and coeffs.d_h == d, "coefficients do not match q")
+    dims = _dims(B, Hq, Hkv, N, d, dv, coeffs.n_groups, q.dtype)
+    if y is None:
+        y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
+    sf = state_floats(d, dv)
+    if state_in is not None:
+        _dev(state_in, "state_in", torch.float32)
+        _need(state_in.numel() == B * Hkv * sf, "state_in size")
+    if return_state and state_out is None:
+        state_out = torch.empty((B, Hkv, sf), dtype=torch.float32, device=q.device)
+    nbytes = int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    cs = coeffs.struct()
+    ps = prep.struct() if prep is not None else None
+    st = L.lib().oal_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
+                         ctypes.byref(ps) if ps is not None else None, _ptr(state_in), _ptr(state_out),
+                         _ptr(y), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
+    L.check(st, "oal_fwd")
+    return (y, state_out) if return_state else y
+
+
+def decode_step(q, k, v, coeffs: Coeffs, state, prep: Optional[Prep] = None, y=None):
+    """One decode step.  q [B, Hq, d], k [B, Hkv, d], v [B, Hkv, 64];
+    state [B, Hkv, state_floats] float32 updated in place.  Returns y [B, Hq, 64]."""
+    _dev(q, "q", ndim=3)
+    _need(q.dtype in _DT, "q must be float32 or bfloat16")
+    _dev(k, "k", q.dtype, 3)
+    _dev(v, "v", q.dtype, 3)
+    _dev(state, "state", torch.float32)
+    B, Hq, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[2]
+    _need(state.numel() == B * Hkv * state_floats(d, dv), "state size")
+    dims = _dims(B, Hq, Hkv, 0, d, dv, coeffs.n_groups, q.dtype)
+    if y is None:
+        y = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+    cs = coeffs.struct()
+    ps = prep.struct() if prep is not None else None
+    st = L.lib().oal_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
+                                 ctypes.byref(ps) if ps is not None else None, _ptr(state), _ptr(y), _stream())
+    L.check(st, "oal_decode_step")
+    return y
+
+
+def contrib(q, k, seq_lens=None, per_prompt=False, workspace=None):
+    """Contribution scores chi [Hq, d] (and chi per prompt [P, Hq, d]).
+
+    q [P, Hq, N, d], k [P, Hkv, N, d]; seq_lens: None or int32 device [P]."""
+    _dev(q, "q", ndim=4)
+    _need(q.dtype in _DT, "q must be float32 or bfloat16")
+    _dev(k, "k", q.dtype, 4)
+    P, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if seq_lens is not None:
+        _dev(seq_lens, "seq_lens", torch.int32, 1)
+    dims = _dims(P, Hq, Hkv, N, d, 64, 1, q.dtype)
+    chi = torch.empty((Hq, d), dtype=torch.float32, device=q.device)
+    chip = torch.empty((P, Hq, d), dtype=torch.float32, device=q.device) if per_prompt else None
+    nbytes = int(L.lib().oal_contrib_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = L.lib().oal_contrib(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(seq_lens), _ptr(chip), _ptr(chi),
+                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
+    L.check(st, "oal_contrib")
+    return (chi, chip) if per_prompt else chi

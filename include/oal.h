@@ -1,0 +1,182 @@
+/*
+ * oal.h -- C ABI of the MI355X (gfx950) library for causal OAL attention.
+ *
+ * OAL ("Not All Dimensions Are Equal: Outlier-Aware Attention Linearization
+ * with Grouped Quadratic Kernels", arXiv 2610.13674) replaces the softmax
+ * kernel by a grouped quadratic kernel.  For a query q and key k of dimension
+ * d_h, with x_r = q_r k_r / sqrt(d_h) (paper, sec. 4.1) and the group sums
+ * s_g = sum_{r in group g} x_r (sec. 4.2):
+ *
+ *     kappa(q, k) = a + sum_g b_g s_g + sum_{g,h} c_gh s_g s_h
+ *
+ * (the dimension-aware kernel of the paper's Eq. (3) with b_r = b_g(r) and
+ * C_rt = c_g(r)g(t), the coefficient sharing of the discussion slides'
+ * "A squared quadratic form guarantees positive weights").  The causal output
+ * is y_i = sum_{j<=i} kappa(q_i,k_j) v_j / sum_{j<=i} kappa(q_i,k_j) (paper,
+ * sec. 2, linear attention; the causal pair set of Eq. (2) includes j = i),
+ * evaluated in linear time through the prefix states of Eq. (5) and the
+ * readout of Eq. (6).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array argument is a caller-owned DEVICE pointer unless stated
+ *    otherwise.  The library never allocates, frees or synchronises, keeps no
+ *    global mutable state and is safe to call from several host threads.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and is complete when that stream is synchronised.
+ *  - Activations are contiguous row-major: q [B, Hq, N, d_h], k [B, Hkv, N,
+ *    d_h], v [B, Hkv, N, d_v], y [B, Hq, N, d_v].  q, k, v and y share the
+ *    element type `dtype` (OAL_F32: float; OAL_BF16: bfloat16 bits).
+ *    Coefficients, pre-map parameters and states are always float32.
+ *  - Query head h reads KV head h / (Hq / Hkv) (GQA with consecutive query
+ *    heads per KV head; the paper's App. B uses the model's native map).
+ *  - Coefficients (device): group_of_dim [Hq, d_h] int32 in [0, G);
+ *    a [Hq]; b [Hq, G]; c [Hq, G, G].  Only the symmetric part of c enters
+ *    the kernel, exactly as in the sum over ordered pairs (g, h).  A group id
+ *    outside [0, G) cannot be detected on the host from device memory: the
+ *    kernels then write NaN to every output of that query head.  Callers that
+ *    hold host copies can check them first with oal_check_coeffs().
+ *  - State layout (per (batch, KV head), float32, `oal_state_floats` floats):
+ *    H [D][d_v] followed by z [D], with D = 1 + d_h + d_h(d_h+1)/2 features in
+ *    the order: 0 = constant, 1 + r = linear term r, then the pairs r <= t in
+ *    row-major upper-triangle order.  Entries are the raw moments of Eq. (5):
+ *    H[f][l] = sum_j phi_f(k_j) v_jl and z[f] = sum_j phi_f(k_j), with
+ *    phi = [1, k_r, k_r k_t]; the packed count is the one of the paper's
+ *    App. D (139,425 floats at d_h = d_v = 64).
+ *  - Supported shapes: d_h in {16, 32, 64}; d_v = 64; 1 <= G <= 8 with any
+ *    group map, or G = d_h singleton groups with diagonal c (the ReBased
+ *    elementwise-square reading).  Others return OAL_ERR_UNSUPPORTED.
+ *  - Every call returns a status; no exception or abort crosses the ABI.
+ *    Arguments are validated on the host before anything is enqueued.  A
+ *    zero-length batch or sequence is valid and enqueues nothing.
+ *  - A denominator <= 0 (possible only when [[a, b^T/2], [b/2, c]] is not
+ *    positive semidefinite) is not trapped: it yields +-Inf or NaN outputs.
+ */
+#ifndef OAL_H
+#define OAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  OAL_OK = 0,
+  OAL_ERR_INVALID_ARG = -1, /* bad dimension, null pointer, Hq % Hkv != 0 ... */
+  OAL_ERR_UNSUPPORTED = -2, /* valid but not implemented (d_h, d_v, G) */
+  OAL_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  OAL_ERR_HIP = -4          /* a HIP launch failed */
+};
+
+enum { OAL_F32 = 0, OAL_BF16 = 1 };
+
+typedef struct oal_dims {
+  int32_t batch;      /* B (prefill, decode: sequences; contrib: prompts P) */
+  int32_t n_q_heads;  /* Hq */
+  int32_t n_kv_heads; /* Hkv, divides Hq */
+  int32_t seq_len;    /* N (prefill and contrib; ignored by decode) */
+  int32_t d_h;        /* query/key head dimension */
+  int32_t d_v;        /* value head dimension */
+  int32_t n_groups;   /* G */
+  int32_t dtype;      /* OAL_F32 or OAL_BF16 */
+} oal_dims;
+
+/* Grouped kernel coefficients, all device pointers (see conventions). */
+typedef struct oal_coeffs {
+  const int32_t* group_of_dim; /* [Hq, d_h] */
+  const float* a;              /* [Hq] */
+  const float* b;              /* [Hq, G] */
+  const float* c;              /* [Hq, G, G] */
+} oal_coeffs;
+
+/* Optional ReBased pre-map x -> gamma * LayerNorm(x) + beta applied to q
+ * and k before the kernel ("Linear Transformers with Learnable Kernel
+ * Functions", section on letting training place the parabola).  LayerNorm
+ * uses the mean and biased variance over d_h and no affine of its own.
+ * Device pointers; pass NULL for the whole struct to disable. */
+typedef struct oal_prep {
+  const float* gamma_q; /* [Hq, d_h] */
+  const float* beta_q;  /* [Hq, d_h] */
+  const float* gamma_k; /* [Hkv, d_h] */
+  const float* beta_k;  /* [Hkv, d_h] */
+  float ln_eps;         /* added to the variance, e.g. 1e-5 */
+} oal_prep;
+
+/* Library version string. */
+const char* oal_version(void);
+
+/* Human-readable name of a status code. */
+const char* oal_status_str(int status);
+
+/* Packed feature count D = 1 + d_h + d_h(d_h+1)/2 (paper, App. D). */
+int64_t oal_feature_count(int32_t d_h);
+
+/* Floats per state block: D * (d_v + 1). */
+int64_t oal_state_floats(int32_t d_h, int32_t d_v);
+
+/* Host helper: maps the factor of the positive group-aware kernel to its
+ * coefficients (paper, sec. 4.3, Eq. (7): kappa = eps + sbar^T L L^T sbar with
+ * sbar = [1, s_1..s_G]; mapping of the discussion slides: with M = L L^T,
+ * a = eps + M_00, b_g = 2 M_0g, c_gh = M_gh).  HOST pointers: L [H, G+1, G+1]
+ * row-major (only the lower triangle is read); outputs a [H], b [H, G],
+ * c [H, G, G].  Computed in double, stored as float. */
+int oal_coeffs_from_factor(int32_t n_heads, int32_t n_groups, double eps, const double* L,
+                           float* a, float* b, float* c);
+
+/* Host helper: checks HOST copies of a group map [Hq, d_h] (every id in
+ * [0, G)) and, when c is non-NULL, that c [Hq, G, G] is finite.  Returns
+ * OAL_OK or OAL_ERR_INVALID_ARG. */
+int oal_check_coeffs(const oal_dims* dims, const int32_t* group_of_dim_host, const float* c_host);
+
+/* Bytes of device workspace oal_fwd needs for `dims` (0 if invalid). */
+size_t oal_fwd_workspace_bytes(const oal_dims* dims);
+
+/* Causal prefill (paper, Eqs. (5)-(6), evaluated chunk by chunk).
+ *   q, k, v, y: activations (see conventions); y is written for all N rows.
+ *   coeffs:     device coefficients; prep: NULL or the ReBased pre-map.
+ *   state_in:   NULL (start from zero) or [B, Hkv, oal_state_floats] initial
+ *               states, so that a call continues an earlier prefix.
+ *   state_out:  NULL or [B, Hkv, oal_state_floats]; receives the states after
+ *               the last token (may not alias state_in).
+ *   workspace:  device scratch of at least oal_fwd_workspace_bytes(dims);
+ *               its contents are undefined after the call.
+ * Calls that share a workspace must be ordered on one stream. */
+int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v,
+            const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, float* state_out,
+            void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One recurrent decode step for `dims->batch` independent sequences (paper,
+ * Eqs. (5)-(6) for a single token): state <- state + phi(k) [v, 1]^T, then
+ * y = (phi_q(q)^T state)[:d_v] / (phi_q(q)^T state)[d_v].  The new token is
+ * part of its own causal prefix.
+ *   q [B, Hq, d_h], k [B, Hkv, d_h], v [B, Hkv, d_v], y [B, Hq, d_v];
+ *   state [B, Hkv, oal_state_floats], updated in place. */
+int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const void* v,
+                    const oal_coeffs* coeffs, const oal_prep* prep, float* state, void* y,
+                    void* stream);
+
+/* Bytes of device workspace oal_contrib needs for `dims` (0 if invalid). */
+size_t oal_contrib_workspace_bytes(const oal_dims* dims);
+
+/* Per-dimension contribution score (paper, sec. 3.1, Eq. (2)):
+ *   chi_{p,r} = mean over causal pairs j <= i < N_p of |q_ir k_jr| / sqrt(d_h),
+ *   chi_r     = equal-weight mean of chi_{p,r} over the P = dims->batch prompts.
+ *   q [P, Hq, N, d_h], k [P, Hkv, N, d_h] (raw, no pre-map); query head h
+ *   pairs with KV head h / (Hq / Hkv).
+ *   seq_lens:       NULL (every prompt has N tokens) or DEVICE int32 [P] with
+ *                   1 <= N_p <= N; rows at and beyond N_p are ignored.  A
+ *                   length outside that range makes the prompt's scores NaN.
+ *   chi_per_prompt: NULL or float [P, Hq, d_h].
+ *   chi_mean:       float [Hq, d_h].
+ * Uses float accumulation of non-negative terms; deterministic. */
+int oal_contrib(const oal_dims* dims, const void* q, const void* k, const int32_t* seq_lens,
+                float* chi_per_prompt, float* chi_mean, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OAL_H */

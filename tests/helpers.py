@@ -1,0 +1,106 @@
+"""Shared helpers for the GPU parity tests (no method arithmetic here).
+
+Coefficient maps are taken separately for each side: the oracle maps (eps, L)
+with its own fp64 routine, the HIP path with the library's host helper.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle as O  # noqa: E402
+
+# Tolerances of the parity bar: max relative error (row-infinity normalised)
+TOL = {"f32": 2e-3, "bf16": 2e-2}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+def require_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+
+
+def to_dev(x, dtype_name):
+    torch = torch_mod()
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(dt).contiguous()
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def oracle_coeffs(wl):
+    if wl.coeff["kind"] == "factor":
+        return O.coeffs_from_factor(wl.coeff["eps"], wl.coeff["L"])
+    return (np.asarray(wl.coeff["a"], np.float64), np.asarray(wl.coeff["b"], np.float64),
+            np.asarray(wl.coeff["c"], np.float64))
+
+
+def gpu_coeffs(wl, groups):
+    import grouped_quadratic_softmax_amd as oal
+    if wl.coeff["kind"] == "factor":
+        a, b, c = oal.coeffs_from_factor(wl.coeff["eps"], wl.coeff["L"])
+    else:
+        a, b, c = wl.coeff["a"], wl.coeff["b"], wl.coeff["c"]
+    return oal.Coeffs(groups, a, b, c)
+
+
+def gpu_prep(wl):
+    import grouped_quadratic_softmax_amd as oal
+    if wl.premap is None:
+        return None
+    p = wl.premap
+    return oal.Prep(p["gamma_q"], p["beta_q"], p["gamma_k"], p["beta_k"], p["ln_eps"])
+
+
+def oracle_prep(wl):
+    if wl.premap is None:
+        return None
+    return {k: (np.asarray(v, np.float64) if not isinstance(v, float) else v) for k, v in wl.premap.items()}
+
+
+def rel_err(y, ref):
+    """max over rows of max_l |y - ref| / max(max_l |ref|, 1e-30) (last axis = l)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.abs(y - ref).max(axis=-1)
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return float((num / den).max())
+
+
+def sample_rows(N, C, n_random, seed):
+    """Every chunk's first and last row, the final row and a seeded random set."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for start in range(0, N, C):
+        rows.add(start)
+        rows.add(min(start + C - 1, N - 1))
+    rows.add(N - 1)
+    rows.update(rng.integers(0, N, size=n_random).tolist())
+    return np.array(sorted(rows))
+
+
+def log(msg):
+    print(msg, flush=True)

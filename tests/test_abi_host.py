@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+entry point, and its host helpers and argument validation behave as
+documented.  No call here reaches a GPU: every error path returns before any
+launch."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oal.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from grouped_quadratic_softmax_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from grouped_quadratic_softmax_amd.build import build
+        build()
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oal_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("oal_fwd", "oal_decode_step", "oal_contrib"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_versions_and_counts(L):
+    lib = L.lib()
+    assert b"gfx950" in lib.oal_version()
+    assert L.status_str(L.OAL_ERR_WORKSPACE) == "OAL_ERR_WORKSPACE"
+    for d in (16, 32, 64):
+        assert lib.oal_feature_count(d) == O.feature_count(d)
+        assert lib.oal_state_floats(d, 64) == O.feature_count(d) * 65
+    assert lib.oal_state_floats(64, 64) == 139425  # OAL slides, state-size slide
+
+
+def test_coeffs_from_factor_matches_oracle(L):
+    import grouped_quadratic_softmax_amd as oal
+    rng = np.random.default_rng(3)
+    for G in (1, 4, 8):
+        Lf = np.tril(rng.uniform(-1, 1, size=(3, G + 1, G + 1)))
+        a, b, c = oal.coeffs_from_factor(1e-3, Lf)
+        ao, bo, co = O.coeffs_from_factor(1e-3, Lf)
+        assert np.allclose(a, ao, rtol=1e-6) and np.allclose(b, bo, rtol=1e-6, atol=1e-7)
+        assert np.allclose(c, co, rtol=1e-6, atol=1e-7)
+
+
+def _dims(L, B=1, Hq=2, Hkv=1, N=8, d=64, dv=64, G=2, dt=1):
+    return L.OalDims(B, Hq, Hkv, N, d, dv, G, dt)
+
+
+def test_check_coeffs(L):
+    lib = L.lib()
+    d = _dims(L)
+    g = np.zeros((2, 64), np.int32)
+    c = np.ones((2, 2, 2), np.float32)
+    vp = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+    assert lib.oal_check_coeffs(ctypes.byref(d), vp(g), vp(c)) == L.OAL_OK
+    g[1, 7] = 2
+    assert lib.oal_check_coeffs(ctypes.byref(d), vp(g), vp(c)) == L.OAL_ERR_INVALID_ARG
+    g[1, 7] = -1
+    assert lib.oal_check_coeffs(ctypes.byref(d), vp(g), vp(c)) == L.OAL_ERR_INVALID_ARG
+    g[1, 7] = 0
+    c[0, 1, 0] = np.inf
+    assert lib.oal_check_coeffs(ctypes.byref(d), vp(g), vp(c)) == L.OAL_ERR_INVALID_ARG
+    with pytest.raises(L.OalError):
+        import grouped_quadratic_softmax_amd as oal
+        oal.Coeffs(np.full((1, 64), 3, np.int32), [1.0], [[1.0, 1.0]], [[[1, 0], [0, 1]]], device="cpu")
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
+
+
+def _fwd(L, dims, coeffs=True, ws=(FAKE, 1 << 40), q=FAKE, y=FAKE, state_in=None, state_out=None, prep=None):
+    lib = L.lib()
+    cs = L.OalCoeffs(0x1000, 0x1000, 0x1000, 0x1000) if coeffs else None
+    return lib.oal_fwd(ctypes.byref(dims) if dims is not None else None, q, FAKE, FAKE,
+                       ctypes.byref(cs) if cs is not None else None,
+                       ctypes.byref(prep) if prep is not None else None, state_in, state_out, y, ws[0],
+                       ctypes.c_size_t(ws[1]), None)
+
+
+def test_fwd_validation_errors(L):
+    E, U, W = L.OAL_ERR_INVALID_ARG, L.OAL_ERR_UNSUPPORTED, L.OAL_ERR_WORKSPACE
+    assert _fwd(L, None) == E
+    assert _fwd(L, _dims(L, Hq=3, Hkv=2)) == E           # Hq % Hkv
+    assert _fwd(L, _dims(L, N=-1)) == E
+    assert _fwd(L, _dims(L, B=-1)) == E
+    assert _fwd(L, _dims(L, dt=7)) == E
+    assert _fwd(L, _dims(L, d=48)) == U                  # unsupported head dim
+    assert _fwd(L, _dims(L, dv=32)) == U
+    assert _fwd(L, _dims(L, G=0)) == E
+    assert _fwd(L, _dims(L, G=65)) == E
+    assert _fwd(L, _dims(L, G=9)) == U
+    assert _fwd(L, _dims(L), coeffs=False) == E
+    assert _fwd(L, _dims(L), q=None) == E
+    assert _fwd(L, _dims(L), y=None) == E
+    assert _fwd(L, _dims(L), ws=(None, 0)) == W
+    need = L.lib().oal_fwd_workspace_bytes(ctypes.byref(_dims(L)))
+    assert need > 0
+    assert _fwd(L, _dims(L), ws=(FAKE, need - 1)) == W
+    assert _fwd(L, _dims(L), state_in=FAKE, state_out=FAKE) == E  # aliasing
+    bad_prep = L.OalPrep(0x1000, 0, 0x1000, 0x1000, 1e-5)
+    assert _fwd(L, _dims(L), prep=bad_prep) == E
+    assert _fwd(L, _dims(L, B=0)) == L.OAL_OK                     # empty batch: nothing enqueued
+
+
+def test_workspace_sizes(L):
+    lib = L.lib()
+    # one internal snapshot per 64-token chunk and (batch, KV head), bf16
+    d = _dims(L, B=4, Hq=14, Hkv=2, N=2048, G=4)
+    kb = 71  # K-blocks of 32 features at d_h = 64
+    assert lib.oal_fwd_workspace_bytes(ctypes.byref(d)) == 32 * 8 * kb * 65 * 32 * 2
+    assert lib.oal_fwd_workspace_bytes(None) == 0
+    assert lib.oal_contrib_workspace_bytes(ctypes.byref(_dims(L, B=2, N=3000))) > 0
+
+
+def test_decode_and_contrib_validation(L):
+    lib = L.lib()
+    cs = L.OalCoeffs(0x1000, 0x1000, 0x1000, 0x1000)
+    d = _dims(L, B=2)
+    assert lib.oal_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == \
+        L.OAL_ERR_INVALID_ARG
+    assert lib.oal_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(cs), None, None, FAKE, None) == \
+        L.OAL_ERR_INVALID_ARG
+    assert lib.oal_decode_step(ctypes.byref(_dims(L, Hq=18, Hkv=2)), FAKE, FAKE, FAKE, ctypes.byref(cs), None,
+                               FAKE, FAKE, None) == L.OAL_ERR_UNSUPPORTED
+    assert lib.oal_decode_step(ctypes.byref(_dims(L, B=0)), FAKE, FAKE, FAKE, ctypes.byref(cs), None, FAKE, FAKE,
+                               None) == L.OAL_OK
+    ws = ctypes.c_size_t(1 << 30)
+    assert lib.oal_contrib(ctypes.byref(_dims(L, B=0)), FAKE, FAKE, None, None, FAKE, FAKE, ws, None) == \
+        L.OAL_ERR_INVALID_ARG
+    assert lib.oal_contrib(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, ws, None) == L.OAL_ERR_INVALID_ARG
+    assert lib.oal_contrib(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, None, ctypes.c_size_t(0), None) == \
+        L.OAL_ERR_WORKSPACE
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        oal.contrib(x, x)

@@ -1,0 +1,81 @@
+"""GPU parity of oal_contrib (contribution score, Eq. (2)) against the oracle."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+from helpers import log, require_gpu, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _contrib(q, k, lens, dtype):
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    sl = None if lens is None else torch.as_tensor(np.asarray(lens, np.int32)).cuda()
+    chi, chip = oal.contrib(to_dev(q, dtype), to_dev(k, dtype), sl, per_prompt=True)
+    return to_np(chi), to_np(chip)
+
+
+@pytest.mark.parametrize("d", [16, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_contrib_bruteforce_varlen_gqa(d, dtype):
+    require_gpu()
+    rng = np.random.default_rng(40 + d)
+    P, Hq, Hkv, N = 3, 4, 2, 37
+    q = rng.standard_normal((P, Hq, N, d)).astype(np.float32)
+    k = rng.standard_normal((P, Hkv, N, d)).astype(np.float32)
+    q[..., 3] *= 9
+    if dtype == "bf16":
+        q, k = S.bf16_round(q), S.bf16_round(k)
+    lens = [37, 20, 1]
+    per, mean = O.chi_bruteforce(q, k, lens)
+    chi, chip = _contrib(q, k, lens, dtype)
+    log(f"[chi] d={d} {dtype} err {np.abs(chip / per - 1).max():.2e}")
+    assert np.allclose(chip, per, rtol=1e-4, atol=0)
+    assert np.allclose(chi, mean, rtol=1e-4, atol=0)
+
+
+def test_contrib_blocks_and_ragged_length():
+    require_gpu()
+    rng = np.random.default_rng(44)
+    P, Hq, Hkv, N, d = 2, 6, 3, 2500, 32
+    q = S.bf16_round(rng.standard_normal((P, Hq, N, d)).astype(np.float32))
+    k = S.bf16_round(rng.standard_normal((P, Hkv, N, d)).astype(np.float32))
+    lens = [2500, 1027]
+    per, mean = O.chi_separable(q, k, lens)
+    chi, chip = _contrib(q, k, lens, "bf16")
+    assert np.allclose(chip, per, rtol=1e-4)
+    assert np.allclose(chi, mean, rtol=1e-4)
+
+
+def test_contrib_c2_full():
+    require_gpu()
+    wl = S.make(2)
+    per, mean = O.chi_separable(wl.q, wl.k)
+    chi, chip = _contrib(wl.q, wl.k, None, "bf16")
+    assert np.allclose(chip, per, rtol=1e-4)
+    assert np.allclose(chi, mean, rtol=1e-4)
+    # the planted outlier dims carry the largest scores of their heads
+    for h in range(wl.n_q_heads):
+        top = set(np.argsort(chi[h])[-2:].tolist())
+        assert top == set(wl.outlier_dims[h // 7].tolist())
+
+
+def test_contrib_c5_full():
+    require_gpu()
+    wl = S.make(5)
+    per, mean = O.chi_separable(wl.q, wl.k)
+    chi, _ = _contrib(wl.q, wl.k, None, "bf16")
+    log(f"[chi] c5 err {np.abs(chi / mean - 1).max():.2e}")
+    assert np.allclose(chi, mean, rtol=1e-4)
+
+
+def test_contrib_bad_length_gives_nan_for_that_prompt_only():
+    require_gpu()
+    rng = np.random.default_rng(45)
+    q = rng.standard_normal((2, 2, 20, 16)).astype(np.float32)
+    k = rng.standard_normal((2, 2, 20, 16)).astype(np.float32)
+    _, chip = _contrib(q, k, [20, 21], "f32")
+    assert np.isfinite(chip[0]).all() and np.isnan(chip[1]).all()

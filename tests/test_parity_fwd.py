@@ -1,0 +1,169 @@
+"""GPU parity of oal_fwd (chunked causal prefill) against the fp64 oracle.
+
+Small cases compare every output row; the full-size workloads run exactly as
+the benchmark launches them and compare a seeded sample of rows (every chunk
+boundary where affordable, the last row, random rows).
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+from helpers import (TOL, gpu_coeffs, gpu_prep, log, oracle_coeffs, oracle_prep, rel_err, require_gpu,
+                     sample_rows, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_case(wl, groups=None, rows=None, tol=None):
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    groups = wl.group_of_dim if groups is None else groups
+    log(f"[fwd] {wl.name} B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} N={wl.seq_len} d={wl.d_h} "
+        f"G={wl.n_groups} {wl.dtype} rows={'all' if rows is None else len(rows)}")
+    q, k, v = to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype), to_dev(wl.v, wl.dtype)
+    y = to_np(oal.fwd(q, k, v, gpu_coeffs(wl, groups), gpu_prep(wl)))
+    a, b, c = oracle_coeffs(wl)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, groups, a, b, c, oracle_prep(wl), rows=rows)
+    got = y if rows is None else y[:, :, rows]
+    err = rel_err(got, ref)
+    log(f"[fwd]   max rel err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= (tol or TOL[wl.dtype]), err
+    return y
+
+
+def test_c1_fp32_full():
+    _run_case(S.make(1))
+
+
+def test_c1_fp32_ragged():
+    _run_case(S.make(1, seq_len=200))
+
+
+def test_c2_gqa_bf16_small():
+    _run_case(S.make(2, batch=2, seq_len=300))
+
+
+def test_c2_gqa_fp32_small():
+    _run_case(S.make(2, batch=1, seq_len=130, dtype="f32"))
+
+
+def test_c3_taylor_d16_small():
+    _run_case(S.make(3, batch=2, n_q_heads=4, n_kv_heads=4, seq_len=333))
+
+
+def test_c3_taylor_d16_fp32():
+    _run_case(S.make(3, batch=1, n_q_heads=2, n_kv_heads=2, seq_len=200, dtype="f32"))
+
+
+def test_c4_rebased_squared_dot_premap():
+    _run_case(S.make(4, batch=2, n_q_heads=2, n_kv_heads=2, seq_len=150, rebased_reading="d"))
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 129])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_lengths(N, dtype):
+    _run_case(S.make(2, batch=2, n_q_heads=4, n_kv_heads=2, seq_len=N, dtype=dtype))
+
+
+def _d32_workload(dtype="bf16"):
+    # d_h = 32 variant of the outlier workload (seeded, same recipe)
+    rng = np.random.default_rng(1032)
+    B, Hq, Hkv, N, d, dv, G = 2, 4, 2, 150, 32, 64, 3
+    q = rng.standard_normal((B, Hq, N, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, N, dv)).astype(np.float32)
+    q[..., [5, 20]] *= 6
+    k[..., [5, 20]] *= 6
+    if dtype == "bf16":
+        q, k, v = S.bf16_round(q), S.bf16_round(k), S.bf16_round(v)
+    groups = np.tile(np.array([2 if r in (5, 20) else r % 2 for r in range(d)], np.int32), (Hq, 1))
+    Ls = np.stack([np.tril(rng.uniform(0.2, 1.0, size=(G + 1, G + 1))) for _ in range(Hq)])
+    return S.Workload("d32", B, Hq, Hkv, N, d, dv, dtype, q, k, v, G, groups,
+                      {"kind": "factor", "eps": 1e-3, "L": Ls})
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_d32(dtype):
+    _run_case(_d32_workload(dtype))
+
+
+def _groups_from_gpu_chi(wl, q, k):
+    import grouped_quadratic_softmax_amd as oal
+    chi = oal.contrib(q, k).cpu().numpy()
+    return oal.groups_from_contribution(chi, wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"])
+
+
+def test_c5_eight_groups_small():
+    require_gpu()
+    wl = S.make(5, n_q_heads=4, n_kv_heads=4, seq_len=260)
+    groups = _groups_from_gpu_chi(wl, to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype))
+    assert groups.max() == 7
+    _run_case(wl, groups=groups)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_state_out_and_continuation(dtype):
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    wl = S.make(2, batch=2, n_q_heads=4, n_kv_heads=2, seq_len=190, dtype=dtype)
+    co = gpu_coeffs(wl, wl.group_of_dim)
+    q, k, v = to_dev(wl.q, dtype), to_dev(wl.k, dtype), to_dev(wl.v, dtype)
+    n1 = 100
+    y_full, s_full = oal.fwd(q, k, v, co, return_state=True)
+    y1, s1 = oal.fwd(q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(), co,
+                     return_state=True)
+    y2, s2 = oal.fwd(q[:, :, n1:].contiguous(), k[:, :, n1:].contiguous(), v[:, :, n1:].contiguous(), co,
+                     state_in=s1, return_state=True)
+    y_cat = np.concatenate([to_np(y1), to_np(y2)], axis=2)
+    a, b, c = oracle_coeffs(wl)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)
+    assert rel_err(y_cat, ref) <= TOL[dtype]
+    assert rel_err(to_np(y_full), ref) <= TOL[dtype]
+    # final state against the oracle's raw Eq. (5) moments
+    D = O.feature_count(wl.d_h)
+    for bi in range(wl.batch):
+        for kh in range(wl.n_kv_heads):
+            ref_s = O.abi_state_from_matrix(O.state_from_prefix(wl.k[bi, kh], wl.v[bi, kh]))
+            for got in (to_np(s_full)[bi, kh], to_np(s2)[bi, kh]):
+                scale = np.abs(ref_s).max()
+                assert np.abs(got - ref_s).max() <= 1e-5 * scale, (bi, kh)
+    assert to_np(s_full).shape[-1] == D * 65
+
+
+def test_zero_length_passes_state_through():
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    wl = S.make(2, batch=2, n_q_heads=4, n_kv_heads=2, seq_len=70)
+    co = gpu_coeffs(wl, wl.group_of_dim)
+    q, k, v = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+    _, s = oal.fwd(q, k, v, co, return_state=True)
+    e = lambda t: t[:, :, :0].contiguous()
+    _, s0 = oal.fwd(e(q), e(k), e(v), co, state_in=s, return_state=True)
+    assert torch.equal(s0, s)
+    _, z = oal.fwd(e(q), e(k), e(v), co, return_state=True)
+    assert float(z.abs().max()) == 0.0
+
+
+# ------------------------------------------------------------- full sizes
+
+def test_c2_full_size_sampled():
+    wl = S.make(2)
+    _run_case(wl, rows=sample_rows(wl.seq_len, 64, 64, seed=2))
+
+
+def test_c3_full_size_sampled():
+    wl = S.make(3)
+    _run_case(wl, rows=sample_rows(wl.seq_len, 512, 48, seed=3))
+
+
+def test_c5_full_size_sampled():
+    require_gpu()
+    wl = S.make(5)
+    groups = _groups_from_gpu_chi(wl, to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype))
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.integers(0, wl.seq_len, 40), [0, 63, 64, 4095, 4096, wl.seq_len - 1]]))
+    _run_case(wl, groups=groups, rows=rows)
