@@ -8,6 +8,9 @@ from ._lib import OalError, lib  # noqa: F401
 from .grouping import groups_from_contribution  # noqa: F401
 from .ops import (  # noqa: F401
     Coeffs,
+    ContribPlan,
+    DecodePlan,
+    PrefillPlan,
     Prep,
     coeffs_from_factor,
     contrib,

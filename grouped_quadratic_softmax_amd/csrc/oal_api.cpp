@@ -114,27 +114,35 @@ size_t oal_fwd_workspace_bytes(const oal_dims* dims) {
   return oal::fwd_workspace_bytes(dims->batch, dims->n_kv_heads, dims->seq_len, dims->d_h, dims->dtype);
 }
 
-int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v, const oal_coeffs* coeffs,
-            const oal_prep* prep, const float* state_in, float* state_out, void* y, void* workspace,
-            size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared validation and dispatch of oal_fwd and its two stages.
+// stages: bit 0 = chunk states, bit 1 = outputs.
+int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v, const oal_coeffs* coeffs,
+               const oal_prep* prep, const float* state_in, float* state_out, void* y, void* workspace,
+               size_t workspace_bytes, void* stream, int stages) {
+  const bool want_states = stages & 1, want_out = stages & 2;
   int st = check_dims(dims, true);
   if (st != OAL_OK) return st;
-  if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
-  if ((st = check_coeff_ptrs(coeffs)) != OAL_OK) return st;
+  if (want_out) {
+    if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
+    if ((st = check_coeff_ptrs(coeffs)) != OAL_OK) return st;
+    if (dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
+  }
   if ((st = check_prep(prep)) != OAL_OK) return st;
-  if (dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
   if (dims->batch == 0) return OAL_OK;
   if (dims->seq_len == 0) {
     // nothing to attend to; the state passes through unchanged
-    if (state_out != nullptr) {
+    if (want_states && state_out != nullptr) {
       const long n = (long)dims->batch * dims->n_kv_heads * oal_state_floats(dims->d_h, dims->d_v);
       if (oal::launch_state_passthrough(state_in, state_out, n, (hipStream_t)stream) != hipSuccess)
         return OAL_ERR_HIP;
     }
     return OAL_OK;
   }
-  if (q == nullptr || k == nullptr || v == nullptr || y == nullptr) return OAL_ERR_INVALID_ARG;
-  if (state_out != nullptr && state_out == state_in) return OAL_ERR_INVALID_ARG;
+  if (k == nullptr || v == nullptr) return OAL_ERR_INVALID_ARG;
+  if (want_out && (q == nullptr || y == nullptr)) return OAL_ERR_INVALID_ARG;
+  if (want_states && state_out != nullptr && state_out == state_in) return OAL_ERR_INVALID_ARG;
   const size_t need = oal_fwd_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need) return OAL_ERR_WORKSPACE;
 
@@ -142,14 +150,37 @@ int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v, c
   a.B = dims->batch; a.Hq = dims->n_q_heads; a.Hkv = dims->n_kv_heads; a.N = dims->seq_len;
   a.d_h = dims->d_h; a.G = dims->n_groups; a.dtype = dims->dtype;
   a.q = q; a.k = k; a.v = v;
-  a.group_of_dim = coeffs->group_of_dim; a.ca = coeffs->a; a.cb = coeffs->b; a.cc = coeffs->c;
+  if (want_out) {
+    a.group_of_dim = coeffs->group_of_dim; a.ca = coeffs->a; a.cb = coeffs->b; a.cc = coeffs->c;
+  }
   a.premap = prep != nullptr;
   if (prep) {
     a.gamma_q = prep->gamma_q; a.beta_q = prep->beta_q; a.gamma_k = prep->gamma_k; a.beta_k = prep->beta_k;
     a.ln_eps = prep->ln_eps;
   }
   a.state_in = state_in; a.state_out = state_out; a.y = y; a.workspace = workspace;
-  return oal::launch_fwd(a, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
+  return oal::launch_fwd(a, stages, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
+}
+
+}  // namespace
+
+int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v, const oal_coeffs* coeffs,
+            const oal_prep* prep, const float* state_in, float* state_out, void* y, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  return fwd_stages(dims, q, k, v, coeffs, prep, state_in, state_out, y, workspace, workspace_bytes, stream, 3);
+}
+
+int oal_fwd_states(const oal_dims* dims, const void* k, const void* v, const oal_prep* prep,
+                   const float* state_in, float* state_out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return fwd_stages(dims, nullptr, k, v, nullptr, prep, state_in, state_out, nullptr, workspace,
+                    workspace_bytes, stream, 1);
+}
+
+int oal_fwd_outputs(const oal_dims* dims, const void* q, const void* k, const void* v,
+                    const oal_coeffs* coeffs, const oal_prep* prep, void* y, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return fwd_stages(dims, q, k, v, coeffs, prep, nullptr, nullptr, y, workspace, workspace_bytes, stream, 2);
 }
 
 int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const void* v,

@@ -133,7 +133,8 @@ __global__ __launch_bounds__(64) void contrib_combine_kernel(const float* __rest
       kc += x[2 * R * DH + r];
     }
     const float pairs = 0.5f * (float)n * (float)(n + 1);
-    const float chi = tot * inv_sqrt_d / pairs;
+    const bool badlen = n < 1 || n > N;
+    const float chi = badlen ? __builtin_nanf("") : tot * inv_sqrt_d / pairs;
     if (chi_per_prompt) chi_per_prompt[((long)p * Hq + h) * DH + r] = chi;
     mean += chi;
   }

@@ -201,13 +201,26 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
           av[0] = r0.x * t0.x; av[1] = r0.y * t0.y; av[2] = r0.z * t0.z; av[3] = r0.w * t0.w;
           av[4] = r1.x * t1.x; av[5] = r1.y * t1.y; av[6] = r1.z * t1.z; av[7] = r1.w * t1.w;
         }
-        const Frag<BF> A = frag_from<BF>(av);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) mma(acc[nt], A, frag_load(&vT[(16 * nt + l16) * VP + jb]));
         float ones[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ones[e] = l16 == 0 ? kT[DH * CP + jb + e] : 0.f;
-        mma(acc[4], A, frag_from<BF>(ones));
+        const Frag<BF> O1 = frag_from<BF>(ones);
+        const Frag<BF> A = frag_from<BF>(av);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) mma(acc[nt], A, frag_load(&vT[(16 * nt + l16) * VP + jb]));
+        mma(acc[4], A, O1);
+        if constexpr (BF) {
+          // a product of two bf16 values has at most 16 significant bits, so
+          // hi + lo (both bf16) carries it exactly: the update is then exact
+          // up to fp32 accumulation, like the fp32 path.
+          float lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lo[e] = av[e] - (float)A.v[e];
+          const Frag<BF> Al = frag_from<BF>(lo);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) mma(acc[nt], Al, frag_load(&vT[(16 * nt + l16) * VP + jb]));
+          mma(acc[4], Al, O1);
+        }
       }
     }
     __syncthreads();
@@ -567,7 +580,7 @@ __global__ __launch_bounds__(256) void out_kernel(
 // --------------------------------------------------------------------------
 
 template <typename T, int DH, int C>
-static hipError_t launch_fwd_t(const FwdLaunch& a, hipStream_t stream) {
+static hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   typedef typename FragStore<T>::type ST;
   const int nchunks = (a.N + C - 1) / C;
   const int BH = a.B * a.Hkv;
@@ -577,7 +590,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a, hipStream_t stream) {
   const T* kk = reinterpret_cast<const T*>(a.k);
   const T* vv = reinterpret_cast<const T*>(a.v);
   T* yy = reinterpret_cast<T*>(a.y);
-  {
+  if (stages & 1) {
     dim3 grid((MT + 3) / 4, BH);
     if (a.premap)
       hipLaunchKernelGGL((scan_kernel<T, DH, C, true>), grid, dim3(256), 0, stream, kk, vv, a.gamma_k,
@@ -588,6 +601,7 @@ static hipError_t launch_fwd_t(const FwdLaunch& a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  if (!(stages & 2)) return hipSuccess;
   dim3 grid(nchunks, a.Hq, a.B);
 #define OAL_OUT(NGV, PM)                                                                              \
   hipLaunchKernelGGL((out_kernel<T, DH, C, NGV, PM>), grid, dim3(256), 0, stream, qq, kk, vv,         \
@@ -634,18 +648,18 @@ size_t fwd_workspace_bytes(int B, int Hkv, int N, int d_h, int dtype) {
   return (size_t)nchunks * B * Hkv * snap_elems(d_h, DV) * elem;
 }
 
-hipError_t launch_fwd(const FwdLaunch& a, hipStream_t stream) {
+hipError_t launch_fwd(const FwdLaunch& a, int stages, hipStream_t stream) {
   if (a.dtype == 1) {
     switch (a.d_h) {
-      case 16: return launch_fwd_t<uint16_t, 16, kChunk>(a, stream);
-      case 32: return launch_fwd_t<uint16_t, 32, kChunk>(a, stream);
-      default: return launch_fwd_t<uint16_t, 64, kChunk>(a, stream);
+      case 16: return launch_fwd_t<uint16_t, 16, kChunk>(a, stages, stream);
+      case 32: return launch_fwd_t<uint16_t, 32, kChunk>(a, stages, stream);
+      default: return launch_fwd_t<uint16_t, 64, kChunk>(a, stages, stream);
     }
   }
   switch (a.d_h) {
-    case 16: return launch_fwd_t<float, 16, kChunk>(a, stream);
-    case 32: return launch_fwd_t<float, 32, kChunk>(a, stream);
-    default: return launch_fwd_t<float, 64, kChunk>(a, stream);
+    case 16: return launch_fwd_t<float, 16, kChunk>(a, stages, stream);
+    case 32: return launch_fwd_t<float, 32, kChunk>(a, stages, stream);
+    default: return launch_fwd_t<float, 64, kChunk>(a, stages, stream);
   }
 }
 

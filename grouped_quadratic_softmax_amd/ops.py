@@ -197,3 +197,90 @@ def contrib(q, k, seq_lens=None, per_prompt=False, workspace=None):
                              _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
     L.check(st, "oal_contrib")
     return (chi, chip) if per_prompt else chi
+
+
+class PrefillPlan:
+    """Pre-marshalled oal_fwd arguments for repeated calls on fixed buffers.
+
+    ``states()`` and ``outputs()`` enqueue the two stages of oal_fwd
+    (``run()`` both) on the stream that is current at construction time.
+    """
+
+    def __init__(self, q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None,
+                 with_state=True):
+        import torch
+        B, Hq, N, d = q.shape
+        Hkv, dv = k.shape[1], v.shape[3]
+        self.q, self.k, self.v, self.coeffs, self.prep = q, k, v, coeffs, prep
+        self.y = torch.empty((B, Hq, N, dv), dtype=q.dtype, device=q.device)
+        self.state_in = state_in
+        self.state_out = (torch.empty((B, Hkv, state_floats(d, dv)), dtype=torch.float32, device=q.device)
+                          if with_state else None)
+        self.dims = _dims(B, Hq, Hkv, N, d, dv, coeffs.n_groups, q.dtype)
+        nbytes = int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(self.dims)))
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        self._cs = coeffs.struct()
+        self._ps = prep.struct() if prep is not None else None
+        pp = ctypes.byref(self._ps) if self._ps is not None else None
+        ws = (_ptr(self.workspace), ctypes.c_size_t(self.workspace.numel()))
+        st = _stream()
+        self._states_args = (ctypes.byref(self.dims), _ptr(k), _ptr(v), pp, _ptr(state_in), _ptr(self.state_out),
+                             *ws, st)
+        self._out_args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(self._cs), pp,
+                          _ptr(self.y), *ws, st)
+        self._lib = L.lib()
+
+    def states(self):
+        L.check(self._lib.oal_fwd_states(*self._states_args), "oal_fwd_states")
+
+    def outputs(self):
+        L.check(self._lib.oal_fwd_outputs(*self._out_args), "oal_fwd_outputs")
+
+    def run(self):
+        self.states()
+        self.outputs()
+        return self.y
+
+
+class DecodePlan:
+    """Pre-marshalled oal_decode_step arguments (state updated in place)."""
+
+    def __init__(self, q, k, v, coeffs: Coeffs, state, prep: Optional[Prep] = None):
+        import torch
+        B, Hq, d = q.shape
+        Hkv, dv = k.shape[1], v.shape[2]
+        self.y = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+        self.dims = _dims(B, Hq, Hkv, 0, d, dv, coeffs.n_groups, q.dtype)
+        self._keep = (q, k, v, coeffs, state, prep)
+        self._cs = coeffs.struct()
+        self._ps = prep.struct() if prep is not None else None
+        pp = ctypes.byref(self._ps) if self._ps is not None else None
+        self._args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(self._cs), pp, _ptr(state),
+                      _ptr(self.y), _stream())
+        self._lib = L.lib()
+
+    def run(self):
+        L.check(self._lib.oal_decode_step(*self._args), "oal_decode_step")
+        return self.y
+
+
+class ContribPlan:
+    """Pre-marshalled oal_contrib arguments."""
+
+    def __init__(self, q, k, seq_lens=None, per_prompt=False):
+        import torch
+        P, Hq, N, d = q.shape
+        Hkv = k.shape[1]
+        self.dims = _dims(P, Hq, Hkv, N, d, 64, 1, q.dtype)
+        self.chi = torch.empty((Hq, d), dtype=torch.float32, device=q.device)
+        self.chi_per_prompt = torch.empty((P, Hq, d), dtype=torch.float32, device=q.device) if per_prompt else None
+        nbytes = int(L.lib().oal_contrib_workspace_bytes(ctypes.byref(self.dims)))
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        self._keep = (q, k, seq_lens)
+        self._args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(seq_lens), _ptr(self.chi_per_prompt),
+                      _ptr(self.chi), _ptr(self.workspace), ctypes.c_size_t(self.workspace.numel()), _stream())
+        self._lib = L.lib()
+
+    def run(self):
+        L.check(self._lib.oal_contrib(*self._args), "oal_contrib")
+        return self.chi

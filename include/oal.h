@@ -147,6 +147,23 @@ int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v,
             const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, float* state_out,
             void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two stages of oal_fwd, for callers that schedule or time them
+ * separately.  oal_fwd(...) is exactly oal_fwd_states(...) followed by
+ * oal_fwd_outputs(...) on the same stream with the same workspace.
+ *   oal_fwd_states:  the prefix states of Eq. (5) at every chunk start, kept
+ *                    in the workspace (and the final state in state_out).
+ *   oal_fwd_outputs: the Eq. (6) readout against those states plus the
+ *                    within-chunk pairs, normalised into y.  The workspace
+ *                    must hold the states of a preceding oal_fwd_states call
+ *                    with the same dims, k, v, prep and state_in.
+ * Arguments and errors as for oal_fwd. */
+int oal_fwd_states(const oal_dims* dims, const void* k, const void* v, const oal_prep* prep,
+                   const float* state_in, float* state_out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+int oal_fwd_outputs(const oal_dims* dims, const void* q, const void* k, const void* v,
+                    const oal_coeffs* coeffs, const oal_prep* prep, void* y, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step for `dims->batch` independent sequences (paper,
  * Eqs. (5)-(6) for a single token): state <- state + phi(k) [v, 1]^T, then
  * y = (phi_q(q)^T state)[:d_v] / (phi_q(q)^T state)[d_v].  The new token is

@@ -167,3 +167,18 @@ def test_c5_full_size_sampled():
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([rng.integers(0, wl.seq_len, 40), [0, 63, 64, 4095, 4096, wl.seq_len - 1]]))
     _run_case(wl, groups=groups, rows=rows)
+
+
+def test_stages_compose_to_fwd_bitwise():
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    wl = S.make(2, batch=2, n_q_heads=14, n_kv_heads=2, seq_len=250)
+    co = gpu_coeffs(wl, wl.group_of_dim)
+    q, k, v = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+    y, st = oal.fwd(q, k, v, co, return_state=True)
+    plan = oal.PrefillPlan(q, k, v, co)
+    plan.states()
+    plan.outputs()
+    torch.cuda.synchronize()
+    assert torch.equal(plan.y, y) and torch.equal(plan.state_out, st)
