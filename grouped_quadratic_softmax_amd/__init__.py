@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     coeffs_from_factor,
     contrib,
     decode_step,
+    decode_workspace_bytes,
     feature_count,
     fwd,
     fwd_workspace_bytes,

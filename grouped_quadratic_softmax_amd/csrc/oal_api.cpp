@@ -183,8 +183,15 @@ int oal_fwd_outputs(const oal_dims* dims, const void* q, const void* k, const vo
   return fwd_stages(dims, q, k, v, coeffs, prep, nullptr, nullptr, y, workspace, workspace_bytes, stream, 2);
 }
 
+size_t oal_decode_workspace_bytes(const oal_dims* dims) {
+  if (check_dims(dims, false) != OAL_OK) return 0;
+  if (dims->n_q_heads / dims->n_kv_heads > 8) return 0;
+  return oal::decode_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->d_h);
+}
+
 int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const void* v,
-                    const oal_coeffs* coeffs, const oal_prep* prep, float* state, void* y, void* stream) {
+                    const oal_coeffs* coeffs, const oal_prep* prep, float* state, void* y, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   int st = check_dims(dims, false);
   if (st != OAL_OK) return st;
   if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
@@ -194,6 +201,8 @@ int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const vo
   if (dims->batch == 0) return OAL_OK;
   if (q == nullptr || k == nullptr || v == nullptr || state == nullptr || y == nullptr)
     return OAL_ERR_INVALID_ARG;
+  const size_t need = oal_decode_workspace_bytes(dims);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return OAL_ERR_WORKSPACE;
   oal::DecodeLaunch a{};
   a.B = dims->batch; a.Hq = dims->n_q_heads; a.Hkv = dims->n_kv_heads; a.d_h = dims->d_h;
   a.G = dims->n_groups; a.dtype = dims->dtype;
@@ -204,7 +213,7 @@ int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const vo
     a.gamma_q = prep->gamma_q; a.beta_q = prep->beta_q; a.gamma_k = prep->gamma_k; a.beta_k = prep->beta_k;
     a.ln_eps = prep->ln_eps;
   }
-  a.state = state; a.y = y;
+  a.state = state; a.y = y; a.workspace = workspace;
   return oal::launch_decode(a, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
 }
 

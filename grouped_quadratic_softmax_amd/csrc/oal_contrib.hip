@@ -7,11 +7,18 @@
 //   A = sum |q|,  B = sum_i |q_i| * (prefix of |k| inside the segment),  K = sum |k|
 // and two adjacent segments L, R combine in order as
 //   (A_L + A_R, B_L + B_R + K_L A_R, K_L + K_R).
-// Lanes of a wave are (token slot, dimension); each lane scans its slot's
-// tokens sequentially (coalesced rows), the slots of a wave are combined with
-// wavefront shuffles, the four waves of a CTA through LDS, and the CTAs of a
-// prompt by a second, sequential kernel.  All terms are non-negative, so fp32
-// accumulation has no cancellation; the result is deterministic.
+//
+// Kernel 1 (partial): one CTA per (token block, KV head, prompt).  Its 256
+// threads are (d_h / 4) dimension quads x token slots; slot s scans a
+// contiguous run of the block's tokens (for bf16 d_h = 64 every row load is
+// one full 128-byte line), the slots of a wave are combined in order with
+// wavefront shuffles, the four waves through LDS, and the block triple goes
+// to the workspace.
+// Kernel 2 (combine): one CTA per query head folds the block triples of each
+// prompt in token order (four contiguous quarters, then an ordered combine
+// of the four), normalises, and averages over prompts with equal weights.
+// All terms are non-negative, so fp32 accumulation has no cancellation; the
+// result is deterministic.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -21,143 +28,215 @@
 
 namespace oal {
 
-constexpr int kContribTB = 1024;  // tokens per CTA (256 per wave)
+namespace {
+
+// Four consecutive activation values as floats.
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xffff0000u));
+}
+
+__device__ __forceinline__ void abs_acc(float (&a)[4], const float4 x) {
+  a[0] += fabsf(x.x);
+  a[1] += fabsf(x.y);
+  a[2] += fabsf(x.z);
+  a[3] += fabsf(x.w);
+}
+
+}  // namespace
+
+// Tokens per partial block: the smallest power of two >= 64 that keeps the
+// number of blocks per prompt at or below 64.
+static int contrib_block_tokens(int N) {
+  int tb = 64;
+  while ((long)tb * 64 < (long)N) tb *= 2;
+  return tb;
+}
 
 template <typename T, int DH, int RMAX>
 __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restrict__ q,
                                                               const T* __restrict__ k,
                                                               const int32_t* __restrict__ seq_lens,
                                                               float* __restrict__ part, int Hq,
-                                                              int Hkv, int N, int nblk) {
-  constexpr int S = kWave / DH;          // token slots per wave
-  constexpr int TW = kContribTB / 4;     // tokens per wave
-  constexpr int TS = TW / S;             // tokens per slot
-  constexpr int NV = 2 * RMAX + 1;       // A[R], B[R], K
+                                                              int Hkv, int N, int nblk, int TB) {
+  constexpr int NQ4 = DH / 4;                  // dimension quads per row
+  constexpr int TPQ = 256 / NQ4;               // token slots per CTA
+  constexpr int SPW = kWave / NQ4;             // token slots per wave
+  constexpr int NV = 2 * RMAX + 1;             // A[R], B[R], K
   __shared__ float xs[4][NV][DH];
 
   const int blk = blockIdx.x, kvh = blockIdx.y, p = blockIdx.z;
   const int R = Hq / Hkv;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int slot = lane / DH, r = lane % DH;
+  const int quad = lane % NQ4, wslot = lane / NQ4;
+  const int slot = wave * SPW + wslot;
   int n = seq_lens ? seq_lens[p] : N;
   const bool badlen = n < 1 || n > N;
   if (badlen) n = 0;
 
-  float A[RMAX], Bs[RMAX], K = 0.f;
+  float A[RMAX][4], Bs[RMAX][4], K[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int hh = 0; hh < RMAX; ++hh) A[hh] = Bs[hh] = 0.f;
+  for (int hh = 0; hh < RMAX; ++hh)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) A[hh][e] = Bs[hh][e] = 0.f;
 
-  const int t0 = blk * kContribTB + wave * TW + slot * TS;
-  const int t1 = min(t0 + TS, n);
-  const T* kp = k + ((long)(p * Hkv + kvh) * N) * DH + r;
-  const T* qp = q + ((long)(p * Hq + kvh * R) * N) * DH + r;
+  const int per = TB / TPQ;  // tokens per slot (a contiguous run)
+  const int t0 = blk * TB + slot * per;
+  const int t1 = min(t0 + per, n);
+  const T* kp = k + ((long)(p * Hkv + kvh) * N) * DH + 4 * quad;
+  const T* qp = q + ((long)(p * Hq + kvh * R) * N) * DH + 4 * quad;
   for (int t = t0; t < t1; ++t) {
-    K += fabsf(to_f32(kp[(long)t * DH]));
+    abs_acc(K, load4(kp + (long)t * DH));
 #pragma unroll
     for (int hh = 0; hh < RMAX; ++hh) {
       if (hh < R) {
-        const float qa = fabsf(to_f32(qp[((long)hh * N + t) * DH]));
-        A[hh] += qa;
-        Bs[hh] += qa * K;
+        const float4 x = load4(qp + ((long)hh * N + t) * DH);
+        const float qa[4] = {fabsf(x.x), fabsf(x.y), fabsf(x.z), fabsf(x.w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          A[hh][e] += qa[e];
+          Bs[hh][e] += qa[e] * K[e];
+        }
       }
     }
   }
 
-  // ordered combine of the slots of this wave (slot s holds tokens after s-1)
+  // ordered combine of the slots of this wave: slot s absorbs slot s + 1,
+  // then the pair at s + 2, ... (the lane of slot s is always the left part)
 #pragma unroll
-  for (int off = DH; off < kWave; off <<= 1) {
-    const float Kr = __shfl_down(K, off);
+  for (int off = NQ4; off < kWave; off <<= 1) {
 #pragma unroll
-    for (int hh = 0; hh < RMAX; ++hh) {
-      const float Ar = __shfl_down(A[hh], off);
-      const float Br = __shfl_down(Bs[hh], off);
-      Bs[hh] += Br + K * Ar;
-      A[hh] += Ar;
-    }
-    K += Kr;
-  }
-  // lanes of slot 0 now hold the wave's triple for dimension r
-  if (slot == 0) {
-#pragma unroll
-    for (int hh = 0; hh < RMAX; ++hh) {
-      xs[wave][hh][r] = A[hh];
-      xs[wave][RMAX + hh][r] = Bs[hh];
-    }
-    xs[wave][2 * RMAX][r] = K;
-  }
-  __syncthreads();
-  if (threadIdx.x < DH) {
-    const int rr = threadIdx.x;
-    float cA[RMAX], cB[RMAX], cK = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < RMAX; ++hh) cA[hh] = cB[hh] = 0.f;
-    for (int w = 0; w < 4; ++w) {
+    for (int e = 0; e < 4; ++e) {
+      const float Kr = __shfl_down(K[e], off);
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
-        const float Ar = xs[w][hh][rr], Br = xs[w][RMAX + hh][rr];
-        cB[hh] += Br + cK * Ar;
-        cA[hh] += Ar;
+        if (hh < R) {
+          const float Ar = __shfl_down(A[hh][e], off);
+          const float Br = __shfl_down(Bs[hh][e], off);
+          Bs[hh][e] += Br + K[e] * Ar;
+          A[hh][e] += Ar;
+        }
       }
-      cK += xs[w][2 * RMAX][rr];
+      K[e] += Kr;
     }
-    float* out = part + (((long)p * Hkv + kvh) * nblk + blk) * (2 * R + 1) * DH;
-    for (int hh = 0; hh < R && hh < RMAX; ++hh) {
-      out[hh * DH + rr] = cA[hh];
-      out[(R + hh) * DH + rr] = cB[hh];
+  }
+  if (wslot == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * quad + e;
+#pragma unroll
+      for (int hh = 0; hh < RMAX; ++hh) {
+        if (hh < R) {
+          xs[wave][hh][r] = A[hh][e];
+          xs[wave][RMAX + hh][r] = Bs[hh][e];
+        }
+      }
+      xs[wave][2 * RMAX][r] = K[e];
     }
-    out[2 * R * DH + rr] = badlen ? __builtin_nanf("") : cK;
+  }
+  __syncthreads();
+  // ordered combine of the four waves: one thread per (head, dimension)
+  float* out = part + (((long)p * Hkv + kvh) * nblk + blk) * (2 * R + 1) * DH;
+  for (int idx = threadIdx.x; idx < R * DH; idx += blockDim.x) {
+    const int hh = idx / DH, r = idx % DH;
+    float cA = 0.f, cB = 0.f, cK = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float Ar = xs[w][hh][r];
+      cB += xs[w][RMAX + hh][r] + cK * Ar;
+      cA += Ar;
+      cK += xs[w][2 * RMAX][r];
+    }
+    out[hh * DH + r] = cA;
+    out[(R + hh) * DH + r] = cB;
+    if (hh == 0) out[2 * R * DH + r] = badlen ? __builtin_nanf("") : cK;
   }
 }
 
-// One CTA per query head; thread r combines the CTA triples of every prompt in
-// token order, then averages over prompts with equal weights.
+// One CTA per query head, 4 x DH threads: part w folds the w-th contiguous
+// quarter of a prompt's blocks in token order, then the four quarter triples
+// are combined in order.
 template <int DH>
-__global__ __launch_bounds__(64) void contrib_combine_kernel(const float* __restrict__ part,
-                                                             const int32_t* __restrict__ seq_lens,
-                                                             float* __restrict__ chi_per_prompt,
-                                                             float* __restrict__ chi_mean, int P,
-                                                             int Hq, int Hkv, int N, int nblk) {
-  const int h = blockIdx.x, r = threadIdx.x;
-  if (r >= DH) return;
+__global__ __launch_bounds__(4 * DH) void contrib_combine_kernel(const float* __restrict__ part,
+                                                                 const int32_t* __restrict__ seq_lens,
+                                                                 float* __restrict__ chi_per_prompt,
+                                                                 float* __restrict__ chi_mean, int P,
+                                                                 int Hq, int Hkv, int N, int nblk, int TB) {
+  __shared__ float red[4][DH];
+  const int h = blockIdx.x;
+  const int r = threadIdx.x % DH, w = threadIdx.x / DH;
   const int R = Hq / Hkv, kvh = h / R, hh = h % R;
   const float inv_sqrt_d = 1.f / sqrtf((float)DH);
   float mean = 0.f;
   for (int p = 0; p < P; ++p) {
     const int n = seq_lens ? seq_lens[p] : N;
-    const float* base = part + ((long)p * Hkv + kvh) * nblk * (2 * R + 1) * DH;
-    float tot = 0.f, kc = 0.f;
-    const int nb_used = n >= 1 && n <= N ? (n + kContribTB - 1) / kContribTB : nblk;
-    for (int blk = 0; blk < nb_used; ++blk) {
-      const float* x = base + (long)blk * (2 * R + 1) * DH;
-      tot += x[(R + hh) * DH + r] + kc * x[hh * DH + r];
-      kc += x[2 * R * DH + r];
-    }
-    const float pairs = 0.5f * (float)n * (float)(n + 1);
     const bool badlen = n < 1 || n > N;
-    const float chi = badlen ? __builtin_nanf("") : tot * inv_sqrt_d / pairs;
-    if (chi_per_prompt) chi_per_prompt[((long)p * Hq + h) * DH + r] = chi;
-    mean += chi;
+    const int nb_used = badlen ? nblk : (n + TB - 1) / TB;
+    const float* base = part + ((long)p * Hkv + kvh) * nblk * (2 * R + 1) * DH;
+    const long stride = (long)(2 * R + 1) * DH;
+    // contiguous quarter of the blocks for this part: [b0, b1)
+    const int b0 = (nb_used * w) / 4, b1 = (nb_used * (w + 1)) / 4;
+    float tA = 0.f, tB = 0.f, tK = 0.f;
+    for (int blk = b0; blk < b1; ++blk) {
+      const float* x = base + blk * stride;
+      const float Ab = x[hh * DH + r];
+      tB += x[(R + hh) * DH + r] + tK * Ab;
+      tA += Ab;
+      tK += x[2 * R * DH + r];
+    }
+    // ordered combine of the four quarters
+    __syncthreads();
+    red[w][r] = tA;
+    __syncthreads();
+    float qa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qa[i] = red[i][r];
+    __syncthreads();
+    red[w][r] = tB;
+    __syncthreads();
+    float qb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qb[i] = red[i][r];
+    __syncthreads();
+    red[w][r] = tK;
+    __syncthreads();
+    if (w == 0) {
+      float cB = 0.f, cK = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cB += qb[i] + cK * qa[i];
+        cK += red[i][r];
+      }
+      const float pairs = 0.5f * (float)n * (float)(n + 1);
+      const float chi = (badlen || cK != cK) ? __builtin_nanf("") : cB * inv_sqrt_d / pairs;
+      if (chi_per_prompt) chi_per_prompt[((long)p * Hq + h) * DH + r] = chi;
+      mean += chi;
+    }
   }
-  chi_mean[(long)h * DH + r] = mean / (float)P;
+  if (w == 0) chi_mean[(long)h * DH + r] = mean / (float)P;
 }
 
 size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h) {
-  const long nblk = (N + kContribTB - 1) / kContribTB;
+  const int TB = contrib_block_tokens(N);
+  const long nblk = (N + TB - 1) / TB;
   const int R = Hq / Hkv;
   return (size_t)P * Hkv * nblk * (2 * R + 1) * d_h * sizeof(float);
 }
 
 template <typename T, int DH, int RMAX>
 static hipError_t launch_contrib_r(const ContribLaunch& a, hipStream_t stream) {
-  const int nblk = (a.N + kContribTB - 1) / kContribTB;
+  const int TB = contrib_block_tokens(a.N);
+  const int nblk = (a.N + TB - 1) / TB;
   float* part = reinterpret_cast<float*>(a.workspace);
   hipLaunchKernelGGL((contrib_partial_kernel<T, DH, RMAX>), dim3(nblk, a.Hkv, a.P), dim3(256), 0, stream,
                      reinterpret_cast<const T*>(a.q), reinterpret_cast<const T*>(a.k), a.seq_lens, part,
-                     a.Hq, a.Hkv, a.N, nblk);
+                     a.Hq, a.Hkv, a.N, nblk, TB);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((contrib_combine_kernel<DH>), dim3(a.Hq), dim3(64), 0, stream, part, a.seq_lens,
-                     a.chi_per_prompt, a.chi_mean, a.P, a.Hq, a.Hkv, a.N, nblk);
+  hipLaunchKernelGGL((contrib_combine_kernel<DH>), dim3(a.Hq), dim3(4 * DH), 0, stream, part, a.seq_lens,
+                     a.chi_per_prompt, a.chi_mean, a.P, a.Hq, a.Hkv, a.N, nblk, TB);
   return hipGetLastError();
 }
 

@@ -7,9 +7,14 @@
 // and den_h += phi_q,h(q_h)_f z[f] (Eq. (6)); y_h = num_h / den_h.  The new
 // token therefore belongs to its own causal prefix.
 //
-// One 256-thread CTA per (sequence, KV head).  The feature values phi_k and
-// phi_q,h of all D rows are computed once into LDS; the streaming loop reads
-// 16 rows per pass as float4 (16 threads per 256-byte row), fully coalesced.
+// The D feature rows of a state are cut into `nslice` slices so that even a
+// handful of sequences fills the chip.  Kernel 1 runs one 256-thread CTA per
+// (slice, sequence x KV head): it computes the feature values phi_k and
+// phi_q,h of its rows into LDS, streams the rows with 16 threads per 256-byte
+// row (float4 loads and stores, fully coalesced, four rows in flight per
+// thread) and writes the partial (num_h, den_h) of the slice.  Kernel 2 adds
+// the slices in a fixed order and divides.  With a single slice kernel 1
+// divides and stores y itself.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -21,6 +26,7 @@ namespace oal {
 
 namespace {
 constexpr int DV = 64;
+constexpr int NC = DV + 1;
 
 template <int DH>
 __device__ __forceinline__ void premap_vec(float* x, const float* __restrict__ gamma,
@@ -37,20 +43,59 @@ __device__ __forceinline__ void premap_vec(float* x, const float* __restrict__ g
   const float inv = 1.f / sqrtf(var + eps);
   for (int c = 0; c < DH; ++c) x[c] = gamma[c] * (x[c] - mu) * inv + beta[c];
 }
+
+// Packed feature f -> (r, t) over the augmented key [k_0 .. k_{d-1}, 1]:
+// f = 0 is (d, d), f = 1 + r is (r, d), and the pairs r <= t follow in
+// row-major upper-triangle order.
+template <int DH>
+__device__ __forceinline__ void feature_pair(int f, int& r, int& t) {
+  if (f == 0) {
+    r = DH;
+    t = DH;
+    return;
+  }
+  if (f <= DH) {
+    r = f - 1;
+    t = DH;
+    return;
+  }
+  const int p = f - 1 - DH;
+  // first pair of row r sits at r*DH - r(r-1)/2; solve for r, then fix up
+  const float b = 2.f * DH + 1.f;
+  int rr = (int)((b - sqrtf(b * b - 8.f * (float)p)) * 0.5f);
+  rr = max(0, min(rr, DH - 1));
+  while (rr > 0 && rr * DH - rr * (rr - 1) / 2 > p) --rr;
+  while (rr + 1 < DH && (rr + 1) * DH - (rr + 1) * rr / 2 <= p) ++rr;
+  r = rr;
+  t = rr + (p - (rr * DH - rr * (rr - 1) / 2));
+}
 }  // namespace
 
+// Rows per slice (a multiple of 16) and slice count for `states` states.
+void decode_slicing(int d_h, long states, int& rows, int& nslice) {
+  const int D = (int)packed_features(d_h);
+  long want = (2048 + states - 1) / states;           // aim for >= 2048 CTAs
+  want = want < 1 ? 1 : want;
+  const long min_slices = (D + 1023) / 1024;           // at most 1024 rows per CTA
+  if (want < min_slices) want = min_slices;
+  const long max_slices = (D + 63) / 64;               // at least 64 rows per CTA
+  if (want > max_slices) want = max_slices;
+  rows = (int)(((D + want - 1) / want + 15) / 16 * 16);
+  nslice = (D + rows - 1) / rows;
+}
+
 template <typename T, int DH, int RMAX, bool PREMAP>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__(256) void decode_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ group_of_dim, const float* __restrict__ ca,
     const float* __restrict__ cb, const float* __restrict__ cc, int G,
     const float* __restrict__ gamma_q, const float* __restrict__ beta_q,
     const float* __restrict__ gamma_k, const float* __restrict__ beta_k, float ln_eps,
-    float* __restrict__ state, T* __restrict__ y, int Hq, int Hkv) {
+    float* __restrict__ state, float* __restrict__ part, T* __restrict__ y, int Hq, int Hkv, int rows) {
   constexpr int D = (int)packed_features(DH);
   extern __shared__ float smem[];
-  float* phik = smem;                 // [D]
-  float* phiq = smem + D;             // [RMAX][D]
+  float* phik = smem;                 // [rows]
+  float* phiq = smem + rows;          // [RMAX][rows]
   __shared__ float khat[DH + 1];
   __shared__ float qhat[RMAX][DH + 1];
   __shared__ float vv[DV];
@@ -58,10 +103,12 @@ __global__ __launch_bounds__(256) void decode_kernel(
   __shared__ float dred[RMAX][256 / kWave];
   __shared__ int bad;
 
-  const int bh = blockIdx.x;
+  const int slice = blockIdx.x, nslice = gridDim.x;
+  const int bh = blockIdx.y;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int R = Hq / Hkv;
   const int tid = threadIdx.x;
+  const int f0 = slice * rows, f1 = min(f0 + rows, D);
 
   if (tid == 0) bad = 0;
   if (tid < DH) khat[tid] = to_f32(k[(long)bh * DH + tid]);
@@ -78,28 +125,19 @@ __global__ __launch_bounds__(256) void decode_kernel(
       const int hh = tid - 64, h = kvh * R + hh;
       premap_vec<DH>(qhat[hh], gamma_q + h * DH, beta_q + h * DH, ln_eps);
     }
-    __syncthreads();
   }
   for (int idx = tid; idx < R * DH; idx += blockDim.x) {
     const int g = group_of_dim[(kvh * R + idx / DH) * DH + idx % DH];
     if (g < 0 || g >= G) atomicOr(&bad, 1);
   }
+  __syncthreads();
 
-  // feature values of every packed row: const, linear r, pairs r <= t
+  // feature values of the slice rows: const, linear r, pairs r <= t
   const float inv_sqrt_d = 1.f / sqrtf((float)DH);
-  for (int f = tid; f < D; f += blockDim.x) {
+  for (int f = f0 + tid; f < f1; f += blockDim.x) {
     int r, t;
-    if (f == 0) {
-      r = DH; t = DH;
-    } else if (f <= DH) {
-      r = f - 1; t = DH;
-    } else {
-      int p = f - 1 - DH;
-      r = 0;
-      while (p >= DH - r) { p -= DH - r; ++r; }
-      t = r + p;
-    }
-    phik[f] = khat[r] * khat[t];
+    feature_pair<DH>(f, r, t);
+    phik[f - f0] = khat[r] * khat[t];
     for (int hh = 0; hh < RMAX; ++hh) {
       if (hh >= R) break;
       const int h = kvh * R + hh;
@@ -115,13 +153,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
         const float m = r == t ? 1.f : 2.f;
         cf = m * 0.5f * (cc[(h * G + g1) * G + g2] + cc[(h * G + g2) * G + g1]) / DH;
       }
-      phiq[hh * D + f] = cf * qhat[hh][r] * qhat[hh][t];
+      phiq[hh * rows + (f - f0)] = cf * qhat[hh][r] * qhat[hh][t];
     }
   }
   __syncthreads();
 
-  // ---- stream H rows: 16 threads per row, float4 each ----
-  float* sp = state + (long)bh * D * (DV + 1);
+  // ---- stream the slice's H rows: 16 threads per row, float4 each ----
+  float* sp = state + (long)bh * D * NC;
   const int c4 = tid % 16, rg = tid / 16;
   const float4 v4 = make_float4(vv[4 * c4], vv[4 * c4 + 1], vv[4 * c4 + 2], vv[4 * c4 + 3]);
   float acc[RMAX][4];
@@ -129,45 +167,50 @@ __global__ __launch_bounds__(256) void decode_kernel(
   for (int hh = 0; hh < RMAX; ++hh) acc[hh][0] = acc[hh][1] = acc[hh][2] = acc[hh][3] = 0.f;
 
   constexpr int U = 4;
-  for (int f0 = rg; f0 < D; f0 += 16 * U) {
+  for (int fb = f0 + rg; fb < f1; fb += 16 * U) {
     float4 hv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int f = f0 + 16 * u;
-      if (f < D) hv[u] = *reinterpret_cast<const float4*>(&sp[(long)f * DV + 4 * c4]);
+      const int f = fb + 16 * u;
+      if (f < f1) hv[u] = *reinterpret_cast<const float4*>(&sp[(long)f * DV + 4 * c4]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int f = f0 + 16 * u;
-      if (f >= D) continue;
-      const float pk = phik[f];
+      const int f = fb + 16 * u;
+      if (f >= f1) continue;
+      const float pk = phik[f - f0];
       float4 x = hv[u];
-      x.x += pk * v4.x; x.y += pk * v4.y; x.z += pk * v4.z; x.w += pk * v4.w;
+      x.x += pk * v4.x;
+      x.y += pk * v4.y;
+      x.z += pk * v4.z;
+      x.w += pk * v4.w;
       *reinterpret_cast<float4*>(&sp[(long)f * DV + 4 * c4]) = x;
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
         if (hh < R) {
-          const float pq = phiq[hh * D + f];
-          acc[hh][0] += pq * x.x; acc[hh][1] += pq * x.y;
-          acc[hh][2] += pq * x.z; acc[hh][3] += pq * x.w;
+          const float pq = phiq[hh * rows + (f - f0)];
+          acc[hh][0] += pq * x.x;
+          acc[hh][1] += pq * x.y;
+          acc[hh][2] += pq * x.z;
+          acc[hh][3] += pq * x.w;
         }
       }
     }
   }
-  // ---- z column ----
+  // ---- the slice's z entries ----
   float dacc[RMAX];
 #pragma unroll
   for (int hh = 0; hh < RMAX; ++hh) dacc[hh] = 0.f;
   float* zp = sp + (long)D * DV;
-  for (int f = tid; f < D; f += blockDim.x) {
-    const float zn = zp[f] + phik[f];
+  for (int f = f0 + tid; f < f1; f += blockDim.x) {
+    const float zn = zp[f] + phik[f - f0];
     zp[f] = zn;
 #pragma unroll
     for (int hh = 0; hh < RMAX; ++hh)
-      if (hh < R) dacc[hh] += phiq[hh * D + f] * zn;
+      if (hh < R) dacc[hh] += phiq[hh * rows + (f - f0)] * zn;
   }
 
-  // ---- reductions ----
+  // ---- reductions (fixed order) ----
 #pragma unroll
   for (int hh = 0; hh < RMAX; ++hh) {
     if (hh >= R) break;
@@ -179,38 +222,79 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
   __syncthreads();
   const float nanv = __builtin_nanf("");
-  for (int idx = tid; idx < R * DV; idx += blockDim.x) {
-    const int hh = idx / DV, n = idx % DV;
-    float num = 0.f;
-    for (int g = 0; g < 16; ++g) num += red[g][hh][n];
-    const float den = dred[hh][0] + dred[hh][1] + dred[hh][2] + dred[hh][3];
-    store_elem(&y[((long)b * Hq + kvh * R + hh) * DV + n], bad ? nanv : num / den);
+  for (int idx = tid; idx < R * NC; idx += blockDim.x) {
+    const int hh = idx / NC, n = idx % NC;
+    float val;
+    if (n < DV) {
+      val = 0.f;
+      for (int g = 0; g < 16; ++g) val += red[g][hh][n];
+    } else {
+      val = dred[hh][0] + dred[hh][1] + dred[hh][2] + dred[hh][3];
+    }
+    if (nslice == 1) {
+      if (n < DV) {
+        const float den = dred[hh][0] + dred[hh][1] + dred[hh][2] + dred[hh][3];
+        store_elem(&y[((long)b * Hq + kvh * R + hh) * DV + n], bad ? nanv : val / den);
+      }
+    } else {
+      part[(((long)bh * nslice + slice) * R + hh) * NC + n] = (bad && n == DV) ? nanv : val;
+    }
   }
+}
+
+// y[b, h, :] = sum over slices of num / sum over slices of den, slices added
+// in index order.  One thread per output element.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_finish_kernel(const float* __restrict__ part, T* __restrict__ y,
+                                                            int B, int Hq, int Hkv, int nslice) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)B * Hq * DV;
+  if (idx >= total) return;
+  const int n = (int)(idx % DV);
+  const long bhq = idx / DV;
+  const int h = (int)(bhq % Hq), b = (int)(bhq / Hq);
+  const int R = Hq / Hkv, kvh = h / R, hh = h % R;
+  const long bh = (long)b * Hkv + kvh;
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < nslice; ++s) {
+    const float* x = part + ((bh * nslice + s) * R + hh) * NC;
+    num += x[n];
+    den += x[DV];
+  }
+  store_elem(&y[idx], num / den);
+}
+
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h) {
+  int rows, nslice;
+  decode_slicing(d_h, (long)B * Hkv, rows, nslice);
+  if (nslice == 1) return 0;
+  return (size_t)B * Hkv * nslice * (Hq / Hkv) * NC * sizeof(float);
 }
 
 template <typename T, int DH, int RMAX>
 static hipError_t launch_decode_r(const DecodeLaunch& a, hipStream_t stream) {
-  constexpr int D = (int)packed_features(DH);
-  const size_t shm = (size_t)(1 + RMAX) * D * sizeof(float);
-  dim3 grid(a.B * a.Hkv);
+  int rows, nslice;
+  decode_slicing(DH, (long)a.B * a.Hkv, rows, nslice);
+  const size_t shm = (size_t)(1 + RMAX) * rows * sizeof(float);
+  dim3 grid(nslice, a.B * a.Hkv);
   const T* qq = reinterpret_cast<const T*>(a.q);
   const T* kk = reinterpret_cast<const T*>(a.k);
   const T* vv = reinterpret_cast<const T*>(a.v);
   T* yy = reinterpret_cast<T*>(a.y);
-  hipError_t err = a.premap
-      ? hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, DH, RMAX, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm)
-      : hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<T, DH, RMAX, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (err != hipSuccess) return err;
+  float* part = reinterpret_cast<float*>(a.workspace);
   if (a.premap)
-    hipLaunchKernelGGL((decode_kernel<T, DH, RMAX, true>), grid, dim3(256), shm, stream, qq, kk, vv,
+    hipLaunchKernelGGL((decode_partial_kernel<T, DH, RMAX, true>), grid, dim3(256), shm, stream, qq, kk, vv,
                        a.group_of_dim, a.ca, a.cb, a.cc, a.G, a.gamma_q, a.beta_q, a.gamma_k, a.beta_k,
-                       a.ln_eps, a.state, yy, a.Hq, a.Hkv);
+                       a.ln_eps, a.state, part, yy, a.Hq, a.Hkv, rows);
   else
-    hipLaunchKernelGGL((decode_kernel<T, DH, RMAX, false>), grid, dim3(256), shm, stream, qq, kk, vv,
+    hipLaunchKernelGGL((decode_partial_kernel<T, DH, RMAX, false>), grid, dim3(256), shm, stream, qq, kk, vv,
                        a.group_of_dim, a.ca, a.cb, a.cc, a.G, nullptr, nullptr, nullptr, nullptr, 0.f,
-                       a.state, yy, a.Hq, a.Hkv);
+                       a.state, part, yy, a.Hq, a.Hkv, rows);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nslice == 1) return err;
+  const long total = (long)a.B * a.Hq * DV;
+  hipLaunchKernelGGL((decode_finish_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     part, yy, a.B, a.Hq, a.Hkv, nslice);
   return hipGetLastError();
 }
 

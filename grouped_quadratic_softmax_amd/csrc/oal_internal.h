@@ -34,6 +34,7 @@ struct DecodeLaunch {
   float ln_eps;
   float* state;
   void* y;
+  void* workspace;
 };
 
 struct ContribLaunch {
@@ -49,6 +50,8 @@ size_t fwd_workspace_bytes(int B, int Hkv, int N, int d_h, int dtype);
 // stages: bit 0 = chunk states (scan), bit 1 = outputs (readout)
 hipError_t launch_fwd(const FwdLaunch& a, int stages, hipStream_t stream);
 hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStream_t stream);
+void decode_slicing(int d_h, long states, int& rows, int& nslice);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h);
 hipError_t launch_contrib(const ContribLaunch& a, hipStream_t stream);

@@ -154,7 +154,12 @@ def fwd(q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None, ret
     return (y, state_out) if return_state else y
 
 
-def decode_step(q, k, v, coeffs: Coeffs, state, prep: Optional[Prep] = None, y=None):
+def decode_workspace_bytes(B, Hq, Hkv, d_h, d_v, G, dtype) -> int:
+    dims = _dims(B, Hq, Hkv, 0, d_h, d_v, G, dtype)
+    return int(L.lib().oal_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+def decode_step(q, k, v, coeffs: Coeffs, state, prep: Optional[Prep] = None, y=None, workspace=None):
     """One decode step.  q [B, Hq, d], k [B, Hkv, d], v [B, Hkv, 64];
     state [B, Hkv, state_floats] float32 updated in place.  Returns y [B, Hq, 64]."""
     _dev(q, "q", ndim=3)
@@ -168,10 +173,15 @@ def decode_step(q, k, v, coeffs: Coeffs, state, prep: Optional[Prep] = None, y=N
     dims = _dims(B, Hq, Hkv, 0, d, dv, coeffs.n_groups, q.dtype)
     if y is None:
         y = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+    nbytes = int(L.lib().oal_decode_workspace_bytes(ctypes.byref(dims)))
+    if nbytes > 0 and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     cs = coeffs.struct()
     ps = prep.struct() if prep is not None else None
     st = L.lib().oal_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
-                                 ctypes.byref(ps) if ps is not None else None, _ptr(state), _ptr(y), _stream())
+                                 ctypes.byref(ps) if ps is not None else None, _ptr(state), _ptr(y),
+                                 _ptr(workspace), ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                                 _stream())
     L.check(st, "oal_decode_step")
     return y
 
@@ -251,12 +261,14 @@ class DecodePlan:
         Hkv, dv = k.shape[1], v.shape[2]
         self.y = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
         self.dims = _dims(B, Hq, Hkv, 0, d, dv, coeffs.n_groups, q.dtype)
+        nbytes = int(L.lib().oal_decode_workspace_bytes(ctypes.byref(self.dims)))
+        self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
         self._keep = (q, k, v, coeffs, state, prep)
         self._cs = coeffs.struct()
         self._ps = prep.struct() if prep is not None else None
         pp = ctypes.byref(self._ps) if self._ps is not None else None
         self._args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(self._cs), pp, _ptr(state),
-                      _ptr(self.y), _stream())
+                      _ptr(self.y), _ptr(self.workspace), ctypes.c_size_t(self.workspace.numel()), _stream())
         self._lib = L.lib()
 
     def run(self):

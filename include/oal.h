@@ -164,15 +164,23 @@ int oal_fwd_outputs(const oal_dims* dims, const void* q, const void* k, const vo
                     const oal_coeffs* coeffs, const oal_prep* prep, void* y, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace oal_decode_step needs for `dims` (0 when none
+ * is needed or `dims` is invalid). */
+size_t oal_decode_workspace_bytes(const oal_dims* dims);
+
 /* One recurrent decode step for `dims->batch` independent sequences (paper,
  * Eqs. (5)-(6) for a single token): state <- state + phi(k) [v, 1]^T, then
  * y = (phi_q(q)^T state)[:d_v] / (phi_q(q)^T state)[d_v].  The new token is
  * part of its own causal prefix.
  *   q [B, Hq, d_h], k [B, Hkv, d_h], v [B, Hkv, d_v], y [B, Hq, d_v];
- *   state [B, Hkv, oal_state_floats], updated in place. */
+ *   state [B, Hkv, oal_state_floats], updated in place;
+ *   workspace: device scratch of at least oal_decode_workspace_bytes(dims)
+ *              (may be NULL when that is 0); contents undefined afterwards.
+ * Supports Hq / Hkv <= 8.  Calls that share a workspace or a state must be
+ * ordered on one stream. */
 int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const void* v,
                     const oal_coeffs* coeffs, const oal_prep* prep, float* state, void* y,
-                    void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace oal_contrib needs for `dims` (0 if invalid). */
 size_t oal_contrib_workspace_bytes(const oal_dims* dims);

@@ -138,14 +138,21 @@ def test_decode_and_contrib_validation(L):
     lib = L.lib()
     cs = L.OalCoeffs(0x1000, 0x1000, 0x1000, 0x1000)
     d = _dims(L, B=2)
-    assert lib.oal_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == \
+    z = ctypes.c_size_t(0)
+    assert lib.oal_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, z, None) == \
         L.OAL_ERR_INVALID_ARG
-    assert lib.oal_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(cs), None, None, FAKE, None) == \
-        L.OAL_ERR_INVALID_ARG
+    assert lib.oal_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(cs), None, None, FAKE, None, z,
+                               None) == L.OAL_ERR_INVALID_ARG
     assert lib.oal_decode_step(ctypes.byref(_dims(L, Hq=18, Hkv=2)), FAKE, FAKE, FAKE, ctypes.byref(cs), None,
-                               FAKE, FAKE, None) == L.OAL_ERR_UNSUPPORTED
+                               FAKE, FAKE, None, z, None) == L.OAL_ERR_UNSUPPORTED
     assert lib.oal_decode_step(ctypes.byref(_dims(L, B=0)), FAKE, FAKE, FAKE, ctypes.byref(cs), None, FAKE, FAKE,
-                               None) == L.OAL_OK
+                               None, z, None) == L.OAL_OK
+    # a few sequences: the state rows are split into slices whose partial
+    # readouts need a workspace
+    need = lib.oal_decode_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert lib.oal_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(cs), None, FAKE, FAKE, FAKE,
+                               ctypes.c_size_t(need - 1), None) == L.OAL_ERR_WORKSPACE
     ws = ctypes.c_size_t(1 << 30)
     assert lib.oal_contrib(ctypes.byref(_dims(L, B=0)), FAKE, FAKE, None, None, FAKE, FAKE, ws, None) == \
         L.OAL_ERR_INVALID_ARG
