@@ -111,7 +111,8 @@ int oal_check_coeffs(const oal_dims* dims, const int32_t* group_of_dim_host, con
 
 size_t oal_fwd_workspace_bytes(const oal_dims* dims) {
   if (check_dims(dims, true) != OAL_OK) return 0;
-  return oal::fwd_workspace_bytes(dims->batch, dims->n_kv_heads, dims->seq_len, dims->d_h, dims->dtype);
+  return oal::fwd_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->seq_len, dims->d_h,
+                                 dims->dtype);
 }
 
 namespace {

@@ -46,7 +46,7 @@ struct ContribLaunch {
   void* workspace;
 };
 
-size_t fwd_workspace_bytes(int B, int Hkv, int N, int d_h, int dtype);
+size_t fwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d_h, int dtype);
 // stages: bit 0 = chunk states (scan), bit 1 = outputs (readout)
 hipError_t launch_fwd(const FwdLaunch& a, int stages, hipStream_t stream);
 hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStream_t stream);

@@ -53,6 +53,12 @@ constexpr int DV = 64;        // value head dimension handled by these kernels
 constexpr int NCOL = DV + 1;  // value columns + normaliser column
 constexpr int C = kChunk;     // tokens per chunk
 constexpr int KG = 2;         // snapshot K-blocks staged per pipeline step
+// LDS column pitch (elements) of a staged snapshot K-block: 80 bytes (fp16)
+// or 144 bytes (fp32), so that 16 lanes reading 16 bytes each hit distinct banks
+template <typename E>
+__host__ __device__ constexpr int stage_pitch() {
+  return sizeof(E) == 2 ? 40 : 36;
+}
 constexpr int kNegExp = -200; // exponent of an all-zero block
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -198,8 +204,63 @@ __device__ __forceinline__ void premap4(float* x, int d0, const float* __restric
 // kernel 1: chunk scan (state update + snapshots)
 // --------------------------------------------------------------------------
 
+constexpr int kScanWaves = 8;  // waves per scan CTA, one K-block each
+
+// Raw activation vector of four elements.
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<uint16_t> {
+  typedef uint2 type;
+};
+template <>
+struct Raw4<float> {
+  typedef float4 type;
+};
+__device__ __forceinline__ void unpack4(const uint2& w, float* out) {
+  out[0] = __uint_as_float(w.x << 16);
+  out[1] = __uint_as_float(w.x & 0xffff0000u);
+  out[2] = __uint_as_float(w.y << 16);
+  out[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack4(const float4& w, float* out) {
+  out[0] = w.x;
+  out[1] = w.y;
+  out[2] = w.z;
+  out[3] = w.w;
+}
+template <typename T>
+__device__ __forceinline__ typename Raw4<T>::type zero_raw4();
+template <>
+__device__ __forceinline__ uint2 zero_raw4<uint16_t>() {
+  return make_uint2(0u, 0u);
+}
+template <>
+__device__ __forceinline__ float4 zero_raw4<float>() {
+  return make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// LayerNorm + affine of a row whose 4-element parts sit in `nl` consecutive
+// lanes (ReBased pre-map, biased variance).
+template <int DH, int nl>
+__device__ __forceinline__ void premap_lanes(float (&x)[4], int d0, const float* __restrict__ gamma,
+                                             const float* __restrict__ beta, float eps) {
+  float s = x[0] + x[1] + x[2] + x[3];
+#pragma unroll
+  for (int o = 1; o < nl; o <<= 1) s += __shfl_xor(s, o);
+  const float mu = s * (1.f / DH);
+  float v2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v2 += (x[i] - mu) * (x[i] - mu);
+#pragma unroll
+  for (int o = 1; o < nl; o <<= 1) v2 += __shfl_xor(v2, o);
+  const float inv = 1.f / sqrtf(v2 * (1.f / DH) + eps);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = gamma[d0 + i] * (x[i] - mu) * inv + beta[d0 + i];
+}
+
 template <typename T, int DH, bool PREMAP>
-__global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, const T* __restrict__ v,
+__global__ __launch_bounds__(512) void scan_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                    const float* __restrict__ gamma_k,
                                                    const float* __restrict__ beta_k, float ln_eps,
                                                    const float* __restrict__ state_in,
@@ -208,22 +269,26 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
                                                    float* __restrict__ sconst, int Hkv, int N, int nchunks) {
   typedef typename Cx<T>::E E;
   typedef typename Cx<T>::Frag F;
+  typedef typename Raw4<T>::type RV;
   constexpr int KB = n_kblocks(DH);
   constexpr int NQ = nq_kblocks(DH);
   constexpr long D = packed_features(DH);
   constexpr long SF = D * NCOL;
-  constexpr int KP = C + 8;    // row pitch of kT / vT (elements)
-  constexpr int QD = DH / 4;   // key dims per staging thread
+  constexpr int KP = C + 8;                 // row pitch of kT / vT (elements)
   constexpr int ONE = DH, ZERO = DH + 1;
+  constexpr int NT = 64 * kScanWaves;       // threads
+  constexpr int RQ = DH / 4;                // 4-element parts per key row
+  constexpr int KT = (C * RQ + NT - 1) / NT;  // key parts per thread
+  constexpr int VT = C * 16 / NT;           // value parts per thread
   __shared__ __align__(16) E kT[(DH + 2) * KP];  // scaled keys, transposed; row DH = ones, DH+1 = zeros
   __shared__ __align__(16) E vT[DV * KP];        // scaled values, transposed
-  __shared__ float wmx[2][4];
+  __shared__ float wmx[3][kScanWaves];
 
   const int bh = blockIdx.y, BH = gridDim.y;
   const int kvh = bh % Hkv;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int lg = lane / 16, l16 = lane % 16;
-  const int kb = blockIdx.x * 4 + wave;
+  const int kb = blockIdx.x * kScanWaves + wave;
   const bool active = kb < KB;
   const int nu = kb < NQ ? 2 : 1;  // key-exponent multiplicity of this K-block's features
   const bool lead = blockIdx.x == 0;
@@ -241,22 +306,6 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
       at[m] = ZERO;
     }
   }
-  // ABI indices of the accumulator rows (4 lg + e of M-tile m); -1 padding
-  long fidx[2][4];
-  bool fcanon[2][4];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      int r, t, mu;
-      if (active && kfeature(DH, kb, acc_position(m, 4 * lg + e), r, t, mu)) {
-        fidx[m][e] = abi_index(DH, r, t);
-        fcanon[m][e] = t == DH || r <= t;
-      } else {
-        fidx[m][e] = -1;
-        fcanon[m][e] = false;
-      }
-    }
 
   f32x4 acc[2][5];
 #pragma unroll
@@ -264,41 +313,57 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
 #pragma unroll
     for (int n = 0; n < 5; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const long sbase = (long)bh * SF;
   // constant-feature row [sum v, n] (raw units), kept by the lead CTA
   float csum = 0.f;
-  const long sbase = (long)bh * SF;
   if (lead && tid < NCOL && state_in != nullptr) csum = tid < DV ? state_in[sbase + tid] : state_in[sbase + D * DV];
 
-  int Ek = 0, Ev = 0;
   const T* kp = k + (long)bh * N * DH;
   const T* vp = v + (long)bh * N * DV;
-  const int srow = tid / 4, sq = tid % 4;  // staging: row, quarter
+  RV kr[KT], vr[VT];
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const int j0 = c * C, nval = min(C, N - j0);
+#pragma unroll
+    for (int i = 0; i < KT; ++i) {
+      const int id = tid + NT * i, row = id / RQ, part = id % RQ;
+      kr[i] = (id < C * RQ && row < nval) ? *reinterpret_cast<const RV*>(kp + (long)(j0 + row) * DH + 4 * part)
+                                          : zero_raw4<T>();
+    }
+#pragma unroll
+    for (int i = 0; i < VT; ++i) {
+      const int id = tid + NT * i, row = id / 16, part = id % 16;
+      vr[i] = row < nval ? *reinterpret_cast<const RV*>(vp + (long)(j0 + row) * DV + 4 * part) : zero_raw4<T>();
+    }
+  };
+  fetch(0);
 
+  int Ek = 0, Ev = 0, beta = 0;
   for (int c = 0; c < nchunks; ++c) {
     const int j0 = c * C;
     const int nvalid = min(C, N - j0);
-    // ---- load the chunk (raw), pre-map, chunk maxima ----
-    float kx[QD], vx[16];
-    if (srow < nvalid) {
-      load_vals<QD>(kp + (long)(j0 + srow) * DH + sq * QD, kx);
-      load_vals<16>(vp + (long)(j0 + srow) * DV + sq * 16, vx);
-    } else {
+    float kx[KT][4], vx[VT][4];
 #pragma unroll
-      for (int i = 0; i < QD; ++i) kx[i] = 0.f;
+    for (int i = 0; i < KT; ++i) unpack4(kr[i], kx[i]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vx[i] = 0.f;
-    }
+    for (int i = 0; i < VT; ++i) unpack4(vr[i], vx[i]);
+    if (c + 1 < nchunks) fetch(c + 1);  // in flight during this chunk
     if (PREMAP) {
-      premap4<DH, QD>(kx, sq * QD, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
-      if (srow >= nvalid)
 #pragma unroll
-        for (int i = 0; i < QD; ++i) kx[i] = 0.f;
+      for (int i = 0; i < KT; ++i) {
+        const int id = tid + NT * i, row = id / RQ, part = id % RQ;
+        premap_lanes<DH, RQ>(kx[i], 4 * part, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
+        if (row >= nvalid || id >= C * RQ) kx[i][0] = kx[i][1] = kx[i][2] = kx[i][3] = 0.f;
+      }
     }
     float mk = 0.f, mv = 0.f;
 #pragma unroll
-    for (int i = 0; i < QD; ++i) mk = fmaxf(mk, fabsf(kx[i]));
+    for (int i = 0; i < KT; ++i)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mv = fmaxf(mv, fabsf(vx[i]));
+      for (int e = 0; e < 4; ++e) mk = fmaxf(mk, fabsf(kx[i][e]));
+#pragma unroll
+    for (int i = 0; i < VT; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mv = fmaxf(mv, fabsf(vx[i][e]));
     mk = wave_max(mk);
     mv = wave_max(mv);
     if (lane == 0) {
@@ -306,53 +371,66 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
       wmx[1][wave] = mv;
     }
     __syncthreads();  // (A): also ends every read of kT / vT of the previous chunk
-    const int ek = exp_above(fmaxf(fmaxf(wmx[0][0], wmx[0][1]), fmaxf(wmx[0][2], wmx[0][3])));
-    const int ev = exp_above(fmaxf(fmaxf(wmx[1][0], wmx[1][1]), fmaxf(wmx[1][2], wmx[1][3])));
+    float mk_all = 0.f, mv_all = 0.f;
+#pragma unroll
+    for (int w = 0; w < kScanWaves; ++w) {
+      mk_all = fmaxf(mk_all, wmx[0][w]);
+      mv_all = fmaxf(mv_all, wmx[1][w]);
+    }
+    const int ek = exp_above(mk_all), ev = exp_above(mv_all);
     if (c == 0) {
       Ek = ek == kNegExp ? 0 : ek;
       Ev = ev == kNegExp ? 0 : ev;
+      // initial state in units 2^(nu Ek + Ev) (2^(nu Ek) for z); the fixed
+      // snapshot exponent beta bounds every later entry: |acc| <= N + M_in
+      float m_in = 0.f;
       if (active && state_in != nullptr) {
         const float sh = pow2(-(nu * Ek + Ev)), sz = pow2(-nu * Ek);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const long f = fidx[m][e];
-            if (f < 0) continue;
+            int r, t, mu;
+            if (!kfeature(DH, kb, acc_position(m, 4 * lg + e), r, t, mu)) continue;
+            const long f = abi_index(DH, r, t);
 #pragma unroll
             for (int n = 0; n < 4; ++n) acc[m][n][e] = state_in[sbase + f * DV + 16 * n + l16] * sh;
             if (l16 == 0) acc[m][4][e] = state_in[sbase + D * DV + f] * sz;
           }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 5; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m_in = fmaxf(m_in, fabsf(acc[m][n][e]));
       }
+      m_in = wave_max(m_in);
+      if (lane == 0) wmx[2][wave] = m_in;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < kScanWaves; ++w) m_in = fmaxf(m_in, wmx[2][w]);
+      beta = exp_above((float)N + m_in) - 15;
+      const float sb = pow2(-beta);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 5; ++n) acc[m][n] *= sb;
     } else if (ek > Ek || ev > Ev) {
       const int dk = max(ek - Ek, 0), dv = max(ev - Ev, 0);
       Ek += dk;
       Ev += dv;
-      if (active) {
-        const float sh = pow2(-(nu * dk + dv)), sz = pow2(-nu * dk);
+      const float sh = pow2(-(nu * dk + dv)), sz = pow2(-nu * dk);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < 2; ++m) {
 #pragma unroll
-          for (int n = 0; n < 4; ++n) acc[m][n] *= sh;
-          acc[m][4] *= sz;
-        }
+        for (int n = 0; n < 4; ++n) acc[m][n] *= sh;
+        acc[m][4] *= sz;
       }
     }
 
-    // ---- snapshot S_c (units 2^(nu Ek + Ev) / 2^(nu Ek) times 2^beta) ----
+    // ---- snapshot S_c: raw = stored * 2^(beta + nu Ek) (* 2^Ev for H) ----
     const long sidx = (long)c * BH + bh;
     if (active) {
-      float mx = 0.f;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int n = 0; n < 5; ++n)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(acc[m][n][e]));
-      mx = wave_max(mx);
-      const int ex = exp_above(mx);
-      const int beta = ex == kNegExp ? kNegExp : ex - 15;
-      const float s = beta == kNegExp ? 0.f : pow2(-beta);
       E* sp = snap + (sidx * KB + kb) * NCOL * 32 + 8 * lg;
 #pragma unroll
       for (int n = 0; n < 5; ++n) {
@@ -360,8 +438,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
         float x[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[e] = acc[0][n][e] * s;
-          x[4 + e] = acc[1][n][e] * s;
+          x[e] = acc[0][n][e];
+          x[4 + e] = acc[1][n][e];
         }
         frag_st(sp + (16 * n + l16) * 32, x);
       }
@@ -373,13 +451,22 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
     }
     if (lead && tid < NCOL) sconst[sidx * NCOL + tid] = csum;
 
-    // ---- scaled chunk -> LDS (transposed) ----
+    // ---- scaled chunk -> LDS (transposed): k / 2^Ek, v / 2^(Ev + beta) ----
     {
-      const float sk = pow2(-Ek), sv = pow2(-Ev);
+      const float sk = pow2(-Ek), sv = pow2(-(Ev + beta));
 #pragma unroll
-      for (int i = 0; i < QD; ++i) kT[(sq * QD + i) * KP + srow] = (E)(kx[i] * sk);
+      for (int i = 0; i < KT; ++i) {
+        const int id = tid + NT * i, row = id / RQ, part = id % RQ;
+        if (id < C * RQ)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vT[(sq * 16 + i) * KP + srow] = (E)(vx[i] * sv);
+          for (int e = 0; e < 4; ++e) kT[(4 * part + e) * KP + row] = (E)(kx[i][e] * sk);
+      }
+#pragma unroll
+      for (int i = 0; i < VT; ++i) {
+        const int id = tid + NT * i, row = id / 16, part = id % 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vT[(4 * part + e) * KP + row] = (E)(vx[i][e] * sv);
+      }
       if (tid < C) {
         kT[ONE * KP + tid] = tid < nvalid ? (E)1.f : (E)0.f;
         kT[ZERO * KP + tid] = (E)0.f;
@@ -390,13 +477,22 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
       // running sum of the values (exact: the fp16 copies hold the bf16 inputs)
       float s = 0.f;
       for (int j = 0; j < nvalid; ++j) s += (float)vT[tid * KP + j];
-      csum += s * pow2(Ev);
+      csum += s * pow2(Ev + beta);
     } else if (lead && tid == DV) {
       csum += (float)nvalid;
     }
 
     // ---- S += phi_k(K_c)^T [V_c | 1] ----
     if (active) {
+      F ones;
+      if constexpr (IsBf16<T>::value) {
+        const _Float16 o = l16 == 0 ? (_Float16)pow2(-beta) : (_Float16)0.f;
+        ones.v = h8{o, o, o, o, o, o, o, o};
+      } else {
+        const float o = l16 == 0 ? pow2(-beta) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones.v[e] = o;
+      }
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks) {
         const int jb = 32 * ks + 8 * lg;
@@ -413,14 +509,15 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
             for (int e = 0; e < 8; ++e) A[m].v[e] = a0.v[e] * a1.v[e];
           }
         }
-        F Bv[5];
+        F Bv[4];
 #pragma unroll
         for (int n = 0; n < 4; ++n) frag_ld(Bv[n], &vT[(16 * n + l16) * KP + jb]);
-        frag_ones_if(Bv[4], l16 == 0);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m) {
 #pragma unroll
-          for (int n = 0; n < 5; ++n) mma(acc[m][n], A[m], Bv[n]);
+          for (int n = 0; n < 4; ++n) mma(acc[m][n], A[m], Bv[n]);
+          mma(acc[m][4], A[m], ones);
+        }
       }
     }
   }
@@ -428,13 +525,15 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
   // ---- final state -> ABI layout (raw moments, each packed entry once) ----
   if (state_out != nullptr) {
     if (active) {
-      const float sh = pow2(nu * Ek + Ev), sz = pow2(nu * Ek);
+      const float sh = pow2(nu * Ek + Ev + beta), sz = pow2(nu * Ek + beta);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const long f = fidx[m][e];
-          if (f < 0 || !fcanon[m][e]) continue;
+          int r, t, mu;
+          if (!kfeature(DH, kb, acc_position(m, 4 * lg + e), r, t, mu)) continue;
+          if (t != DH && r > t) continue;  // the (t, r) copy of a diagonal block writes it
+          const long f = abi_index(DH, r, t);
 #pragma unroll
           for (int n = 0; n < 4; ++n) state_out[sbase + f * DV + 16 * n + l16] = acc[m][n][e] * sh;
           if (l16 == 0) state_out[sbase + D * DV + f] = acc[m][4][e] * sz;
@@ -448,8 +547,89 @@ __global__ __launch_bounds__(256) void scan_kernel(const T* __restrict__ k, cons
 }
 
 // --------------------------------------------------------------------------
-// kernel 2: chunk readout + intra-chunk block + normalisation
+// kernel 2: per-head coefficient tables (once per call)
 // --------------------------------------------------------------------------
+
+// Per query head: the polynomial table [a, b_g / sqrt(d), sym(c)_gh / d]
+// (NPC floats), the exponent c_h with 2^c_h >= every feature coefficient
+// (kBadHead when a group id is out of range), and the feature coefficients
+// of the K-blocked layout divided by 2^c_h, with multiplicity two for the
+// off-diagonal pairs ([KB][32] elements).
+constexpr int kBadHead = 1 << 20;
+
+template <int NG>
+__host__ __device__ constexpr int npc() {
+  return 1 + NG + NG * NG;
+}
+
+template <typename T, int DH, int NG>
+__global__ __launch_bounds__(256) void coef_kernel(const int32_t* __restrict__ group_of_dim,
+                                                   const float* __restrict__ ca, const float* __restrict__ cb,
+                                                   const float* __restrict__ cc, int G,
+                                                   typename Cx<T>::E* __restrict__ cft, float* __restrict__ cpc,
+                                                   int* __restrict__ cex) {
+  typedef typename Cx<T>::E E;
+  constexpr int KB = n_kblocks(DH);
+  constexpr int NPC = npc<NG>();
+  __shared__ int gm[DH];
+  __shared__ float pc[NPC];
+  __shared__ int bad, ce;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float inv_sqrt_d = 1.f / sqrtf((float)DH);
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int r = tid; r < DH; r += blockDim.x) {
+    const int g = group_of_dim[h * DH + r];
+    gm[r] = g;
+    if (g < 0 || g >= G) atomicOr(&bad, 1);
+  }
+  for (int i2 = tid; i2 < NPC; i2 += blockDim.x) {
+    float val = 0.f;
+    if (i2 == 0) {
+      val = ca[h];
+    } else if (i2 <= NG) {
+      const int g = i2 - 1;
+      val = g < G ? cb[h * G + g] * inv_sqrt_d : 0.f;
+    } else {
+      const int gh = i2 - 1 - NG, g = gh / NG, g2 = gh % NG;
+      val = (g < G && g2 < G) ? 0.5f * (cc[(h * G + g) * G + g2] + cc[(h * G + g2) * G + g]) / DH : 0.f;
+    }
+    pc[i2] = val;
+    cpc[(long)h * NPC + i2] = val;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float mx = 0.f;
+    for (int g = 0; g < NG; ++g) {
+      mx = fmaxf(mx, fabsf(pc[1 + g]));
+      for (int g2 = 0; g2 < NG; ++g2) mx = fmaxf(mx, 2.f * fabsf(pc[1 + NG + g * NG + g2]));
+    }
+    const int e = exp_above(mx);
+    ce = e == kNegExp ? 0 : e;
+    cex[h] = bad ? kBadHead : ce;
+  }
+  __syncthreads();
+  const float sc = pow2(-ce);
+  for (int idx = tid; idx < KB * 32; idx += blockDim.x) {
+    const int kk = idx / 32, pos = idx % 32;
+    float val = 0.f;
+    int r, t, mu;
+    if (!bad && kfeature(DH, kk, pos, r, t, mu)) {
+      if (t == DH) val = pc[1 + gm[r]];
+      else val = (float)mu * pc[1 + NG + gm[r] * NG + gm[t]];
+    }
+    cft[(long)h * KB * 32 + idx] = (E)(val * sc);
+  }
+}
+
+// --------------------------------------------------------------------------
+// kernel 3: chunk readout + intra-chunk block + normalisation
+// --------------------------------------------------------------------------
+
+// Readout CTAs have NW = 4 or 8 waves: wave w owns rows 16 (w % 4) .. of the
+// chunk and the heads hh with hh % (NW / 4) == w / 4.  Eight waves give two
+// waves per SIMD but only 256 registers each (up to four heads per wave
+// fit); four waves give 512 registers each (seven heads per wave).
 
 // Dynamic LDS layout of the readout kernel (bytes), for RG heads per pass.
 struct ReadoutLds {
@@ -466,16 +646,17 @@ __host__ __device__ inline ReadoutLds readout_lds(int RG) {
   L.kh = L.coef + (long)RG * KB * 32 * sizeof(E);
   L.vt = L.kh + (long)C * DHP * sizeof(E);
   L.bst = L.vt + (long)DV * (C + 8) * sizeof(T);
-  L.total = L.bst + 2L * KG * NCOL * 32 * sizeof(E);
+  // two stage buffers of KG K-blocks, columns padded to SP elements
+  L.total = L.bst + 2L * KG * NCOL * stage_pitch<E>() * sizeof(E);
   return L;
 }
 
-template <typename T, int DH, int RMAX, int NG, bool PREMAP>
-__global__ __launch_bounds__(256) void readout_kernel(
+template <typename T, int DH, int RMAX, int NG, bool PREMAP, int NW>
+__global__ __launch_bounds__(64 * NW) void readout_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ group_of_dim, const float* __restrict__ ca, const float* __restrict__ cb,
-    const float* __restrict__ cc, int G, const float* __restrict__ gamma_q, const float* __restrict__ beta_q,
-    const float* __restrict__ gamma_k, const float* __restrict__ beta_k, float ln_eps,
+    const typename Cx<T>::E* __restrict__ cft, const float* __restrict__ cpc, const int* __restrict__ cex,
+    const float* __restrict__ gamma_q, const float* __restrict__ beta_q, const float* __restrict__ gamma_k,
+    const float* __restrict__ beta_k, float ln_eps, const int32_t* __restrict__ group_of_dim,
     const typename Cx<T>::E* __restrict__ snap, const int* __restrict__ sexp, const float* __restrict__ sconst,
     int has_state_in, T* __restrict__ y, int Hq, int Hkv, int N, int nchunks, int RG) {
   typedef typename Cx<T>::E E;
@@ -487,11 +668,13 @@ __global__ __launch_bounds__(256) void readout_kernel(
   constexpr int DHP = DH + 8;
   constexpr int VP = C + 8;
   constexpr int STEPS = (DH + 31) / 32;  // K steps of the score GEMM
-  constexpr int NPC = 1 + NG + NG * NG;
+  constexpr int NPC = npc<NG>();
   constexpr int QD = DH / 4;
+  constexpr int NT = 64 * NW;
+  constexpr int HS = NW / 4;  // head split between the waves of a row tile
 
   extern __shared__ __align__(16) unsigned char lds[];
-  const ReadoutLds LL = readout_lds<T, DH>(RG);
+  const ReadoutLds LL = readout_lds<T, DH>(RMAX);
   E* qh = reinterpret_cast<E*>(lds + LL.qh);      // [RG][C][DHP] q / 2^f
   E* coef = reinterpret_cast<E*>(lds + LL.coef);  // [RG][KB][32] coefficients / 2^c_h
   E* kh = reinterpret_cast<E*>(lds + LL.kh);      // [C][DHP] k / 2^aK
@@ -501,11 +684,10 @@ __global__ __launch_bounds__(256) void readout_kernel(
   __shared__ float kscale[KB];  // per-K-block fold factor 2^(15 + tau - tau_max(type))
   __shared__ int qoff[NQ][4];   // quadratic K-block, lane group -> r0 | t0 << 16
   __shared__ int gm[RMAX][DH];
-  __shared__ float pc[RMAX][NPC];  // a, b_g/sqrt(d), sym(c)_gh/d
+  __shared__ float pc[RMAX][NPC];
   __shared__ int cexp[RMAX];
-  __shared__ int badh[RMAX];
   __shared__ float cst[NCOL];
-  __shared__ float wmx[4];
+  __shared__ float wmx[NW];
   __shared__ int sc_int[3];  // aK, tau_quad_max, tau_lin_max
 
   const int c = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
@@ -513,49 +695,52 @@ __global__ __launch_bounds__(256) void readout_kernel(
   const int R = Hq / Hkv;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int lg = lane / 16, l16 = lane % 16;
+  const int rt = wave % 4, kpar = wave / 4;  // row tile, head class
   const int j0 = c * C;
   const int nvalid = min(C, N - j0);
-  const float inv_sqrt_d = 1.f / sqrtf((float)DH);
   const bool inter = c > 0 || has_state_in;
   const long sidx = (long)c * BH + bh;
-  const int srow = tid / 4, sq = tid % 4;
+  const int srow = (tid / 4) % C, sq = tid % 4;  // staging (threads < 256): row, quarter
+  const bool stager = tid < 4 * C;
 
   // ---- chunk-wide prologue: K (scores), V (P . V), snapshot scales ----
   {
     float kx[QD];
     const T* kp = k + ((long)bh * N + j0) * DH;
     const T* vp = v + ((long)bh * N + j0) * DV;
-    if (srow < nvalid) {
-      load_vals<QD>(kp + (long)srow * DH + sq * QD, kx);
 #pragma unroll
-      for (int i = 0; i < 16; i += 8) {
-        // raw copy of the values into the transposed tile
-        if constexpr (IsBf16<T>::value) {
-          const uint4 w = *reinterpret_cast<const uint4*>(vp + (long)srow * DV + sq * 16 + i);
-          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int i = 0; i < QD; ++i) kx[i] = 0.f;
+    if (stager) {
+      if (srow < nvalid) {
+        load_vals<QD>(kp + (long)srow * DH + sq * QD, kx);
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            vTi[(sq * 16 + i + 2 * jj) * VP + srow] = (uint16_t)(ws[jj] & 0xffffu);
-            vTi[(sq * 16 + i + 2 * jj + 1) * VP + srow] = (uint16_t)(ws[jj] >> 16);
+        for (int i = 0; i < 16; i += 8) {
+          // raw copy of the values into the transposed tile
+          if constexpr (IsBf16<T>::value) {
+            const uint4 w = *reinterpret_cast<const uint4*>(vp + (long)srow * DV + sq * 16 + i);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              vTi[(sq * 16 + i + 2 * jj) * VP + srow] = (uint16_t)(ws[jj] & 0xffffu);
+              vTi[(sq * 16 + i + 2 * jj + 1) * VP + srow] = (uint16_t)(ws[jj] >> 16);
+            }
+          } else {
+            float t8[8];
+            load_vals<8>(vp + (long)srow * DV + sq * 16 + i, t8);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) vTi[(sq * 16 + i + jj) * VP + srow] = t8[jj];
           }
-        } else {
-          float t8[8];
-          load_vals<8>(vp + (long)srow * DV + sq * 16 + i, t8);
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) vTi[(sq * 16 + i + jj) * VP + srow] = t8[jj];
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vTi[(sq * 16 + i) * VP + srow] = T(0);
       }
-    } else {
+      if (PREMAP) {
+        premap4<DH, QD>(kx, sq * QD, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
+        if (srow >= nvalid)
 #pragma unroll
-      for (int i = 0; i < QD; ++i) kx[i] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) vTi[(sq * 16 + i) * VP + srow] = T(0);
-    }
-    if (PREMAP) {
-      premap4<DH, QD>(kx, sq * QD, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
-      if (srow >= nvalid)
-#pragma unroll
-        for (int i = 0; i < QD; ++i) kx[i] = 0.f;
+          for (int i = 0; i < QD; ++i) kx[i] = 0.f;
+      }
     }
     float mk = 0.f;
 #pragma unroll
@@ -563,110 +748,84 @@ __global__ __launch_bounds__(256) void readout_kernel(
     mk = wave_max(mk);
     if (lane == 0) wmx[wave] = mk;
     if (tid < NCOL) cst[tid] = inter ? sconst[sidx * NCOL + tid] : 0.f;
-    __syncthreads();
-    int aK = exp_above(fmaxf(fmaxf(wmx[0], wmx[1]), fmaxf(wmx[2], wmx[3])));
-    if (aK == kNegExp) aK = 0;
-    const float sk = pow2(-aK);
-#pragma unroll
-    for (int i = 0; i < QD; ++i) kh[srow * DHP + sq * QD + i] = (E)(kx[i] * sk);
+    for (int idx = tid; idx < NQ * 4; idx += NT) {
+      // padding pairs read row offset 0; their coefficients are zero
+      int rb, tb;
+      pair_of(DH, 2 * (idx / 4) + (idx % 4) / 2, rb, tb);
+      qoff[idx / 4][idx % 4] = rb < 0 ? 0 : (4 * rb + 2 * (idx % 2)) | ((4 * tb) << 16);
+    }
     if (tid == 0) {
-      sc_int[0] = aK;
       int tq = kNegExp, tl = kNegExp;
       if (inter) {
         const int* ex = sexp + sidx * (KB + 2);
         const int Ek = ex[KB];
         for (int kk = 0; kk < KB; ++kk) {
-          const int be = ex[kk];
-          if (be == kNegExp) continue;
-          if (kk < NQ) tq = max(tq, be + 2 * Ek);
-          else tl = max(tl, be + Ek);
+          if (kk < NQ) tq = max(tq, ex[kk] + 2 * Ek);
+          else tl = max(tl, ex[kk] + Ek);
         }
       }
       sc_int[1] = tq;
       sc_int[2] = tl;
     }
     __syncthreads();
-    for (int idx = tid; idx < NQ * 4; idx += blockDim.x) {
-      // padding pairs read row offset 0; their coefficients are zero
-      int rb, tb;
-      pair_of(DH, 2 * (idx / 4) + (idx % 4) / 2, rb, tb);
-      qoff[idx / 4][idx % 4] = rb < 0 ? 0 : (4 * rb + 2 * (idx % 2)) | ((4 * tb) << 16);
+    float mall = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mall = fmaxf(mall, wmx[w]);
+    int aK = exp_above(mall);
+    if (aK == kNegExp) aK = 0;
+    if (stager) {
+      const float sk = pow2(-aK);
+#pragma unroll
+      for (int i = 0; i < QD; ++i) kh[srow * DHP + sq * QD + i] = (E)(kx[i] * sk);
     }
+    if (tid == 0) sc_int[0] = aK;
     if (tid < KB) {
       float f = 0.f;
       if (inter) {
         const int* ex = sexp + sidx * (KB + 2);
         const int be = ex[tid], Ek = ex[KB];
-        if (be != kNegExp) {
-          const int tau = tid < NQ ? be + 2 * Ek : be + Ek;
-          const int tmax = tid < NQ ? sc_int[1] : sc_int[2];
-          f = pow2(15 + tau - tmax);
-        }
+        const int tau = tid < NQ ? be + 2 * Ek : be + Ek;
+        const int tmax = tid < NQ ? sc_int[1] : sc_int[2];
+        f = pow2(15 + tau - tmax);
       }
       kscale[tid] = f;
     }
   }
+  __syncthreads();
   const int aK = sc_int[0];
-  // units of the inter partial sums: an all-zero block type takes the other's
   const int tau_q = sc_int[1] != kNegExp ? sc_int[1] : (sc_int[2] != kNegExp ? sc_int[2] : 0);
   const int tau_l = sc_int[2] != kNegExp ? sc_int[2] : tau_q;
   const int Ev = inter ? sexp[sidx * (KB + 2) + KB + 1] : 0;
+  const int row = 16 * rt + l16;  // A-operand row of this lane
 
-  for (int h0 = 0; h0 < R; h0 += RG) {
-    const int nh = min(RG, R - h0);
+  for (int h0 = 0; h0 < R; h0 += RMAX) {
+    constexpr int nh = RMAX;         // head slots per pass
+    const int nreal = min(RMAX, R - h0);  // slots beyond are dead: zero features, no output
     __syncthreads();  // previous head group done with qh / coef / bst
-    // ---- per-head coefficients (row a2) ----
-    for (int idx = tid; idx < nh * DH; idx += blockDim.x) {
-      const int hh = idx / DH, r = idx % DH, h = kvh * R + h0 + hh;
-      gm[hh][r] = group_of_dim[h * DH + r];
+    // ---- per-head tables (precomputed) ----
+    {
+      constexpr int VEC = 16 / sizeof(E);
+      const int nv = nh * KB * 32 / VEC, nvr = nreal * KB * 32 / VEC;
+      const uint4* src = reinterpret_cast<const uint4*>(cft + (long)(kvh * R + h0) * KB * 32);
+      for (int i = tid; i < nv; i += NT) reinterpret_cast<uint4*>(coef)[i] = i < nvr ? src[i] : make_uint4(0, 0, 0, 0);
     }
-    if (tid < RMAX) badh[tid] = 0;
-    __syncthreads();
-    for (int idx = tid; idx < nh * DH; idx += blockDim.x) {
+    for (int idx = tid; idx < nh * DH; idx += NT) {
       const int hh = idx / DH, r = idx % DH;
-      if (gm[hh][r] < 0 || gm[hh][r] >= G) atomicOr(&badh[hh], 1);
+      gm[hh][r] = hh < nreal ? group_of_dim[(kvh * R + h0 + hh) * DH + r] : 0;
     }
-    for (int idx = tid; idx < nh * NPC; idx += blockDim.x) {
-      const int hh = idx / NPC, i2 = idx % NPC, h = kvh * R + h0 + hh;
-      float val = 0.f;
-      if (i2 == 0) {
-        val = ca[h];
-      } else if (i2 <= NG) {
-        const int g = i2 - 1;
-        val = g < G ? cb[h * G + g] * inv_sqrt_d : 0.f;
-      } else {
-        const int gh = i2 - 1 - NG, g = gh / NG, g2 = gh % NG;
-        val = (g < G && g2 < G) ? 0.5f * (cc[(h * G + g) * G + g2] + cc[(h * G + g2) * G + g]) / DH : 0.f;
-      }
-      pc[hh][i2] = val;
+    for (int idx = tid; idx < nh * NPC; idx += NT) {
+      const int hh = idx / NPC, i2 = idx % NPC;
+      pc[hh][i2] = hh < nreal ? cpc[(long)(kvh * R + h0 + hh) * NPC + i2] : 0.f;
     }
-    __syncthreads();
-    if (tid < nh) {
-      // normaliser of the feature coefficients: 2^cexp >= every |coefficient|
-      float mx = 0.f;
-      for (int g = 0; g < NG; ++g) {
-        mx = fmaxf(mx, fabsf(pc[tid][1 + g]));
-        for (int g2 = 0; g2 < NG; ++g2) mx = fmaxf(mx, 2.f * fabsf(pc[tid][1 + NG + g * NG + g2]));
-      }
-      const int e = exp_above(mx);
-      cexp[tid] = e == kNegExp ? 0 : e;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < nh * KB * 32; idx += blockDim.x) {
-      const int hh = idx / (KB * 32), kk = (idx / 32) % KB, pos = idx % 32;
-      float val = 0.f;
-      int r, t, mu;
-      if (!badh[hh] && kfeature(DH, kk, pos, r, t, mu)) {
-        if (t == DH) val = pc[hh][1 + gm[hh][r]];
-        else val = (float)mu * pc[hh][1 + NG + gm[hh][r] * NG + gm[hh][t]];
-      }
-      coef[idx] = (E)(val * pow2(-cexp[hh]));
-    }
+    if (tid < nh) cexp[tid] = tid < nreal ? cex[kvh * R + h0 + tid] : 0;
     // ---- stage q rows of the head group (pre-map, row exponent) ----
-    for (int it = 0; it < nh; ++it) {
-      const int h = kvh * R + h0 + it;
+#pragma unroll 1
+    for (int it0 = 0; it0 < nh; it0 += NT / (4 * C)) {
+      const int it = it0 + tid / (4 * C);
+      const bool live = it < nreal;
+      const int h = kvh * R + h0 + (live ? it : 0);
       float qx[QD];
-      if (srow < nvalid) {
+      if (live && srow < nvalid) {
         load_vals<QD>(q + ((long)(b * Hq + h) * N + j0 + srow) * DH + sq * QD, qx);
       } else {
 #pragma unroll
@@ -681,164 +840,34 @@ __global__ __launch_bounds__(256) void readout_kernel(
       int f = exp_above(mq);
       if (f == kNegExp || srow >= nvalid) f = 0;
       const float s = pow2(-f);
+      if (it < nh) {
 #pragma unroll
-      for (int i = 0; i < QD; ++i) qh[((long)it * C + srow) * DHP + sq * QD + i] = srow < nvalid ? (E)(qx[i] * s) : (E)0.f;
-      if (sq == 0) qexp[it][srow] = f;
+        for (int i = 0; i < QD; ++i)
+          qh[((long)it * C + srow) * DHP + sq * QD + i] = live && srow < nvalid ? (E)(qx[i] * s) : (E)0.f;
+        if (sq == 0) qexp[it][srow] = f;
+      }
     }
     __syncthreads();
 
-    // ---- inter-chunk read: phi_q(Q_c) . S_c ----
-    f32x4 acc[RMAX][5];
+    // ---- accumulators: this wave serves the heads hh = HS j + kpar ----
+    // acc[j] holds, per row, (intra part + constant feature) pre-scaled into
+    // the units of the inter partial sums, to which the inter read then adds;
+    // units (value columns / normaliser) are 2^(f + c_h + tau_l - 15 + Ev) /
+    // 2^(f + c_h + tau_l - 15) during the linear K-blocks and, after one
+    // rescale by 2^(tau_l - tau_q - f), 2^(2 f + c_h + tau_q - 15 + Ev) /
+    // 2^(2 f + c_h + tau_q - 15).  y = num / den then only needs 2^Ev.
+    constexpr int HOWN = (RMAX + HS - 1) / HS;
+    f32x4 acc[HOWN][5];
 #pragma unroll
-    for (int hh = 0; hh < RMAX; ++hh)
+    for (int j = 0; j < HOWN; ++j)
 #pragma unroll
-      for (int n = 0; n < 5; ++n) acc[hh][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int row = 16 * wave + l16;  // A-operand row of this lane
+      for (int n = 0; n < 5; ++n) acc[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (inter) {
-      const E* sbase = snap + sidx * KB * NCOL * 32;
-      constexpr int BLK = NCOL * 32;                // elements per staged K-block
-      constexpr int VEC = 16 / sizeof(E);           // elements per 16-byte vector
-      constexpr int NV16 = KG * BLK / VEC;          // vectors per stage
-      constexpr int PER = (NV16 + 255) / 256;
-      // staging order: the linear K-blocks padded to whole stages, then the
-      // quadratic ones; slot i -> K-block (or -1 for a padding slot)
-      constexpr int NLS = (NL + KG - 1) / KG * KG;
-      constexpr int NSL = NLS / KG;                 // linear stages
-      constexpr int NSTAGE = NSL + (NQ + KG - 1) / KG;
-      auto kb_at = [&](int i) { return i < NLS ? (i < NL ? NQ + i : -1) : (i - NLS < NQ ? i - NLS : -1); };
-      uint4 pre[PER];
-      auto fetch = [&](int sg) {
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int vi = tid + 256 * u;
-          if (vi < NV16) {
-            const int slot = vi / (BLK / VEC), off = vi % (BLK / VEC);
-            const int kk = kb_at(sg * KG + slot);
-            if (kk >= 0) pre[u] = reinterpret_cast<const uint4*>(sbase + (long)kk * BLK)[off];
-          }
-        }
-      };
-      auto put = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int vi = tid + 256 * u;
-          if (vi < NV16) reinterpret_cast<uint4*>(bst + (long)buf * KG * BLK)[vi] = pre[u];
-        }
-      };
-      auto load_b = [&](F (&Bf)[5], int buf, int slot) {
-        const E* bp = bst + ((long)buf * KG + slot) * BLK + 8 * lg;
-#pragma unroll
-        for (int n = 0; n < 4; ++n) frag_ld(Bf[n], bp + (16 * n + l16) * 32);
-        if (l16 == 0) frag_ld(Bf[4], bp + DV * 32);
-        else frag_zero(Bf[4]);
-      };
-      fetch(0);
-      put(0);
-      __syncthreads();
-      // -- linear K-blocks: (q_u ks) coef; the row factor 2^-f of the
-      //    constant "one" is applied when the partial sums are rescaled --
-      for (int sg = 0; sg < NSL; ++sg) {
-        const int buf = sg & 1;
-        fetch(sg + 1);
-#pragma unroll
-        for (int slot = 0; slot < KG; ++slot) {
-          const int kk = kb_at(sg * KG + slot);
-          if (kk < 0) continue;
-          const float ks = kscale[kk];
-          if (ks == 0.f) continue;
-          F Bf[5];
-          load_b(Bf, buf, slot);
-          const int u0 = 32 * (kk - NQ) + 8 * lg;
-          const bool live = u0 < DH;
-          const int uo = live ? u0 : 0;
-#pragma unroll
-          for (int hh = 0; hh < RMAX; ++hh) {
-            if (hh >= nh) break;
-            const E* qrow = qh + ((long)hh * C + row) * DHP;
-            const E* cf = coef + ((long)hh * KB + kk) * 32 + 8 * lg;
-            F A;
-            if constexpr (IsBf16<T>::value) {
-              const _Float16 s16 = (_Float16)ks;
-              const h8 qv = *reinterpret_cast<const h8*>(qrow + uo);
-              const h8 cv = *reinterpret_cast<const h8*>(cf);
-              A.v = (qv * h8{s16, s16, s16, s16, s16, s16, s16, s16}) * cv;
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) A.v[e] = (qrow[uo + e] * ks) * cf[e];
-            }
-#pragma unroll
-            for (int n = 0; n < 5; ++n) mma(acc[hh][n], A, Bf[n]);
-          }
-        }
-        put(buf ^ 1);
-        __syncthreads();
-      }
-      // move the linear partial sums to quadratic units: per row a factor
-      // 2^(f + tau_l - 2 f - tau_q)
-#pragma unroll
-      for (int hh = 0; hh < RMAX; ++hh) {
-        if (hh >= nh) break;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float fr = pow2(tau_l - tau_q - qexp[hh][16 * wave + 4 * lg + e]);
-#pragma unroll
-          for (int n = 0; n < 5; ++n) acc[hh][n][e] *= fr;
-        }
-      }
-      // -- quadratic K-blocks: (q_r ks) q_t coef for r in {r0, r0 + 1} and
-      //    t in t0..t0+3 (offsets of this lane group from qoff) --
-      for (int sg = NSL; sg < NSTAGE; ++sg) {
-        const int buf = sg & 1;
-        if (sg + 1 < NSTAGE) fetch(sg + 1);
-#pragma unroll
-        for (int slot = 0; slot < KG; ++slot) {
-          const int kk = kb_at(sg * KG + slot);
-          if (kk < 0) continue;
-          const float ks = kscale[kk];
-          if (ks == 0.f) continue;
-          F Bf[5];
-          load_b(Bf, buf, slot);
-          const int off = qoff[kk][lg];
-          const int r0 = off & 0xffff, t0 = off >> 16;
-#pragma unroll
-          for (int hh = 0; hh < RMAX; ++hh) {
-            if (hh >= nh) break;
-            const E* qrow = qh + ((long)hh * C + row) * DHP;
-            const E* cf = coef + ((long)hh * KB + kk) * 32 + 8 * lg;
-            F A;
-            if constexpr (IsBf16<T>::value) {
-              const _Float16 s16 = (_Float16)ks;
-              const h8 cv = *reinterpret_cast<const h8*>(cf);
-              const h2 rs = *reinterpret_cast<const h2*>(qrow + r0) * h2{s16, s16};
-              const h4 tq = *reinterpret_cast<const h4*>(qrow + t0);
-              const h2 t01 = h2{tq[0], tq[1]}, t23 = h2{tq[2], tq[3]};
-              const h2 e0 = (rs.xx * t01) * h2{cv[0], cv[1]};
-              const h2 e1 = (rs.xx * t23) * h2{cv[2], cv[3]};
-              const h2 e2 = (rs.yy * t01) * h2{cv[4], cv[5]};
-              const h2 e3 = (rs.yy * t23) * h2{cv[6], cv[7]};
-              A.v = h8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) A.v[e] = (qrow[r0 + e / 4] * ks) * qrow[t0 + e % 4] * cf[e];
-            }
-#pragma unroll
-            for (int n = 0; n < 5; ++n) mma(acc[hh][n], A, Bf[n]);
-          }
-        }
-        if (sg + 1 < NSTAGE) put(buf ^ 1);
-        __syncthreads();
-      }
-    }
-
-    // ---- intra-chunk block and normalisation, per head ----
-#pragma unroll
-    for (int hh = 0; hh < RMAX; ++hh) {
-      if (hh >= nh) break;
-      const int h = kvh * R + h0 + hh;
-      float pcr[NPC];
-#pragma unroll
-      for (int i2 = 0; i2 < NPC; ++i2) pcr[i2] = pc[hh][i2];
+    // ---- intra-chunk block (one head at a time) ----
+#pragma unroll 1
+    for (int j = 0; j < HOWN; ++j) {
+      const int hh = HS * j + kpar;
+      const float* pcr = pc[hh];  // LDS
       // masked query fragments per group (B operand of the transposed scores)
       F Bq[NG][STEPS];
       {
@@ -864,16 +893,15 @@ __global__ __launch_bounds__(256) void readout_kernel(
       // raw dot products: q / 2^f_row times k / 2^aK (the polynomial table
       // carries the 1/sqrt(d) and 1/d of the scores)
       const float sfac = pow2(qexp[hh][row] + aK);
-      f32x4 iacc[5];
+      f32x4 cur[5];
 #pragma unroll
-      for (int n = 0; n < 5; ++n) iacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int it = wave;  // row tile of this wave
-      for (int jt0 = 0; jt0 <= it; jt0 += 2) {
+      for (int n = 0; n < 5; ++n) cur[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int jt0 = 0; jt0 <= rt; jt0 += 2) {
         float p[8];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int jt = jt0 + half;
-          if (jt > it) {
+          if (jt > rt) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) p[4 * half + e] = 0.f;
             continue;
@@ -919,43 +947,229 @@ __global__ __launch_bounds__(256) void readout_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             vb[e] = to_f32(vr[ja + e]);
-            vb[4 + e] = jb + e < C ? to_f32(vr[jb + e]) : 0.f;
+            vb[4 + e] = to_f32(vr[jb + e]);
           }
-          mma(iacc[n], A, frag_from<IsBf16<T>::value>(vb));
+          mma(cur[n], A, frag_from<IsBf16<T>::value>(vb));
         }
         float ones[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ones[e] = l16 == 0 ? 1.f : 0.f;
-        mma(iacc[4], A, frag_from<IsBf16<T>::value>(ones));
+        mma(cur[4], A, frag_from<IsBf16<T>::value>(ones));
       }
-
-      // ---- combine, normalise, store ----
-      // inter units: rows 2^(2 f + cexp + tau_q - 15), value columns also 2^Ev
-      float den[4];
+      // constant feature and pre-scaling into the linear-block units
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int rr = 16 * wave + 4 * lg + e;
-        const float ui = inter ? pow2(2 * qexp[hh][rr] + cexp[hh] + tau_q - 15) : 0.f;
-        float dsum = iacc[4][e] + pcr[0] * cst[DV];
-        if (inter) dsum += acc[hh][4][e] * ui;
-        den[e] = __shfl(dsum, (lane & ~15));  // column 64 lives in lane l16 == 0
-        const float uv = ui * pow2(Ev);
+        const int rr = 16 * rt + 4 * lg + e;
+        const float uz = inter ? pow2(-(qexp[hh][rr] + cexp[hh] + tau_l - 15)) : 1.f;
+        const float uh = inter ? uz * pow2(-Ev) : 1.f;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const float num = iacc[n][e] + pcr[0] * cst[16 * n + l16] + (inter ? acc[hh][n][e] * uv : 0.f);
-          iacc[n][e] = num;
+        for (int n = 0; n < 4; ++n) cur[n][e] = (cur[n][e] + pcr[0] * cst[16 * n + l16]) * uh;
+        cur[4][e] = (cur[4][e] + pcr[0] * cst[DV]) * uz;
+      }
+      // static placement keeps every accumulator set in registers
+#pragma unroll
+      for (int jj = 0; jj < HOWN; ++jj)
+        if (jj == j)
+#pragma unroll
+          for (int n = 0; n < 5; ++n) acc[jj][n] = cur[n];
+    }
+
+    // ---- inter-chunk read: phi_q(Q_c) . S_c ----
+    if (inter) {
+      const E* sbase = snap + sidx * KB * NCOL * 32;
+      constexpr int BLK = NCOL * 32;                // elements per snapshot K-block
+      constexpr int SP = stage_pitch<E>();          // staged column pitch
+      constexpr int SBLK = NCOL * SP;               // elements per staged K-block
+      constexpr int VEC = 16 / sizeof(E);           // elements per 16-byte vector
+      constexpr int VPB = BLK / VEC;                // vectors per K-block
+      constexpr int NV16 = KG * VPB;                // vectors per stage
+      constexpr int PER = (NV16 + NT - 1) / NT;
+      // stage 0 holds the linear K-blocks (NL <= KG), stages 1.. the quadratic ones
+      static_assert(NL <= KG, "one linear stage");
+      constexpr int NSTAGE = 1 + (NQ + KG - 1) / KG;
+      auto kb_at = [&](int sg, int slot) __attribute__((always_inline)) {
+        // padding slots map to a real K-block; their scale is forced to zero
+        return sg == 0 ? NQ + min(slot, NL - 1) : min((sg - 1) * KG + slot, NQ - 1);
+      };
+      auto slot_live = [&](int sg, int slot) __attribute__((always_inline)) {
+        return sg == 0 ? slot < NL : (sg - 1) * KG + slot < NQ;
+      };
+      struct StageRegs {
+        uint4 v[PER];
+      };
+      // unconditional loads (clamped to valid addresses) keep the stage in
+      // registers; vectors beyond the stage are never written to LDS
+      auto fetch = [&](int sg) __attribute__((always_inline)) {
+        StageRegs r;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int vi = min(tid + NT * u, NV16 - 1);
+          r.v[u] = reinterpret_cast<const uint4*>(sbase + (long)kb_at(sg, vi / VPB) * BLK)[vi % VPB];
+        }
+        return r;
+      };
+      // LDS copy with columns padded to SP elements (80-byte pitch for fp16):
+      // the 16 lanes of a lane group then read conflict-free
+      auto put = [&](int buf, const StageRegs r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const int vi = tid + NT * u;
+          if (vi < NV16) {
+            const int slot = vi / VPB, w = vi % VPB, col = w / (32 / VEC), part = w % (32 / VEC);
+            *reinterpret_cast<uint4*>(bst + ((long)buf * KG + slot) * SBLK + col * SP + part * VEC) = r.v[u];
+          }
+        }
+      };
+      auto load_b = [&](F (&Bf)[5], int buf, int slot) __attribute__((always_inline)) {
+        const E* bp = bst + ((long)buf * KG + slot) * SBLK + 8 * lg;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) frag_ld(Bf[n], bp + (16 * n + l16) * SP);
+        if (l16 == 0) frag_ld(Bf[4], bp + DV * SP);
+        else frag_zero(Bf[4]);
+      };
+      // linear K-blocks: (q_u ks) coef; their row factor 2^-f (the row's
+      // "one") is applied when the partial sums are rescaled
+      auto compute_lin = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int slot = 0; slot < NL; ++slot) {
+          const int kk = NQ + slot;
+          F Bf[5];
+          load_b(Bf, buf, slot);
+          const int u0 = 32 * slot + 8 * lg;
+          const int uo = u0 < DH ? u0 : 0;  // padding features have zero coefficients
+#pragma unroll
+          for (int j = 0; j < HOWN; ++j) {
+            const int hh = HS * j + kpar;
+            const E* qrow = qh + ((long)hh * C + row) * DHP;
+            const E* cf = coef + ((long)hh * KB + kk) * 32 + 8 * lg;
+            F A;
+            if constexpr (IsBf16<T>::value) {
+              const _Float16 s16 = (_Float16)kscale[kk];
+              const h8 qv = *reinterpret_cast<const h8*>(qrow + uo);
+              const h8 cv = *reinterpret_cast<const h8*>(cf);
+              A.v = (qv * h8{s16, s16, s16, s16, s16, s16, s16, s16}) * cv;
+            } else {
+              const float ks = kscale[kk];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) A.v[e] = (qrow[uo + e] * ks) * cf[e];
+            }
+#pragma unroll
+            for (int n = 0; n < 5; ++n) mma(acc[j][n], A, Bf[n]);
+          }
+        }
+      };
+      // quadratic K-blocks: (q_r ks) q_t coef for r in {r0, r0 + 1}, t in
+      // t0..t0+3; branch-free so that the accumulators update in place
+      auto compute_quad = [&](int sg, int buf) __attribute__((always_inline)) {
+#pragma unroll 1
+        for (int slot = 0; slot < KG; ++slot) {
+          const int kk = kb_at(sg, slot);
+          const float ks = slot_live(sg, slot) ? kscale[kk] : 0.f;
+          F Bf[5];
+          load_b(Bf, buf, slot);
+          const int off = qoff[kk][lg];
+          const int r0 = off & 0xffff, t0 = off >> 16;
+#pragma unroll
+          for (int j = 0; j < HOWN; ++j) {
+            const int hh = HS * j + kpar;
+            const E* qrow = qh + ((long)hh * C + row) * DHP;
+            const E* cf = coef + ((long)hh * KB + kk) * 32 + 8 * lg;
+            F A;
+            if constexpr (IsBf16<T>::value) {
+              const _Float16 s16 = (_Float16)ks;
+              const h8 cv = *reinterpret_cast<const h8*>(cf);
+              const h2 rs = *reinterpret_cast<const h2*>(qrow + r0) * h2{s16, s16};
+              const h4 tq = *reinterpret_cast<const h4*>(qrow + t0);
+              const h2 t01 = h2{tq[0], tq[1]}, t23 = h2{tq[2], tq[3]};
+              const h2 e0 = (rs.xx * t01) * h2{cv[0], cv[1]};
+              const h2 e1 = (rs.xx * t23) * h2{cv[2], cv[3]};
+              const h2 e2 = (rs.yy * t01) * h2{cv[4], cv[5]};
+              const h2 e3 = (rs.yy * t23) * h2{cv[6], cv[7]};
+              A.v = h8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) A.v[e] = (qrow[r0 + e / 4] * ks) * qrow[t0 + e % 4] * cf[e];
+            }
+#pragma unroll
+            for (int n = 0; n < 5; ++n) mma(acc[j][n], A, Bf[n]);
+          }
+        }
+      };
+      // pipeline: stage sg computes from LDS buffer sg & 1 while the loads of
+      // stages sg + 1 (registers, issued one stage earlier) and sg + 2
+      // (issued now) are in flight
+      StageRegs ra = fetch(0);
+      StageRegs rb2 = fetch(NSTAGE > 1 ? 1 : 0);
+      put(0, ra);
+      __syncthreads();
+      if (2 < NSTAGE) ra = fetch(2);
+      compute_lin(0);
+      put(1, rb2);
+      __syncthreads();
+      // linear K-blocks done: to quadratic units, 2^(tau_l - tau_q - f) per row
+#pragma unroll
+      for (int j = 0; j < HOWN; ++j) {
+        const int hh = HS * j + kpar;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float fr = pow2(tau_l - tau_q - qexp[hh][16 * rt + 4 * lg + e]);
+#pragma unroll
+          for (int n = 0; n < 5; ++n) acc[j][n][e] *= fr;
         }
       }
-      T* yp = y + ((long)(b * Hq + h) * N + j0) * DV;
-      const float nanv = __builtin_nanf("");
+      for (int sg = 1; sg < NSTAGE; sg += 2) {
+        if (sg + 2 < NSTAGE) rb2 = fetch(sg + 2);
+        compute_quad(sg, 1);
+        if (sg + 1 < NSTAGE) put(0, ra);
+        __syncthreads();
+        if (sg + 1 >= NSTAGE) break;
+        if (sg + 3 < NSTAGE) ra = fetch(sg + 3);
+        compute_quad(sg + 1, 0);
+        if (sg + 2 < NSTAGE) put(1, rb2);
+        __syncthreads();
+      }
+    }
+
+    // ---- normalise and store (one head at a time) ----
+    const float sev = inter ? pow2(Ev) : 1.f;
+    const float nanv = __builtin_nanf("");
+    // the wave's 16 x 64 output tile goes through its own LDS slice (the
+    // stage buffers are free now) and leaves as 16-byte row segments
+    T* yt = reinterpret_cast<T*>(bst) + wave * 16 * DV;
+#pragma unroll 1
+    for (int j = 0; j < HOWN; ++j) {
+      const int hh = HS * j + kpar;
+      if (hh >= nreal) break;
+      const int h = kvh * R + h0 + hh;
+      f32x4 cur[5];
+#pragma unroll
+      for (int n = 0; n < 5; ++n) cur[n] = acc[0][n];
+#pragma unroll
+      for (int jj = 1; jj < HOWN; ++jj)
+        if (jj == j)
+#pragma unroll
+          for (int n = 0; n < 5; ++n) cur[n] = acc[jj][n];
+      const bool badh = cexp[hh] == kBadHead;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int rr = 16 * wave + 4 * lg + e;
-        if (rr >= nvalid) continue;
+        const float den = __shfl(cur[4][e], (lane & ~15));  // column 64 lives in lane l16 == 0
+        // bf16 outputs: one reciprocal per row (its rounding is far below the
+        // output's); fp32 outputs: IEEE division
+        const float rden = IsBf16<T>::value ? sev / den : 0.f;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          const float val = badh[hh] ? nanv : iacc[n][e] / den[e];
-          store_elem(&yp[(long)rr * DV + 16 * n + l16], val);
+          const float val = badh ? nanv : (IsBf16<T>::value ? cur[n][e] * rden : (cur[n][e] * sev) / den);
+          store_elem(&yt[(4 * lg + e) * DV + 16 * n + l16], val);
+        }
+      }
+      {
+        constexpr int VPR = DV * sizeof(T) / 16;  // 16-byte vectors per row
+        T* yp = y + ((long)(b * Hq + h) * N + j0 + 16 * rt) * DV;
+#pragma unroll
+        for (int u = 0; u < 16 * VPR / 64; ++u) {
+          const int vi = lane + 64 * u, r = vi / VPR, cv = vi % VPR;
+          const uint4 w = reinterpret_cast<const uint4*>(yt)[vi];
+          if (16 * rt + r < nvalid) reinterpret_cast<uint4*>(yp + (long)r * DV)[cv] = w;
         }
       }
     }
@@ -970,31 +1184,37 @@ namespace {
 
 template <typename T, int DH>
 struct FwdWs {
-  long snap_bytes, exp_off, const_off, total;
+  long snap_bytes, exp_off, const_off, cft_off, cpc_off, cex_off, total;
 };
 
+constexpr int kNpcMax = 1 + 8 + 64;
+
 template <typename T, int DH>
-FwdWs<T, DH> fwd_ws(int B, int Hkv, int N) {
+FwdWs<T, DH> fwd_ws(int B, int Hq, int Hkv, int N) {
   typedef typename Cx<T>::E E;
   constexpr int KB = n_kblocks(DH);
   const long nchunks = (N + C - 1) / C;
   const long snaps = nchunks * B * Hkv;
+  auto up = [](long x) { return (x + 255) / 256 * 256; };
   FwdWs<T, DH> w;
   w.snap_bytes = snaps * KB * NCOL * 32 * (long)sizeof(E);
-  w.exp_off = (w.snap_bytes + 255) / 256 * 256;
-  w.const_off = w.exp_off + (snaps * (KB + 2) * 4 + 255) / 256 * 256;
-  w.total = w.const_off + snaps * NCOL * 4;
+  w.exp_off = up(w.snap_bytes);
+  w.const_off = w.exp_off + up(snaps * (KB + 2) * 4);
+  w.cft_off = w.const_off + up(snaps * NCOL * 4);
+  w.cpc_off = w.cft_off + up((long)Hq * KB * 32 * sizeof(E));
+  w.cex_off = w.cpc_off + up((long)Hq * kNpcMax * 4);
+  w.total = w.cex_off + up((long)Hq * 4);
   return w;
 }
 
-constexpr int kRmaxWide = 8;  // query heads per KV head served in one pass (bf16)
-
+// Query heads per KV head served in one pass: 4 (two per wave; eight waves),
+// 2, or 1; the last pass of a head count that is not a multiple carries dead
+// slots.  fp32 activations use at most 2.
 template <typename T, int DH>
 int pick_rg(int R) {
-  int rg = R < kRmaxWide ? R : kRmaxWide;
-  if (!IsBf16<T>::value && rg > 2) rg = 2;
-  while (rg > 1 && readout_lds<T, DH>(rg).total > 150 * 1024) --rg;
-  return rg;
+  if (R >= 3 && IsBf16<T>::value && readout_lds<T, DH>(4).total <= 148 * 1024) return 4;
+  if (R >= 2 && readout_lds<T, DH>(2).total <= 148 * 1024) return 2;
+  return 1;
 }
 
 }  // namespace
@@ -1005,23 +1225,26 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   const int nchunks = (a.N + C - 1) / C;
   const int BH = a.B * a.Hkv;
   constexpr int KB = n_kblocks(DH);
-  const FwdWs<T, DH> w = fwd_ws<T, DH>(a.B, a.Hkv, a.N);
+  const FwdWs<T, DH> w = fwd_ws<T, DH>(a.B, a.Hq, a.Hkv, a.N);
   unsigned char* ws = reinterpret_cast<unsigned char*>(a.workspace);
   E* snap = reinterpret_cast<E*>(ws);
   int* sexp = reinterpret_cast<int*>(ws + w.exp_off);
   float* sconst = reinterpret_cast<float*>(ws + w.const_off);
+  E* cft = reinterpret_cast<E*>(ws + w.cft_off);
+  float* cpc = reinterpret_cast<float*>(ws + w.cpc_off);
+  int* cex = reinterpret_cast<int*>(ws + w.cex_off);
   const T* qq = reinterpret_cast<const T*>(a.q);
   const T* kk = reinterpret_cast<const T*>(a.k);
   const T* vv = reinterpret_cast<const T*>(a.v);
   T* yy = reinterpret_cast<T*>(a.y);
   if (stages & 1) {
-    dim3 grid((KB + 3) / 4, BH);
+    dim3 grid((KB + kScanWaves - 1) / kScanWaves, BH);
     if (a.premap)
-      hipLaunchKernelGGL((scan_kernel<T, DH, true>), grid, dim3(256), 0, stream, kk, vv, a.gamma_k, a.beta_k,
-                         a.ln_eps, a.state_in, a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks);
+      hipLaunchKernelGGL((scan_kernel<T, DH, true>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv, a.gamma_k,
+                         a.beta_k, a.ln_eps, a.state_in, a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks);
     else
-      hipLaunchKernelGGL((scan_kernel<T, DH, false>), grid, dim3(256), 0, stream, kk, vv, nullptr, nullptr, 0.f,
-                         a.state_in, a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks);
+      hipLaunchKernelGGL((scan_kernel<T, DH, false>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv, nullptr,
+                         nullptr, 0.f, a.state_in, a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -1033,12 +1256,17 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   const int has_in = a.state_in != nullptr;
 #define OAL_OUT(RM, NGV, PM)                                                                                    \
   do {                                                                                                          \
-    auto fn = readout_kernel<T, DH, RM, NGV, PM>;                                                               \
+    hipLaunchKernelGGL((coef_kernel<T, DH, NGV>), dim3(a.Hq), dim3(256), 0, stream, a.group_of_dim, a.ca, a.cb, \
+                       a.cc, a.G, cft, cpc, cex);                                                               \
+    hipError_t e1 = hipGetLastError();                                                                          \
+    if (e1 != hipSuccess) return e1;                                                                            \
+    constexpr int NWV = (RM % 2 == 0 && RM <= 4) ? 8 : 4;                                                                         \
+    auto fn = readout_kernel<T, DH, RM, NGV, PM, NWV>;                                                          \
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),                                      \
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);                  \
     if (e2 != hipSuccess) return e2;                                                                            \
-    hipLaunchKernelGGL(fn, grid, dim3(256), shm, stream, qq, kk, vv, a.group_of_dim, a.ca, a.cb, a.cc, a.G,     \
-                       a.gamma_q, a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, snap, sexp, sconst, has_in, yy,      \
+    hipLaunchKernelGGL(fn, grid, dim3(64 * NWV), shm, stream, qq, kk, vv, cft, cpc, cex, a.gamma_q,             \
+                       a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, a.group_of_dim, snap, sexp, sconst, has_in, yy, \
                        a.Hq, a.Hkv, a.N, nchunks, rg);                                                          \
   } while (0)
 #define OAL_OUT_NG(RM, PM)                 \
@@ -1049,15 +1277,28 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
       default: OAL_OUT(RM, 8, PM); break;  \
     }                                      \
   } while (0)
-#define OAL_OUT_RM(PM)                                           \
-  do {                                                           \
-    if (rg <= 2 || !IsBf16<T>::value) OAL_OUT_NG(2, PM);         \
-    else OAL_OUT_NG(kRmaxWide, PM);                              \
-  } while (0)
   const int ng = a.G <= 1 ? 1 : a.G <= 4 ? 4 : 8;
-  if (a.premap) OAL_OUT_RM(true);
-  else OAL_OUT_RM(false);
-#undef OAL_OUT_RM
+#define OAL_OUT_RG(PM)                       \
+  do {                                       \
+    switch (rg) {                            \
+      case 1: OAL_OUT_NG(1, PM); break;      \
+      case 2: OAL_OUT_NG(2, PM); break;      \
+      default: OAL_OUT_NG(4, PM); break;     \
+    }                                        \
+  } while (0)
+  if constexpr (IsBf16<T>::value) {
+    if (a.premap) OAL_OUT_RG(true);
+    else OAL_OUT_RG(false);
+  } else {
+    if (rg == 2) {
+      if (a.premap) OAL_OUT_NG(2, true);
+      else OAL_OUT_NG(2, false);
+    } else {
+      if (a.premap) OAL_OUT_NG(1, true);
+      else OAL_OUT_NG(1, false);
+    }
+  }
+#undef OAL_OUT_RG
 #undef OAL_OUT_NG
 #undef OAL_OUT
   return hipGetLastError();

@@ -10,9 +10,9 @@ namespace oal {
 hipError_t launch_fwd_d16(const FwdLaunch& a, int stages, hipStream_t stream);
 hipError_t launch_fwd_d32(const FwdLaunch& a, int stages, hipStream_t stream);
 hipError_t launch_fwd_d64(const FwdLaunch& a, int stages, hipStream_t stream);
-size_t fwd_workspace_bytes_d16(int B, int Hkv, int N, int dtype);
-size_t fwd_workspace_bytes_d32(int B, int Hkv, int N, int dtype);
-size_t fwd_workspace_bytes_d64(int B, int Hkv, int N, int dtype);
+size_t fwd_workspace_bytes_d16(int B, int Hq, int Hkv, int N, int dtype);
+size_t fwd_workspace_bytes_d32(int B, int Hq, int Hkv, int N, int dtype);
+size_t fwd_workspace_bytes_d64(int B, int Hq, int Hkv, int N, int dtype);
 
 // state_out <- state_in (or zeros) for an empty sequence; a plain kernel so
 // that callers may capture it in a graph.
@@ -28,11 +28,11 @@ hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStr
   return hipGetLastError();
 }
 
-size_t fwd_workspace_bytes(int B, int Hkv, int N, int d_h, int dtype) {
+size_t fwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d_h, int dtype) {
   switch (d_h) {
-    case 16: return fwd_workspace_bytes_d16(B, Hkv, N, dtype);
-    case 32: return fwd_workspace_bytes_d32(B, Hkv, N, dtype);
-    default: return fwd_workspace_bytes_d64(B, Hkv, N, dtype);
+    case 16: return fwd_workspace_bytes_d16(B, Hq, Hkv, N, dtype);
+    case 32: return fwd_workspace_bytes_d32(B, Hq, Hkv, N, dtype);
+    default: return fwd_workspace_bytes_d64(B, Hq, Hkv, N, dtype);
   }
 }
 
