@@ -20,7 +20,6 @@ batched decode step with 256 x 16 fp32 states (HBM-bound).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,19 +30,13 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+COPY_BYTES = 1 << 30        # calibration copy for the HBM byte counters
+METRIC = "causal OAL attention tokens/s at 1 GPU; % bf16 MFMA peak (prefill), % HBM BW (decode)"
 DV = 64
 
 
 def feature_count(d):
     return 1 + d + d * (d + 1) // 2
-
-
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in ("oal_prefill.hip", "oal_device.h", "oal_layout.h", "oal_internal.h"):
-        with open(os.path.join(ROOT, "grouped_quadratic_softmax_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
 
 
 def load_traffic(key):
@@ -54,7 +47,8 @@ def load_traffic(key):
             rec = json.load(f).get(key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256") != kernel_source_hash():
+    from grouped_quadratic_softmax_amd.profiling import source_hash
+    if not rec or rec.get("source_sha256") != source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -150,10 +144,9 @@ def run_main(args):
     readout_flops = B * N * Hq * 2 * D * (DV + 1)         # one launch of the readout kernel
     update_flops = B * N * Hkv * 2 * D * (DV + 1)
     achieved = readout_flops / (out_ms * 1e-3) / 1e12
-    traffic = load_traffic("oal_out_kernel_c2")
+    traffic = load_traffic("readout_kernel_qwen_layer")
     result = {
-        "metric": "causal OAL attention tokens/s at 1 GPU (prefill + decode step); % bf16 MFMA peak "
-                  "(prefill readout), % HBM BW (decode)",
+        "metric": METRIC,
         "value": tokens_per_step / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -169,7 +162,7 @@ def run_main(args):
                                "bf16; step = chi + prefill(+final state) + 1 decode token/seq",
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {
-            "kernel": "out_kernel (oal_fwd_outputs: chunk readout + intra-chunk + normalise)",
+            "kernel": "readout_kernel (oal_fwd_outputs: coefficient tables, chunk readout, intra-chunk block, normalise)",
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
@@ -237,6 +230,39 @@ def run_secondary(args):
     return out
 
 
+def run_pmc_target(args):
+    """Launch only one kernel repeatedly, for rocprofv3 counter passes.
+
+    ``readout``: the chunk readout of the main workload (after one states
+    pass); ``copy``: a plain device copy of 1 GiB (fp32), whose FETCH_SIZE and
+    WRITE_SIZE readings calibrate the counters against a known byte count."""
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    import synthetic as S
+
+    if args.pmc_target == "copy":
+        n = COPY_BYTES // 4
+        src = torch.ones(n, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                          "launches": args.steps}), flush=True)
+        return
+    wl = S.make(2, seq_len=2048 + 1)
+    N = wl.seq_len - 1
+    q, k, v = (t[:, :, :N].contiguous() for t in device_inputs(wl))
+    pre = oal.PrefillPlan(q, k, v, coeffs_for(wl))
+    pre.states()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        pre.outputs()
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_target": "readout", "launches": args.steps}), flush=True)
+
+
 def cpu_baseline(wl, n_seq=2):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload:
     the first ``n_seq`` sequences, every query head, every token."""
@@ -272,6 +298,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--pmc-target", choices=("readout", "copy"), default=None,
+                    help="only launch this kernel --steps times (for rocprofv3 counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -282,6 +310,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.pmc_target:
+        run_pmc_target(args)
+        return
     result, wl = run_main(args)
     print(f"[bench] main done: {result['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
     if not args.no_secondary:

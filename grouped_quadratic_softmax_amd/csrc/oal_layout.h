@@ -40,7 +40,7 @@ __host__ __device__ constexpr int n_kblocks(int d) { return nq_kblocks(d) + nl_k
 __host__ __device__ constexpr long packed_features(int d) { return 1L + d + (long)d * (d + 1) / 2; }
 
 // Block pair p (tb-major) -> (rb, tb); p beyond the real pairs -> (-1, -1).
-__host__ __device__ inline void pair_of(int d, int p, int& rb, int& tb) {
+__host__ __device__ constexpr void pair_of(int d, int p, int& rb, int& tb) {
   if (p >= n_pairs(d)) {
     rb = -1;
     tb = -1;
@@ -55,10 +55,10 @@ __host__ __device__ inline void pair_of(int d, int p, int& rb, int& tb) {
 // Feature at position k of K-block kb.  Returns false for padding.  On
 // success r is the first dimension, t the second (t == d for a linear
 // feature) and mult the query-side multiplicity (1 or 2).
-__host__ __device__ inline bool kfeature(int d, int kb, int k, int& r, int& t, int& mult) {
+__host__ __device__ constexpr bool kfeature(int d, int kb, int k, int& r, int& t, int& mult) {
   if (kb < nq_kblocks(d)) {
     const int lg = k / 8;
-    int rb, tb;
+    int rb = 0, tb = 0;
     pair_of(d, 2 * kb + lg / 2, rb, tb);
     if (rb < 0) return false;
     r = 4 * rb + 2 * (lg % 2) + (k % 8) / 4;
@@ -85,6 +85,25 @@ __host__ __device__ inline long abi_index(int d, int r, int t) {
   }
   const long before = (long)r * d - (long)r * (r - 1) / 2;
   return 1 + d + before + (t - r);
+}
+
+// Compile-time table of kfeature over all K-block positions:
+// r | t << 7 | mult << 14, or kPadFeature for padding.
+constexpr unsigned short kPadFeature = 0xffff;
+template <int D>
+struct KPosTable {
+  unsigned short e[n_kblocks(D) * 32];
+};
+template <int D>
+constexpr KPosTable<D> make_kpos_table() {
+  KPosTable<D> tab{};
+  for (int kb = 0; kb < n_kblocks(D); ++kb)
+    for (int k = 0; k < 32; ++k) {
+      int r = 0, t = 0, m = 0;
+      tab.e[kb * 32 + k] =
+          kfeature(D, kb, k, r, t, m) ? (unsigned short)(r | (t << 7) | (m << 14)) : kPadFeature;
+    }
+  return tab;
 }
 
 // Accumulator row rho (0..15) of scan M-tile m (0, 1) -> K-block position.

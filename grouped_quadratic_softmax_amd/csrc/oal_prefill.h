@@ -546,15 +546,8 @@ __global__ __launch_bounds__(512) void scan_kernel(const T* __restrict__ k, cons
   }
 }
 
-// --------------------------------------------------------------------------
-// kernel 2: per-head coefficient tables (once per call)
-// --------------------------------------------------------------------------
-
-// Per query head: the polynomial table [a, b_g / sqrt(d), sym(c)_gh / d]
-// (NPC floats), the exponent c_h with 2^c_h >= every feature coefficient
-// (kBadHead when a group id is out of range), and the feature coefficients
-// of the K-blocked layout divided by 2^c_h, with multiplicity two for the
-// off-diagonal pairs ([KB][32] elements).
+// Value of a bad head's coefficient exponent (a group id out of range): the
+// readout writes NaN for every output of that head.
 constexpr int kBadHead = 1 << 20;
 
 template <int NG>
@@ -562,68 +555,12 @@ __host__ __device__ constexpr int npc() {
   return 1 + NG + NG * NG;
 }
 
-template <typename T, int DH, int NG>
-__global__ __launch_bounds__(256) void coef_kernel(const int32_t* __restrict__ group_of_dim,
-                                                   const float* __restrict__ ca, const float* __restrict__ cb,
-                                                   const float* __restrict__ cc, int G,
-                                                   typename Cx<T>::E* __restrict__ cft, float* __restrict__ cpc,
-                                                   int* __restrict__ cex) {
-  typedef typename Cx<T>::E E;
-  constexpr int KB = n_kblocks(DH);
-  constexpr int NPC = npc<NG>();
-  __shared__ int gm[DH];
-  __shared__ float pc[NPC];
-  __shared__ int bad, ce;
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const float inv_sqrt_d = 1.f / sqrtf((float)DH);
-  if (tid == 0) bad = 0;
-  __syncthreads();
-  for (int r = tid; r < DH; r += blockDim.x) {
-    const int g = group_of_dim[h * DH + r];
-    gm[r] = g;
-    if (g < 0 || g >= G) atomicOr(&bad, 1);
-  }
-  for (int i2 = tid; i2 < NPC; i2 += blockDim.x) {
-    float val = 0.f;
-    if (i2 == 0) {
-      val = ca[h];
-    } else if (i2 <= NG) {
-      const int g = i2 - 1;
-      val = g < G ? cb[h * G + g] * inv_sqrt_d : 0.f;
-    } else {
-      const int gh = i2 - 1 - NG, g = gh / NG, g2 = gh % NG;
-      val = (g < G && g2 < G) ? 0.5f * (cc[(h * G + g) * G + g2] + cc[(h * G + g2) * G + g]) / DH : 0.f;
-    }
-    pc[i2] = val;
-    cpc[(long)h * NPC + i2] = val;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float mx = 0.f;
-    for (int g = 0; g < NG; ++g) {
-      mx = fmaxf(mx, fabsf(pc[1 + g]));
-      for (int g2 = 0; g2 < NG; ++g2) mx = fmaxf(mx, 2.f * fabsf(pc[1 + NG + g * NG + g2]));
-    }
-    const int e = exp_above(mx);
-    ce = e == kNegExp ? 0 : e;
-    cex[h] = bad ? kBadHead : ce;
-  }
-  __syncthreads();
-  const float sc = pow2(-ce);
-  for (int idx = tid; idx < KB * 32; idx += blockDim.x) {
-    const int kk = idx / 32, pos = idx % 32;
-    float val = 0.f;
-    int r, t, mu;
-    if (!bad && kfeature(DH, kk, pos, r, t, mu)) {
-      if (t == DH) val = pc[1 + gm[r]];
-      else val = (float)mu * pc[1 + NG + gm[r] * NG + gm[t]];
-    }
-    cft[(long)h * KB * 32 + idx] = (E)(val * sc);
-  }
-}
+// Feature position -> (r, t, multiplicity) of the K-blocked layout.
+template <int DH>
+__device__ constexpr KPosTable<DH> kpos_dev = make_kpos_table<DH>();
 
 // --------------------------------------------------------------------------
-// kernel 3: chunk readout + intra-chunk block + normalisation
+// kernel 2: chunk readout + intra-chunk block + normalisation
 // --------------------------------------------------------------------------
 
 // Readout CTAs have NW = 4 or 8 waves: wave w owns rows 16 (w % 4) .. of the
@@ -654,7 +591,7 @@ __host__ __device__ inline ReadoutLds readout_lds(int RG) {
 template <typename T, int DH, int RMAX, int NG, bool PREMAP, int NW>
 __global__ __launch_bounds__(64 * NW) void readout_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const typename Cx<T>::E* __restrict__ cft, const float* __restrict__ cpc, const int* __restrict__ cex,
+    const float* __restrict__ ca, const float* __restrict__ cb, const float* __restrict__ cc, int G,
     const float* __restrict__ gamma_q, const float* __restrict__ beta_q, const float* __restrict__ gamma_k,
     const float* __restrict__ beta_k, float ln_eps, const int32_t* __restrict__ group_of_dim,
     const typename Cx<T>::E* __restrict__ snap, const int* __restrict__ sexp, const float* __restrict__ sconst,
@@ -802,22 +739,53 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
     constexpr int nh = RMAX;         // head slots per pass
     const int nreal = min(RMAX, R - h0);  // slots beyond are dead: zero features, no output
     __syncthreads();  // previous head group done with qh / coef / bst
-    // ---- per-head tables (precomputed) ----
-    {
-      constexpr int VEC = 16 / sizeof(E);
-      const int nv = nh * KB * 32 / VEC, nvr = nreal * KB * 32 / VEC;
-      const uint4* src = reinterpret_cast<const uint4*>(cft + (long)(kvh * R + h0) * KB * 32);
-      for (int i = tid; i < nv; i += NT) reinterpret_cast<uint4*>(coef)[i] = i < nvr ? src[i] : make_uint4(0, 0, 0, 0);
-    }
+    // ---- per-head tables: polynomial [a, b_g / sqrt(d), sym(c)_gh / d],
+    // exponent c_h with 2^c_h above every feature coefficient (kBadHead for
+    // a group id out of range), feature coefficients / 2^c_h ----
     for (int idx = tid; idx < nh * DH; idx += NT) {
       const int hh = idx / DH, r = idx % DH;
       gm[hh][r] = hh < nreal ? group_of_dim[(kvh * R + h0 + hh) * DH + r] : 0;
     }
     for (int idx = tid; idx < nh * NPC; idx += NT) {
-      const int hh = idx / NPC, i2 = idx % NPC;
-      pc[hh][i2] = hh < nreal ? cpc[(long)(kvh * R + h0 + hh) * NPC + i2] : 0.f;
+      const int hh = idx / NPC, i2 = idx % NPC, h = kvh * R + h0 + hh;
+      float val = 0.f;
+      if (hh < nreal) {
+        if (i2 == 0) {
+          val = ca[h];
+        } else if (i2 <= NG) {
+          const int g = i2 - 1;
+          val = g < G ? cb[h * G + g] * (1.f / sqrtf((float)DH)) : 0.f;
+        } else {
+          const int gh = i2 - 1 - NG, g = gh / NG, g2 = gh % NG;
+          val = (g < G && g2 < G) ? 0.5f * (cc[(h * G + g) * G + g2] + cc[(h * G + g2) * G + g]) / DH : 0.f;
+        }
+      }
+      pc[hh][i2] = val;
     }
-    if (tid < nh) cexp[tid] = tid < nreal ? cex[kvh * R + h0 + tid] : 0;
+    __syncthreads();
+    if (wave < nh) {  // one wave per head slot
+      const bool bad = lane < DH && (unsigned)gm[wave][lane] >= (unsigned)G;
+      float mx = 0.f;
+      for (int i2 = 1 + lane; i2 < NPC; i2 += kWave) mx = fmaxf(mx, (i2 <= NG ? 1.f : 2.f) * fabsf(pc[wave][i2]));
+      mx = wave_max(mx);
+      const bool anybad = __ballot(bad) != 0;
+      if (lane == 0) {
+        const int e = exp_above(mx);
+        cexp[wave] = wave >= nreal ? 0 : anybad ? kBadHead : e == kNegExp ? 0 : e;
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nh * KB * 32; idx += NT) {
+      const int hh = idx / (KB * 32);
+      const unsigned short fe = kpos_dev<DH>.e[idx % (KB * 32)];
+      const int ce = cexp[hh];
+      float val = 0.f;
+      if (fe != kPadFeature && ce != kBadHead) {
+        const int r = fe & 127, t = (fe >> 7) & 127, gr = gm[hh][r];
+        val = t == DH ? pc[hh][1 + gr] : (float)(fe >> 14) * pc[hh][1 + NG + gr * NG + gm[hh][t]];
+      }
+      coef[idx] = (E)(val * pow2(-ce));
+    }
     // ---- stage q rows of the head group (pre-map, row exponent) ----
 #pragma unroll 1
     for (int it0 = 0; it0 < nh; it0 += NT / (4 * C)) {
@@ -1184,10 +1152,8 @@ namespace {
 
 template <typename T, int DH>
 struct FwdWs {
-  long snap_bytes, exp_off, const_off, cft_off, cpc_off, cex_off, total;
+  long snap_bytes, exp_off, const_off, total;
 };
-
-constexpr int kNpcMax = 1 + 8 + 64;
 
 template <typename T, int DH>
 FwdWs<T, DH> fwd_ws(int B, int Hq, int Hkv, int N) {
@@ -1200,10 +1166,7 @@ FwdWs<T, DH> fwd_ws(int B, int Hq, int Hkv, int N) {
   w.snap_bytes = snaps * KB * NCOL * 32 * (long)sizeof(E);
   w.exp_off = up(w.snap_bytes);
   w.const_off = w.exp_off + up(snaps * (KB + 2) * 4);
-  w.cft_off = w.const_off + up(snaps * NCOL * 4);
-  w.cpc_off = w.cft_off + up((long)Hq * KB * 32 * sizeof(E));
-  w.cex_off = w.cpc_off + up((long)Hq * kNpcMax * 4);
-  w.total = w.cex_off + up((long)Hq * 4);
+  w.total = w.const_off + up(snaps * NCOL * 4);
   return w;
 }
 
@@ -1230,9 +1193,6 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   E* snap = reinterpret_cast<E*>(ws);
   int* sexp = reinterpret_cast<int*>(ws + w.exp_off);
   float* sconst = reinterpret_cast<float*>(ws + w.const_off);
-  E* cft = reinterpret_cast<E*>(ws + w.cft_off);
-  float* cpc = reinterpret_cast<float*>(ws + w.cpc_off);
-  int* cex = reinterpret_cast<int*>(ws + w.cex_off);
   const T* qq = reinterpret_cast<const T*>(a.q);
   const T* kk = reinterpret_cast<const T*>(a.k);
   const T* vv = reinterpret_cast<const T*>(a.v);
@@ -1256,16 +1216,12 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   const int has_in = a.state_in != nullptr;
 #define OAL_OUT(RM, NGV, PM)                                                                                    \
   do {                                                                                                          \
-    hipLaunchKernelGGL((coef_kernel<T, DH, NGV>), dim3(a.Hq), dim3(256), 0, stream, a.group_of_dim, a.ca, a.cb, \
-                       a.cc, a.G, cft, cpc, cex);                                                               \
-    hipError_t e1 = hipGetLastError();                                                                          \
-    if (e1 != hipSuccess) return e1;                                                                            \
     constexpr int NWV = (RM % 2 == 0 && RM <= 4) ? 8 : 4;                                                                         \
     auto fn = readout_kernel<T, DH, RM, NGV, PM, NWV>;                                                          \
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),                                      \
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);                  \
     if (e2 != hipSuccess) return e2;                                                                            \
-    hipLaunchKernelGGL(fn, grid, dim3(64 * NWV), shm, stream, qq, kk, vv, cft, cpc, cex, a.gamma_q,             \
+    hipLaunchKernelGGL(fn, grid, dim3(64 * NWV), shm, stream, qq, kk, vv, a.ca, a.cb, a.cc, a.G, a.gamma_q,             \
                        a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, a.group_of_dim, snap, sexp, sconst, has_in, yy, \
                        a.Hq, a.Hkv, a.N, nchunks, rg);                                                          \
   } while (0)
