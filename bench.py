@@ -234,7 +234,7 @@ def run_pmc_target(args):
     """Launch only one kernel repeatedly, for rocprofv3 counter passes.
 
     ``readout``: the chunk readout of the main workload (after one states
-    pass); ``copy``: a plain device copy of 1 GiB (fp32), whose FETCH_SIZE and
+    pass); ``states``: the chunk scan of the main workload; ``copy``: a plain device copy of 1 GiB (fp32), whose FETCH_SIZE and
     WRITE_SIZE readings calibrate the counters against a known byte count."""
     import torch
     import grouped_quadratic_softmax_amd as oal
@@ -258,9 +258,12 @@ def run_pmc_target(args):
     pre.states()
     torch.cuda.synchronize()
     for _ in range(args.steps):
-        pre.outputs()
+        if args.pmc_target == "readout":
+            pre.outputs()
+        else:
+            pre.states()
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_target": "readout", "launches": args.steps}), flush=True)
+    print(json.dumps({"pmc_target": args.pmc_target, "launches": args.steps}), flush=True)
 
 
 def cpu_baseline(wl, min_seconds=10.0):
@@ -305,7 +308,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--pmc-target", choices=("readout", "copy"), default=None,
+    ap.add_argument("--pmc-target", choices=("readout", "states", "copy"), default=None,
                     help="only launch this kernel --steps times (for rocprofv3 counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

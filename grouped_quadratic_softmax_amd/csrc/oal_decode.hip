@@ -216,8 +216,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     if (hh >= R) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[rg][hh][4 * c4 + e] = acc[hh][e];
-    float dsum = dacc[hh];
-    for (int off = 32; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off);
+    const float dsum = wave_sum(dacc[hh]);
     if (tid % kWave == 0) dred[hh][tid / kWave] = dsum;
   }
   __syncthreads();

@@ -115,11 +115,55 @@ __device__ __forceinline__ void store4(float* p, const f32x4& x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
-// LayerNorm + affine of one row held by `n` consecutive lanes of a wave
-// (each lane holds `per` elements).  Used for the ReBased pre-map.
-__device__ __forceinline__ float wave_sum_width(float x, int width) {
-  for (int off = width / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, width);
-  return x;
+// ---- cross-lane reductions on DPP (no LDS round trip) ----
+// DPP control codes: quad_perm patterns and shifts within a row of 16 lanes.
+constexpr int kDppXor1 = 0xb1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppShr1 = 0x111;  // row_shr:1
+constexpr int kDppShr2 = 0x112;
+constexpr int kDppShr4 = 0x114;
+constexpr int kDppShr8 = 0x118;
+
+// x of the lane selected by CTRL; a lane whose source lies outside its row
+// receives `fill`.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                               __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+// sum / max over aligned groups of 4 lanes, in every lane of the group
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp<kDppXor1>(x, 0.f);
+  return x + dpp<kDppXor2>(x, 0.f);
+}
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x, x));
+  return fmaxf(x, dpp<kDppXor2>(x, x));
+}
+// sum / max over each row of 16 lanes, valid in the row's last lane
+__device__ __forceinline__ float row_sum_last(float x) {
+  x += dpp<kDppShr1>(x, 0.f);
+  x += dpp<kDppShr2>(x, 0.f);
+  x += dpp<kDppShr4>(x, 0.f);
+  return x + dpp<kDppShr8>(x, 0.f);
+}
+__device__ __forceinline__ float row_max_last(float x) {
+  x = fmaxf(x, dpp<kDppShr1>(x, x));
+  x = fmaxf(x, dpp<kDppShr2>(x, x));
+  x = fmaxf(x, dpp<kDppShr4>(x, x));
+  return fmaxf(x, dpp<kDppShr8>(x, x));
+}
+// over the whole wave, returned (uniform) in every lane
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum_last(x);
+  return (lane_value(x, 15) + lane_value(x, 31)) + (lane_value(x, 47) + lane_value(x, 63));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max_last(x);
+  return fmaxf(fmaxf(lane_value(x, 15), lane_value(x, 31)), fmaxf(lane_value(x, 47), lane_value(x, 63)));
 }
 
 }  // namespace oal

@@ -137,11 +137,6 @@ __device__ __forceinline__ int exp_above(float m) {
 }
 __device__ __forceinline__ float pow2(int e) { return ldexpf(1.f, e); }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
 
 // n consecutive activations (n a multiple of 4) starting at p -> floats
 template <int n>
@@ -182,8 +177,7 @@ __device__ __forceinline__ void premap4(float* x, int d0, const float* __restric
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < n; ++i) s += x[i];
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
+  s = quad_sum(s);
   const float mu = s * (1.f / DH);
   float v2 = 0.f;
 #pragma unroll
@@ -191,8 +185,7 @@ __device__ __forceinline__ void premap4(float* x, int d0, const float* __restric
     const float t = x[i] - mu;
     v2 += t * t;
   }
-  v2 += __shfl_xor(v2, 1);
-  v2 += __shfl_xor(v2, 2);
+  v2 = quad_sum(v2);
   const float inv = 1.f / sqrtf(v2 * (1.f / DH) + eps);
 #pragma unroll
   for (int i = 0; i < n; ++i) x[i] = gamma[d0 + i] * (x[i] - mu) * inv + beta[d0 + i];
@@ -204,109 +197,115 @@ __device__ __forceinline__ void premap4(float* x, int d0, const float* __restric
 // kernel 1: chunk scan (state update + snapshots)
 // --------------------------------------------------------------------------
 
-constexpr int kScanWaves = 8;  // waves per scan CTA, one K-block each
+// One CTA per (eight K-blocks, batch x KV head), twelve waves in two roles:
+//  * compute waves 0..7: wave w keeps K-block 8 blockIdx.x + w of S in fp32
+//    MFMA accumulators (the wave after the last K-block keeps the constant
+//    feature's row [sum v, n]); per chunk it writes the snapshot S_c and adds
+//    phi_k(K_c)^T [V_c | 1].  They issue only stores to global memory.
+//  * loader waves 8..11: lane = token, each holding 16 or 32 dimensions of
+//    the keys (waves 8, 9) or values (10, 11); they load chunks ahead, reduce
+//    the chunk maxima that set the scaling exponents, apply the pre-map, and
+//    write the scaled tiles transposed into LDS (double-buffered).  They issue
+//    only loads, so their waits never cover the snapshot stores.
+// One barrier per chunk separates staging chunk c+1 from reading chunk c.
+constexpr int kScanCompute = 8;
+constexpr int kScanLoad = 4;
+constexpr int kScanWaves = kScanCompute + kScanLoad;
 
-// Raw activation vector of four elements.
+// Eight consecutive activations of one row, as loaded.
 template <typename T>
-struct Raw4;
+struct Raw8;
 template <>
-struct Raw4<uint16_t> {
-  typedef uint2 type;
+struct Raw8<uint16_t> {
+  uint4 w;
 };
 template <>
-struct Raw4<float> {
-  typedef float4 type;
+struct Raw8<float> {
+  float4 a, b;
 };
-__device__ __forceinline__ void unpack4(const uint2& w, float* out) {
-  out[0] = __uint_as_float(w.x << 16);
-  out[1] = __uint_as_float(w.x & 0xffff0000u);
-  out[2] = __uint_as_float(w.y << 16);
-  out[3] = __uint_as_float(w.y & 0xffff0000u);
+__device__ __forceinline__ void ld8(Raw8<uint16_t>& r, const uint16_t* p) { r.w = *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void ld8(Raw8<float>& r, const float* p) {
+  r.a = reinterpret_cast<const float4*>(p)[0];
+  r.b = reinterpret_cast<const float4*>(p)[1];
 }
-__device__ __forceinline__ void unpack4(const float4& w, float* out) {
-  out[0] = w.x;
-  out[1] = w.y;
-  out[2] = w.z;
-  out[3] = w.w;
+__device__ __forceinline__ void zero8(Raw8<uint16_t>& r) { r.w = make_uint4(0u, 0u, 0u, 0u); }
+__device__ __forceinline__ void zero8(Raw8<float>& r) {
+  r.a = make_float4(0.f, 0.f, 0.f, 0.f);
+  r.b = r.a;
 }
-template <typename T>
-__device__ __forceinline__ typename Raw4<T>::type zero_raw4();
-template <>
-__device__ __forceinline__ uint2 zero_raw4<uint16_t>() {
-  return make_uint2(0u, 0u);
+__device__ __forceinline__ void unpack8(const Raw8<uint16_t>& r, float (&x)[8]) {
+  const uint32_t ws[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __uint_as_float(ws[j] << 16);
+    x[2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
+  }
 }
-template <>
-__device__ __forceinline__ float4 zero_raw4<float>() {
-  return make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// LayerNorm + affine of a row whose 4-element parts sit in `nl` consecutive
-// lanes (ReBased pre-map, biased variance).
-template <int DH, int nl>
-__device__ __forceinline__ void premap_lanes(float (&x)[4], int d0, const float* __restrict__ gamma,
-                                             const float* __restrict__ beta, float eps) {
-  float s = x[0] + x[1] + x[2] + x[3];
-#pragma unroll
-  for (int o = 1; o < nl; o <<= 1) s += __shfl_xor(s, o);
-  const float mu = s * (1.f / DH);
-  float v2 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v2 += (x[i] - mu) * (x[i] - mu);
-#pragma unroll
-  for (int o = 1; o < nl; o <<= 1) v2 += __shfl_xor(v2, o);
-  const float inv = 1.f / sqrtf(v2 * (1.f / DH) + eps);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = gamma[d0 + i] * (x[i] - mu) * inv + beta[d0 + i];
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float (&x)[8]) {
+  x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+  x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
 }
 
 template <typename T, int DH, bool PREMAP>
-__global__ __launch_bounds__(512) void scan_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                   const float* __restrict__ gamma_k,
-                                                   const float* __restrict__ beta_k, float ln_eps,
-                                                   const float* __restrict__ state_in,
-                                                   float* __restrict__ state_out,
-                                                   typename Cx<T>::E* __restrict__ snap, int* __restrict__ sexp,
-                                                   float* __restrict__ sconst, int Hkv, int N, int nchunks) {
+__global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gamma_k,
+    const float* __restrict__ beta_k, float ln_eps, const float* __restrict__ state_in,
+    float* __restrict__ state_out, typename Cx<T>::E* __restrict__ snap, int* __restrict__ sexp,
+    float* __restrict__ sconst, int Hkv, int N, int nchunks) {
   typedef typename Cx<T>::E E;
   typedef typename Cx<T>::Frag F;
-  typedef typename Raw4<T>::type RV;
   constexpr int KB = n_kblocks(DH);
   constexpr int NQ = nq_kblocks(DH);
   constexpr long D = packed_features(DH);
   constexpr long SF = D * NCOL;
-  constexpr int KP = C + 8;                 // row pitch of kT / vT (elements)
-  constexpr int ONE = DH, ZERO = DH + 1;
-  constexpr int NT = 64 * kScanWaves;       // threads
-  constexpr int RQ = DH / 4;                // 4-element parts per key row
-  constexpr int KT = (C * RQ + NT - 1) / NT;  // key parts per thread
-  constexpr int VT = C * 16 / NT;           // value parts per thread
-  __shared__ __align__(16) E kT[(DH + 2) * KP];  // scaled keys, transposed; row DH = ones, DH+1 = zeros
-  __shared__ __align__(16) E vT[DV * KP];        // scaled values, transposed
-  __shared__ float wmx[3][kScanWaves];
+  constexpr int KP = C + 8;                // row pitch of the transposed tiles (elements)
+  constexpr int ONE = DH, ZERO = DH + 1;   // rows of ones / zeros after the key rows
+  constexpr int VROW = DH + 2;             // first value row
+  constexpr int BUF = (DH + 2 + DV) * KP;  // elements per staging buffer
+  constexpr int KUL = DH / 16;             // key units (8 dimensions) per loader lane
+  constexpr int UL = DV / 16;              // value units per loader lane (>= KUL)
+  constexpr int NR = IsBf16<T>::value ? 3 : 2;  // chunks held in loader registers
+  __shared__ __align__(16) E tile[2][BUF];
+  __shared__ float wmx[2][kScanLoad];      // [slot][loader wave]: max |k| (waves 0, 1), |v| (2, 3)
+  __shared__ float wm_in[kScanCompute];
+  __shared__ __align__(16) float gb[2][DH];  // pre-map gamma, beta of the KV head
 
   const int bh = blockIdx.y, BH = gridDim.y;
   const int kvh = bh % Hkv;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int lg = lane / 16, l16 = lane % 16;
-  const int kb = blockIdx.x * kScanWaves + wave;
-  const bool active = kb < KB;
-  const int nu = kb < NQ ? 2 : 1;  // key-exponent multiplicity of this K-block's features
-  const bool lead = blockIdx.x == 0;
+  const bool loader = wave >= kScanCompute;
+  // compute role
+  const int kb = blockIdx.x * kScanCompute + wave;
+  const bool active = !loader && kb < KB;  // a K-block of S
+  const bool cwave = !loader && kb == KB;  // the constant feature's row
+  const int nu = kb < NQ ? 2 : (kb < KB ? 1 : 0);  // key-exponent multiplicity of the wave's features
+  const bool lead = blockIdx.x == 0 && tid == 0;
+  // loader role: token ltok, units lhalf + 2 i (dimensions 8 unit ..)
+  const int lw = wave - kScanCompute;
+  const bool kload = loader && lw < 2;
+  const int ltok = 32 * (lw & 1) + (lane & 31);
+  const int lhalf = lane >> 5;
 
-  // A operand (phi_k) rows of this lane: feature of accumulator row l16
+  if (PREMAP)
+    for (int i = tid; i < 2 * DH; i += blockDim.x) gb[i / DH][i % DH] = (i < DH ? gamma_k : beta_k)[kvh * DH + i % DH];
+
+  // A operand (phi_k) rows of this lane: the features of accumulator row l16
   int ar[2], at[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    int r, t, mu;
+    int r = 0, t = 0, mu = 0;
     if (active && kfeature(DH, kb, acc_position(m, l16), r, t, mu)) {
       ar[m] = r;
       at[m] = t;
+    } else if (cwave && m == 0 && l16 == 0) {
+      ar[m] = ONE;
+      at[m] = ONE;
     } else {
       ar[m] = ZERO;
       at[m] = ZERO;
     }
   }
-
   f32x4 acc[2][5];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -314,212 +313,267 @@ __global__ __launch_bounds__(512) void scan_kernel(const T* __restrict__ k, cons
     for (int n = 0; n < 5; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const long sbase = (long)bh * SF;
-  // constant-feature row [sum v, n] (raw units), kept by the lead CTA
-  float csum = 0.f;
-  if (lead && tid < NCOL && state_in != nullptr) csum = tid < DV ? state_in[sbase + tid] : state_in[sbase + D * DV];
-
   const T* kp = k + (long)bh * N * DH;
   const T* vp = v + (long)bh * N * DV;
-  RV kr[KT], vr[VT];
+
+  // ---- loader helpers ----
+  struct RawSet {
+    Raw8<T> u[UL];
+    float mu, inv;  // pre-map statistics of the token (keys)
+  };
   auto fetch = [&](int c) __attribute__((always_inline)) {
-    const int j0 = c * C, nval = min(C, N - j0);
+    RawSet r;
+    const int row = c * C + ltok;
+    const long rr = row < N ? row : N - 1;
 #pragma unroll
-    for (int i = 0; i < KT; ++i) {
-      const int id = tid + NT * i, row = id / RQ, part = id % RQ;
-      kr[i] = (id < C * RQ && row < nval) ? *reinterpret_cast<const RV*>(kp + (long)(j0 + row) * DH + 4 * part)
-                                          : zero_raw4<T>();
+    for (int i = 0; i < UL; ++i) {
+      const int unit = lhalf + 2 * i;
+      if (kload ? i < KUL : true) {
+        ld8(r.u[i], kload ? kp + rr * DH + 8 * unit : vp + rr * DV + 8 * unit);
+        if (row >= N) zero8(r.u[i]);
+      } else {
+        zero8(r.u[i]);
+      }
     }
+    r.mu = 0.f;
+    r.inv = 0.f;
+    return r;
+  };
+  // values of unit i with the pre-map applied (keys)
+  auto values = [&](const RawSet& r, int i, float (&x)[8]) __attribute__((always_inline)) {
+    unpack8(r.u[i], x);
+    if (PREMAP && kload) {
+      const int d0 = 8 * (lhalf + 2 * i);
 #pragma unroll
-    for (int i = 0; i < VT; ++i) {
-      const int id = tid + NT * i, row = id / 16, part = id % 16;
-      vr[i] = row < nval ? *reinterpret_cast<const RV*>(vp + (long)(j0 + row) * DV + 4 * part) : zero_raw4<T>();
+      for (int e = 0; e < 8; ++e) x[e] = gb[0][d0 + e] * (x[e] - r.mu) * r.inv + gb[1][d0 + e];
     }
   };
-  fetch(0);
+  // pre-map statistics and this wave's maximum into wmx[slot]
+  auto convert = [&](RawSet& r, int c, int slot) __attribute__((always_inline)) {
+    const bool valid = c * C + ltok < N;
+    if (PREMAP && kload) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < KUL; ++i) {
+        float x[8];
+        unpack8(r.u[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += x[e];
+      }
+      s += __shfl_xor(s, 32);
+      const float mu = s * (1.f / DH);
+      float q2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < KUL; ++i) {
+        float x[8];
+        unpack8(r.u[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q2 += (x[e] - mu) * (x[e] - mu);
+      }
+      q2 += __shfl_xor(q2, 32);
+      r.mu = mu;
+      r.inv = valid ? 1.f / sqrtf(q2 * (1.f / DH) + ln_eps) : 0.f;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < UL; ++i) {
+      if (kload && i >= KUL) continue;
+      float x[8];
+      values(r, i, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, valid ? fabsf(x[e]) : 0.f);
+    }
+    m = wave_max(m);
+    if (lane == 0) wmx[slot][lw] = m;
+  };
+  // scaled chunk -> staging buffer: k / 2^ekx, v / 2^evx, transposed
+  auto stage = [&](const RawSet& r, int c, int buf, int ekx, int evx) __attribute__((always_inline)) {
+    E* tb = tile[buf];
+    const bool valid = c * C + ltok < N;
+    const float sc = pow2(kload ? -ekx : -evx);
+#pragma unroll
+    for (int i = 0; i < UL; ++i) {
+      if (kload && i >= KUL) continue;
+      float x[8];
+      values(r, i, x);
+      const int r0 = (kload ? 0 : VROW) + 8 * (lhalf + 2 * i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tb[(r0 + e) * KP + ltok] = valid ? (E)(x[e] * sc) : (E)0.f;
+    }
+    if (kload) tb[(lhalf ? ZERO : ONE) * KP + ltok] = (!lhalf && valid) ? (E)1.f : (E)0.f;
+  };
+  auto chunk_exps = [&](int slot, int& ek, int& ev) __attribute__((always_inline)) {
+    ek = exp_above(fmaxf(wmx[slot][0], wmx[slot][1]));
+    ev = exp_above(fmaxf(wmx[slot][2], wmx[slot][3]));
+  };
 
+  // ---- prologue: chunk 0 staged, maxima of chunk 1 reduced ----
+  RawSet R[NR];
+  if (loader) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (i < nchunks) R[i] = fetch(i);
+    convert(R[0], 0, 0);
+  }
+  __syncthreads();
   int Ek = 0, Ev = 0, beta = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    const int j0 = c * C;
-    const int nvalid = min(C, N - j0);
-    float kx[KT][4], vx[VT][4];
-#pragma unroll
-    for (int i = 0; i < KT; ++i) unpack4(kr[i], kx[i]);
-#pragma unroll
-    for (int i = 0; i < VT; ++i) unpack4(vr[i], vx[i]);
-    if (c + 1 < nchunks) fetch(c + 1);  // in flight during this chunk
-    if (PREMAP) {
-#pragma unroll
-      for (int i = 0; i < KT; ++i) {
-        const int id = tid + NT * i, row = id / RQ, part = id % RQ;
-        premap_lanes<DH, RQ>(kx[i], 4 * part, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
-        if (row >= nvalid || id >= C * RQ) kx[i][0] = kx[i][1] = kx[i][2] = kx[i][3] = 0.f;
-      }
-    }
-    float mk = 0.f, mv = 0.f;
-#pragma unroll
-    for (int i = 0; i < KT; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mk = fmaxf(mk, fabsf(kx[i][e]));
-#pragma unroll
-    for (int i = 0; i < VT; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mv = fmaxf(mv, fabsf(vx[i][e]));
-    mk = wave_max(mk);
-    mv = wave_max(mv);
-    if (lane == 0) {
-      wmx[0][wave] = mk;
-      wmx[1][wave] = mv;
-    }
-    __syncthreads();  // (A): also ends every read of kT / vT of the previous chunk
-    float mk_all = 0.f, mv_all = 0.f;
-#pragma unroll
-    for (int w = 0; w < kScanWaves; ++w) {
-      mk_all = fmaxf(mk_all, wmx[0][w]);
-      mv_all = fmaxf(mv_all, wmx[1][w]);
-    }
-    const int ek = exp_above(mk_all), ev = exp_above(mv_all);
-    if (c == 0) {
-      Ek = ek == kNegExp ? 0 : ek;
-      Ev = ev == kNegExp ? 0 : ev;
-      // initial state in units 2^(nu Ek + Ev) (2^(nu Ek) for z); the fixed
-      // snapshot exponent beta bounds every later entry: |acc| <= N + M_in
-      float m_in = 0.f;
-      if (active && state_in != nullptr) {
-        const float sh = pow2(-(nu * Ek + Ev)), sz = pow2(-nu * Ek);
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            int r, t, mu;
-            if (!kfeature(DH, kb, acc_position(m, 4 * lg + e), r, t, mu)) continue;
-            const long f = abi_index(DH, r, t);
-#pragma unroll
-            for (int n = 0; n < 4; ++n) acc[m][n][e] = state_in[sbase + f * DV + 16 * n + l16] * sh;
-            if (l16 == 0) acc[m][4][e] = state_in[sbase + D * DV + f] * sz;
-          }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int n = 0; n < 5; ++n)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m_in = fmaxf(m_in, fabsf(acc[m][n][e]));
-      }
-      m_in = wave_max(m_in);
-      if (lane == 0) wmx[2][wave] = m_in;
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < kScanWaves; ++w) m_in = fmaxf(m_in, wmx[2][w]);
-      beta = exp_above((float)N + m_in) - 15;
-      const float sb = pow2(-beta);
+  {
+    int ek, ev;
+    chunk_exps(0, ek, ev);
+    Ek = ek == kNegExp ? 0 : ek;
+    Ev = ev == kNegExp ? 0 : ev;
+    // initial state in units 2^(nu Ek + Ev) (2^(nu Ek) for z); the fixed
+    // snapshot exponent beta bounds every later entry: |acc| <= N + M_in
+    float m_in = 0.f;
+    if (state_in != nullptr && (active || cwave)) {
+      const float sh = pow2(-(nu * Ek + Ev)), sz = pow2(-nu * Ek);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int n = 0; n < 5; ++n) acc[m][n] *= sb;
-    } else if (ek > Ek || ev > Ev) {
-      const int dk = max(ek - Ek, 0), dv = max(ev - Ev, 0);
-      Ek += dk;
-      Ev += dv;
-      const float sh = pow2(-(nu * dk + dv)), sz = pow2(-nu * dk);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] *= sh;
-        acc[m][4] *= sz;
-      }
-    }
-
-    // ---- snapshot S_c: raw = stored * 2^(beta + nu Ek) (* 2^Ev for H) ----
-    const long sidx = (long)c * BH + bh;
-    if (active) {
-      E* sp = snap + (sidx * KB + kb) * NCOL * 32 + 8 * lg;
-#pragma unroll
-      for (int n = 0; n < 5; ++n) {
-        if (n == 4 && l16 != 0) continue;
-        float x[8];
-#pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[e] = acc[0][n][e];
-          x[4 + e] = acc[1][n][e];
-        }
-        frag_st(sp + (16 * n + l16) * 32, x);
-      }
-      if (lane == 0) sexp[sidx * (KB + 2) + kb] = beta;
-    }
-    if (lead && tid == 0) {
-      sexp[sidx * (KB + 2) + KB] = Ek;
-      sexp[sidx * (KB + 2) + KB + 1] = Ev;
-    }
-    if (lead && tid < NCOL) sconst[sidx * NCOL + tid] = csum;
-
-    // ---- scaled chunk -> LDS (transposed): k / 2^Ek, v / 2^(Ev + beta) ----
-    {
-      const float sk = pow2(-Ek), sv = pow2(-(Ev + beta));
-#pragma unroll
-      for (int i = 0; i < KT; ++i) {
-        const int id = tid + NT * i, row = id / RQ, part = id % RQ;
-        if (id < C * RQ)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kT[(4 * part + e) * KP + row] = (E)(kx[i][e] * sk);
-      }
-#pragma unroll
-      for (int i = 0; i < VT; ++i) {
-        const int id = tid + NT * i, row = id / 16, part = id % 16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vT[(4 * part + e) * KP + row] = (E)(vx[i][e] * sv);
-      }
-      if (tid < C) {
-        kT[ONE * KP + tid] = tid < nvalid ? (E)1.f : (E)0.f;
-        kT[ZERO * KP + tid] = (E)0.f;
-      }
-    }
-    __syncthreads();  // (B)
-    if (lead && tid < DV) {
-      // running sum of the values (exact: the fp16 copies hold the bf16 inputs)
-      float s = 0.f;
-      for (int j = 0; j < nvalid; ++j) s += (float)vT[tid * KP + j];
-      csum += s * pow2(Ev + beta);
-    } else if (lead && tid == DV) {
-      csum += (float)nvalid;
-    }
-
-    // ---- S += phi_k(K_c)^T [V_c | 1] ----
-    if (active) {
-      F ones;
-      if constexpr (IsBf16<T>::value) {
-        const _Float16 o = l16 == 0 ? (_Float16)pow2(-beta) : (_Float16)0.f;
-        ones.v = h8{o, o, o, o, o, o, o, o};
-      } else {
-        const float o = l16 == 0 ? pow2(-beta) : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ones.v[e] = o;
-      }
-#pragma unroll
-      for (int ks = 0; ks < C / 32; ++ks) {
-        const int jb = 32 * ks + 8 * lg;
-        F A[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          F a0, a1;
-          frag_ld(a0, &kT[ar[m] * KP + jb]);
-          frag_ld(a1, &kT[at[m] * KP + jb]);
-          if constexpr (IsBf16<T>::value) {
-            A[m].v = a0.v * a1.v;
+          long f;
+          int r = 0, t = 0, mu = 0;
+          if (active) {
+            if (!kfeature(DH, kb, acc_position(m, 4 * lg + e), r, t, mu)) continue;
+            f = abi_index(DH, r, t);
           } else {
+            if (m != 0 || lg != 0 || e != 0) continue;
+            f = 0;
+          }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) A[m].v[e] = a0.v[e] * a1.v[e];
+          for (int n = 0; n < 4; ++n) acc[m][n][e] = state_in[sbase + f * DV + 16 * n + l16] * sh;
+          if (l16 == 0) acc[m][4][e] = state_in[sbase + D * DV + f] * sz;
+        }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 5; ++n)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m_in = fmaxf(m_in, fabsf(acc[m][n][e]));
+    }
+    if (!loader) {
+      m_in = wave_max(m_in);
+      if (lane == 0) wm_in[wave] = m_in;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kScanCompute; ++w) m_in = fmaxf(m_in, wm_in[w]);
+    beta = exp_above((float)N + m_in) - 15;
+    const float sb = pow2(-beta);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 5; ++n) acc[m][n] *= sb;
+  }
+  if (loader) {
+    stage(R[0], 0, 0, Ek, Ev + beta);
+    if (nchunks > 1) convert(R[1], 1, 1);
+    if (NR < nchunks) R[0] = fetch(NR);
+  }
+  __syncthreads();
+
+  F ones;
+  if constexpr (IsBf16<T>::value) {
+    const _Float16 o = l16 == 0 ? (_Float16)pow2(-beta) : (_Float16)0.f;
+    ones.v = h8{o, o, o, o, o, o, o, o};
+  } else {
+    const float o = l16 == 0 ? pow2(-beta) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones.v[e] = o;
+  }
+
+  // Chunk c.  Loader registers: rs = chunk c+1 (staged now, then refilled
+  // with chunk c+1+NR), rc = chunk c+2 (maxima reduced now).
+  auto step = [&](int c, RawSet& rs, RawSet& rc) __attribute__((always_inline)) {
+    int Ek1 = Ek, Ev1 = Ev;  // exponents of chunk c+1
+    if (c + 1 < nchunks) {
+      int ek, ev;
+      chunk_exps((c + 1) & 1, ek, ev);
+      Ek1 = max(Ek, ek);
+      Ev1 = max(Ev, ev);
+    }
+    if (loader) {
+      if (c + 1 < nchunks) stage(rs, c + 1, (c + 1) & 1, Ek1, Ev1 + beta);
+      if (c + 2 < nchunks) convert(rc, c + 2, c & 1);
+      if (c + 1 + NR < nchunks) rs = fetch(c + 1 + NR);
+    } else {
+      // ---- snapshot S_c: raw = stored * 2^(beta + nu Ek) (* 2^Ev for H) ----
+      const long sidx = (long)c * BH + bh;
+      if (active) {
+        E* sp = snap + (sidx * KB + kb) * NCOL * 32 + 8 * lg;
+#pragma unroll
+        for (int n = 0; n < 5; ++n) {
+          if (n == 4 && l16 != 0) continue;
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = acc[0][n][e];
+            x[4 + e] = acc[1][n][e];
+          }
+          frag_st(sp + (16 * n + l16) * 32, x);
+        }
+        if (lane == 0) sexp[sidx * (KB + 2) + kb] = beta;
+      } else if (cwave && lg == 0) {
+        const float sh = pow2(Ev + beta);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) sconst[sidx * NCOL + 16 * n + l16] = acc[0][n][0] * sh;
+        if (l16 == 0) sconst[sidx * NCOL + DV] = acc[0][4][0] * pow2(beta);
+      }
+      if (lead) {
+        sexp[sidx * (KB + 2) + KB] = Ek;
+        sexp[sidx * (KB + 2) + KB + 1] = Ev;
+      }
+      // ---- S += phi_k(K_c)^T [V_c | 1] ----
+      if (active || cwave) {
+        const E* kT = tile[c & 1];
+        const E* vT = kT + VROW * KP;
+#pragma unroll
+        for (int ks = 0; ks < C / 32; ++ks) {
+          const int jb = 32 * ks + 8 * lg;
+          F A[2];
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            F a0, a1;
+            frag_ld(a0, &kT[ar[m] * KP + jb]);
+            frag_ld(a1, &kT[at[m] * KP + jb]);
+            if constexpr (IsBf16<T>::value) {
+              A[m].v = a0.v * a1.v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) A[m].v[e] = a0.v[e] * a1.v[e];
+            }
+          }
+          F Bv[4];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) frag_ld(Bv[n], &vT[(16 * n + l16) * KP + jb]);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int n = 0; n < 4; ++n) mma(acc[m][n], A[m], Bv[n]);
+            mma(acc[m][4], A[m], ones);
           }
         }
-        F Bv[4];
-#pragma unroll
-        for (int n = 0; n < 4; ++n) frag_ld(Bv[n], &vT[(16 * n + l16) * KP + jb]);
+      }
+      // ---- units of chunk c+1 ----
+      if (Ek1 > Ek || Ev1 > Ev) {
+        const int dk = Ek1 - Ek, dv = Ev1 - Ev;
+        const float sh = pow2(-(nu * dk + dv)), sz = pow2(-nu * dk);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
 #pragma unroll
-          for (int n = 0; n < 4; ++n) mma(acc[m][n], A[m], Bv[n]);
-          mma(acc[m][4], A[m], ones);
+          for (int n = 0; n < 4; ++n) acc[m][n] *= sh;
+          acc[m][4] *= sz;
         }
       }
     }
+    Ek = Ek1;
+    Ev = Ev1;
+    __syncthreads();
+  };
+  for (int c0 = 0; c0 < nchunks; c0 += NR) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      if (c0 + i < nchunks) step(c0 + i, R[(i + 1) % NR], R[(i + 2) % NR]);
   }
 
   // ---- final state -> ABI layout (raw moments, each packed entry once) ----
@@ -530,7 +584,7 @@ __global__ __launch_bounds__(512) void scan_kernel(const T* __restrict__ k, cons
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          int r, t, mu;
+          int r = 0, t = 0, mu = 0;
           if (!kfeature(DH, kb, acc_position(m, 4 * lg + e), r, t, mu)) continue;
           if (t != DH && r > t) continue;  // the (t, r) copy of a diagonal block writes it
           const long f = abi_index(DH, r, t);
@@ -538,10 +592,11 @@ __global__ __launch_bounds__(512) void scan_kernel(const T* __restrict__ k, cons
           for (int n = 0; n < 4; ++n) state_out[sbase + f * DV + 16 * n + l16] = acc[m][n][e] * sh;
           if (l16 == 0) state_out[sbase + D * DV + f] = acc[m][4][e] * sz;
         }
-    }
-    if (lead && tid < NCOL) {
-      if (tid < DV) state_out[sbase + tid] = csum;
-      else state_out[sbase + D * DV] = csum;
+    } else if (cwave && lg == 0) {
+      const float sh = pow2(Ev + beta);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) state_out[sbase + 16 * n + l16] = acc[0][n][0] * sh;
+      if (l16 == 0) state_out[sbase + D * DV] = acc[0][4][0] * pow2(beta);
     }
   }
 }
@@ -803,8 +858,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
       float mq = 0.f;
 #pragma unroll
       for (int i = 0; i < QD; ++i) mq = fmaxf(mq, fabsf(qx[i]));
-      mq = fmaxf(mq, __shfl_xor(mq, 1));
-      mq = fmaxf(mq, __shfl_xor(mq, 2));
+      mq = quad_max(mq);
       int f = exp_above(mq);
       if (f == kNegExp || srow >= nvalid) f = 0;
       const float s = pow2(-f);
@@ -1198,7 +1252,7 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   const T* vv = reinterpret_cast<const T*>(a.v);
   T* yy = reinterpret_cast<T*>(a.y);
   if (stages & 1) {
-    dim3 grid((KB + kScanWaves - 1) / kScanWaves, BH);
+    dim3 grid((KB + 1 + kScanCompute - 1) / kScanCompute, BH);  // K-blocks + the constant row
     if (a.premap)
       hipLaunchKernelGGL((scan_kernel<T, DH, true>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv, a.gamma_k,
                          a.beta_k, a.ln_eps, a.state_in, a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks);
