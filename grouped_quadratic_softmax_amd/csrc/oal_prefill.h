@@ -55,9 +55,11 @@ constexpr int C = kChunk;     // tokens per chunk
 constexpr int KG = 2;         // snapshot K-blocks staged per pipeline step
 // LDS column pitch (elements) of a staged snapshot K-block: 80 bytes (fp16)
 // or 144 bytes (fp32), so that 16 lanes reading 16 bytes each hit distinct banks
+// Elements of one staged group of KG snapshot K-blocks in LDS: KG value
+// blocks of 64 columns x 32 features, then KG z blocks of 32.
 template <typename E>
-__host__ __device__ constexpr int stage_pitch() {
-  return sizeof(E) == 2 ? 40 : 36;
+__host__ __device__ constexpr int stage_elems() {
+  return KG * (DV * 32 + 32);
 }
 constexpr int kNegExp = -200; // exponent of an all-zero block
 
@@ -125,6 +127,26 @@ __device__ __forceinline__ void frag_st(_Float16* p, const float (&x)[8]) {
 __device__ __forceinline__ void frag_st(float* p, const float (&x)[8]) {
   reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// s_waitcnt immediate that waits for vector-memory count <= n (other counters
+// untouched): vmcnt in bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15.
+template <int n>
+constexpr int kWaitVm = (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+// ... and, in the same instruction, for every LDS operation (lgkmcnt = 0)
+template <int n>
+constexpr int kWaitVmLds = (n & 15) | ((n >> 4) << 14) | (7 << 4);
+
+// Workgroup barrier for LDS producer/consumer steps whose global-to-LDS
+// loads are waited for explicitly: the wait (vector-memory count <= N, all
+// LDS operations done) precedes the barrier, and the empty asm with a memory
+// clobber keeps the compiler from moving memory operations across it (a
+// __syncthreads() would also wait for the loads of later stages).
+template <int N>
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitVmLds<N>);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---- power-of-two helpers ----
@@ -281,6 +303,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   const bool cwave = !loader && kb == KB;  // the constant feature's row
   const int nu = kb < NQ ? 2 : (kb < KB ? 1 : 0);  // key-exponent multiplicity of the wave's features
   const bool lead = blockIdx.x == 0 && tid == 0;
+  const long nsnap = (long)nchunks * BH;  // snapshots in the workspace
   // loader role: token ltok, units lhalf + 2 i (dimensions 8 unit ..)
   const int lw = wave - kScanCompute;
   const bool kload = loader && lw < 2;
@@ -500,7 +523,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
       // ---- snapshot S_c: raw = stored * 2^(beta + nu Ek) (* 2^Ev for H) ----
       const long sidx = (long)c * BH + bh;
       if (active) {
-        E* sp = snap + (sidx * KB + kb) * NCOL * 32 + 8 * lg;
+        E* sp = snap + (sidx * KB + kb) * DV * 32 + 8 * lg;
+        E* sz = snap + nsnap * KB * DV * 32 + (sidx * KB + kb) * 32 + 8 * lg;
 #pragma unroll
         for (int n = 0; n < 5; ++n) {
           if (n == 4 && l16 != 0) continue;
@@ -510,7 +534,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
             x[e] = acc[0][n][e];
             x[4 + e] = acc[1][n][e];
           }
-          frag_st(sp + (16 * n + l16) * 32, x);
+          frag_st(n < 4 ? sp + (16 * n + l16) * 32 : sz, x);
         }
         if (lane == 0) sexp[sidx * (KB + 2) + kb] = beta;
       } else if (cwave && lg == 0) {
@@ -635,11 +659,11 @@ __host__ __device__ inline ReadoutLds readout_lds(int RG) {
   ReadoutLds L;
   L.qh = 0;
   L.coef = L.qh + (long)RG * C * DHP * sizeof(E);
-  L.kh = L.coef + (long)RG * KB * 32 * sizeof(E);
+  L.kh = L.coef + (long)RG * (KB + 1) * 32 * sizeof(E);
   L.vt = L.kh + (long)C * DHP * sizeof(E);
   L.bst = L.vt + (long)DV * (C + 8) * sizeof(T);
-  // two stage buffers of KG K-blocks, columns padded to SP elements
-  L.total = L.bst + 2L * KG * NCOL * stage_pitch<E>() * sizeof(E);
+  // three stage buffers of KG K-blocks: value columns, then the z column
+  L.total = L.bst + 3L * stage_elems<E>() * sizeof(E);
   return L;
 }
 
@@ -668,19 +692,20 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
   extern __shared__ __align__(16) unsigned char lds[];
   const ReadoutLds LL = readout_lds<T, DH>(RMAX);
   E* qh = reinterpret_cast<E*>(lds + LL.qh);      // [RG][C][DHP] q / 2^f
-  E* coef = reinterpret_cast<E*>(lds + LL.coef);  // [RG][KB][32] coefficients / 2^c_h
+  E* coef = reinterpret_cast<E*>(lds + LL.coef);  // [RG][KB + 1][32] coefficients * kscale / 2^c_h
   E* kh = reinterpret_cast<E*>(lds + LL.kh);      // [C][DHP] k / 2^aK
   T* vTi = reinterpret_cast<T*>(lds + LL.vt);     // [DV][VP] raw values, transposed
   E* bst = reinterpret_cast<E*>(lds + LL.bst);    // [2][KG][NCOL][32]
   __shared__ int qexp[RMAX][C];
   __shared__ float kscale[KB];  // per-K-block fold factor 2^(15 + tau - tau_max(type))
-  __shared__ int qoff[NQ][4];   // quadratic K-block, lane group -> r0 | t0 << 16
   __shared__ int gm[RMAX][DH];
   __shared__ float pc[RMAX][NPC];
   __shared__ int cexp[RMAX];
   __shared__ float cst[NCOL];
   __shared__ float wmx[NW];
   __shared__ int sc_int[3];  // aK, tau_quad_max, tau_lin_max
+  __shared__ float wtau[2][2];
+  __shared__ __align__(16) int zdummy[NW][4];  // sink of the waves' padding z loads
 
   const int c = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
   const int b = bh / Hkv, kvh = bh % Hkv;
@@ -694,6 +719,74 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
   const long sidx = (long)c * BH + bh;
   const int srow = (tid / 4) % C, sq = tid % 4;  // staging (threads < 256): row, quarter
   const bool stager = tid < 4 * C;
+
+  // ---- snapshot staging: KG K-blocks per stage, stage 0 = the linear ones ----
+  // Stages go straight from global memory into LDS (16 bytes per lane, the
+  // lane's bytes landing at the wave's base + 16 lane).  In LDS the column
+  // parts (eight features) are swizzled, part' = (part + col/2 + col/8) % 4,
+  // so that the 16 lanes of a lane group read their B fragments without
+  // bank conflicts.
+  const E* sv0 = snap + sidx * KB * DV * 32;                     // value blocks
+  const E* sz0 = snap + (long)nchunks * BH * KB * DV * 32 + sidx * KB * 32;  // z blocks
+  constexpr int VE = 16 / sizeof(E);            // elements per 16-byte vector
+  constexpr int VH = sizeof(E) / 2;             // vectors per eight-element part
+  constexpr int VPB = DV * 32 / VE;             // value vectors per K-block
+  constexpr int LPT = KG * VPB / NT;            // value vectors per thread and stage
+  constexpr int ZV = KG * 32 / VE;              // z vectors per stage (wave 0)
+  static_assert(KG * VPB % NT == 0 && ZV <= kWave, "stage split");
+  constexpr int SE = stage_elems<E>();
+  static_assert(NL <= KG, "one linear stage");
+  constexpr int NSTAGE = 1 + (NQ + KG - 1) / KG;
+  auto kb_at = [&](int sg, int slot) __attribute__((always_inline)) {
+    // padding slots map to a real K-block; their scale is forced to zero
+    return sg == 0 ? NQ + min(slot, NL - 1) : min((sg - 1) * KG + slot, NQ - 1);
+  };
+  auto slot_live = [&](int sg, int slot) __attribute__((always_inline)) {
+    return sg == 0 ? slot < NL : (sg - 1) * KG + slot < NQ;
+  };
+  // LDS element offset of (column, part) inside a value block
+  auto swz = [](int col, int part) __attribute__((always_inline)) {
+    return (4 * col + ((part + col / 2 + col / 8) & 3)) * 8;
+  };
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef const __attribute__((address_space(1))) void gbl_void;
+  auto issue = [&](int sg, int buf) __attribute__((always_inline)) {
+    E* dst = bst + (long)buf * SE;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int w = tid + NT * i;                 // LDS vector of this lane
+      const int slot = w / VPB, wl = w % VPB;
+      const int pu = wl / VH, half = wl % VH;
+      const int col = pu / 4, pp = pu % 4;
+      const int part = (pp - col / 2 - col / 8) & 3;
+      const E* src = sv0 + (long)kb_at(sg, slot) * DV * 32 + ((4 * col + part) * VH + half) * VE;
+      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(dst + (long)(w - lane) * VE), 16, 0, 0);
+    }
+    // z vectors: lanes < ZV of wave 0; every other wave issues the same
+    // instruction with only lane 0 live, into its own 16-byte dummy slot, so
+    // that all waves count the same number of outstanding loads
+    if (lane < (wave == 0 ? ZV : 1)) {
+      const int slot = lane / (32 / VE), part = lane % (32 / VE);
+      const E* src = sz0 + (long)kb_at(sg, slot) * 32 + part * VE;
+      void* zd = wave == 0 ? (void*)(dst + KG * DV * 32) : (void*)&zdummy[wave][0];
+      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)zd, 16, 0, 0);
+    }
+  };
+  // barrier after which the stages issued before the last issue are in LDS
+  // (one_left: the wave's most recent stage issue may still be in flight)
+  auto stage_sync = [&](bool one_left) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    if (one_left) {
+      lds_barrier<LPT + 1>();
+    } else {
+      lds_barrier<0>();
+    }
+  };
+  // the first two stages are requested before anything else
+  if (inter) {
+    issue(0, 0);
+    issue(1, 1);
+  }
 
   // ---- chunk-wide prologue: K (scores), V (P . V), snapshot scales ----
   {
@@ -740,26 +833,27 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
     mk = wave_max(mk);
     if (lane == 0) wmx[wave] = mk;
     if (tid < NCOL) cst[tid] = inter ? sconst[sidx * NCOL + tid] : 0.f;
-    for (int idx = tid; idx < NQ * 4; idx += NT) {
-      // padding pairs read row offset 0; their coefficients are zero
-      int rb, tb;
-      pair_of(DH, 2 * (idx / 4) + (idx % 4) / 2, rb, tb);
-      qoff[idx / 4][idx % 4] = rb < 0 ? 0 : (4 * rb + 2 * (idx % 2)) | ((4 * tb) << 16);
+    // snapshot exponents: tau of K-block tid, maxima per feature type
+    int tau_me = kNegExp;
+    if (inter && tid < KB) {
+      const int* ex = sexp + sidx * (KB + 2);
+      tau_me = ex[tid] + (tid < NQ ? 2 : 1) * ex[KB];
     }
-    if (tid == 0) {
-      int tq = kNegExp, tl = kNegExp;
-      if (inter) {
-        const int* ex = sexp + sidx * (KB + 2);
-        const int Ek = ex[KB];
-        for (int kk = 0; kk < KB; ++kk) {
-          if (kk < NQ) tq = max(tq, ex[kk] + 2 * Ek);
-          else tl = max(tl, ex[kk] + Ek);
-        }
+    static_assert(KB <= 2 * kWave, "two waves reduce the K-block exponents");
+    if (wave < 2) {
+      const float tqw = wave_max(tid < NQ ? (float)tau_me : (float)kNegExp);
+      const float tlw = wave_max(tid >= NQ && tid < KB ? (float)tau_me : (float)kNegExp);
+      if (lane == 0) {
+        wtau[0][wave] = tqw;
+        wtau[1][wave] = tlw;
       }
+    }
+    __syncthreads();
+    const int tq = (int)fmaxf(wtau[0][0], wtau[0][1]), tl = (int)fmaxf(wtau[1][0], wtau[1][1]);
+    if (tid == 0) {
       sc_int[1] = tq;
       sc_int[2] = tl;
     }
-    __syncthreads();
     float mall = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mall = fmaxf(mall, wmx[w]);
@@ -771,17 +865,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
       for (int i = 0; i < QD; ++i) kh[srow * DHP + sq * QD + i] = (E)(kx[i] * sk);
     }
     if (tid == 0) sc_int[0] = aK;
-    if (tid < KB) {
-      float f = 0.f;
-      if (inter) {
-        const int* ex = sexp + sidx * (KB + 2);
-        const int be = ex[tid], Ek = ex[KB];
-        const int tau = tid < NQ ? be + 2 * Ek : be + Ek;
-        const int tmax = tid < NQ ? sc_int[1] : sc_int[2];
-        f = pow2(15 + tau - tmax);
-      }
-      kscale[tid] = f;
-    }
+    if (tid < KB) kscale[tid] = inter ? pow2(15 + tau_me - (tid < NQ ? tq : tl)) : 0.f;
   }
   __syncthreads();
   const int aK = sc_int[0];
@@ -794,6 +878,10 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
     constexpr int nh = RMAX;         // head slots per pass
     const int nreal = min(RMAX, R - h0);  // slots beyond are dead: zero features, no output
     __syncthreads();  // previous head group done with qh / coef / bst
+    if (inter && h0 > 0) {
+      issue(0, 0);
+      issue(1, 1);
+    }
     // ---- per-head tables: polynomial [a, b_g / sqrt(d), sym(c)_gh / d],
     // exponent c_h with 2^c_h above every feature coefficient (kBadHead for
     // a group id out of range), feature coefficients / 2^c_h ----
@@ -830,16 +918,27 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < nh * KB * 32; idx += NT) {
-      const int hh = idx / (KB * 32);
-      const unsigned short fe = kpos_dev<DH>.e[idx % (KB * 32)];
-      const int ce = cexp[hh];
-      float val = 0.f;
-      if (fe != kPadFeature && ce != kBadHead) {
-        const int r = fe & 127, t = (fe >> 7) & 127, gr = gm[hh][r];
-        val = t == DH ? pc[hh][1 + gr] : (float)(fe >> 14) * pc[hh][1 + NG + gr * NG + gm[hh][t]];
+    // position-major: one table entry per thread and position, all slots
+#pragma unroll
+    for (int it = 0; it < ((KB + 1) * 32 + NT - 1) / NT; ++it) {
+      const int pos = tid + NT * it;
+      if (pos < (KB + 1) * 32) {
+        // block KB is all zeros: padding slots of the last stage read it
+        const unsigned short fe = pos < KB * 32 ? kpos_dev<DH>.e[pos] : kPadFeature;
+        const float ks = pos < KB * 32 ? kscale[pos / 32] : 0.f;
+        const int r = fe & 127, t = (fe >> 7) & 127;
+        const float mu = (float)(fe >> 14);
+#pragma unroll
+        for (int hh = 0; hh < nh; ++hh) {
+          const int ce = cexp[hh];
+          float val = 0.f;
+          if (fe != kPadFeature && ce != kBadHead) {
+            const int gr = gm[hh][r];
+            val = t == DH ? pc[hh][1 + gr] : mu * pc[hh][1 + NG + gr * NG + gm[hh][t]];
+          }
+          coef[hh * (KB + 1) * 32 + pos] = (E)(val * pow2(-ce) * ks);
+        }
       }
-      coef[idx] = (E)(val * pow2(-ce));
     }
     // ---- stage q rows of the head group (pre-map, row exponent) ----
 #pragma unroll 1
@@ -964,14 +1063,20 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
         const int ja = 16 * jt0 + 4 * lg, jb = ja + 16;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
+          // values of keys ja..ja+3 and jb..jb+3, straight from the tile
           const T* vr = vTi + (16 * n + l16) * VP;
-          float vb[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vb[e] = to_f32(vr[ja + e]);
-            vb[4 + e] = to_f32(vr[jb + e]);
+          PF Bv;
+          if constexpr (IsBf16<T>::value) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(vr + ja);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vr + jb);
+            Bv.v = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          } else {
+            const float4 lo = *reinterpret_cast<const float4*>(vr + ja);
+            const float4 hi = *reinterpret_cast<const float4*>(vr + jb);
+            Bv.v[0] = lo.x; Bv.v[1] = lo.y; Bv.v[2] = lo.z; Bv.v[3] = lo.w;
+            Bv.v[4] = hi.x; Bv.v[5] = hi.y; Bv.v[6] = hi.z; Bv.v[7] = hi.w;
           }
-          mma(cur[n], A, frag_from<IsBf16<T>::value>(vb));
+          mma(cur[n], A, Bv);
         }
         float ones[8];
 #pragma unroll
@@ -998,55 +1103,11 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
 
     // ---- inter-chunk read: phi_q(Q_c) . S_c ----
     if (inter) {
-      const E* sbase = snap + sidx * KB * NCOL * 32;
-      constexpr int BLK = NCOL * 32;                // elements per snapshot K-block
-      constexpr int SP = stage_pitch<E>();          // staged column pitch
-      constexpr int SBLK = NCOL * SP;               // elements per staged K-block
-      constexpr int VEC = 16 / sizeof(E);           // elements per 16-byte vector
-      constexpr int VPB = BLK / VEC;                // vectors per K-block
-      constexpr int NV16 = KG * VPB;                // vectors per stage
-      constexpr int PER = (NV16 + NT - 1) / NT;
-      // stage 0 holds the linear K-blocks (NL <= KG), stages 1.. the quadratic ones
-      static_assert(NL <= KG, "one linear stage");
-      constexpr int NSTAGE = 1 + (NQ + KG - 1) / KG;
-      auto kb_at = [&](int sg, int slot) __attribute__((always_inline)) {
-        // padding slots map to a real K-block; their scale is forced to zero
-        return sg == 0 ? NQ + min(slot, NL - 1) : min((sg - 1) * KG + slot, NQ - 1);
-      };
-      auto slot_live = [&](int sg, int slot) __attribute__((always_inline)) {
-        return sg == 0 ? slot < NL : (sg - 1) * KG + slot < NQ;
-      };
-      struct StageRegs {
-        uint4 v[PER];
-      };
-      // unconditional loads (clamped to valid addresses) keep the stage in
-      // registers; vectors beyond the stage are never written to LDS
-      auto fetch = [&](int sg) __attribute__((always_inline)) {
-        StageRegs r;
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int vi = min(tid + NT * u, NV16 - 1);
-          r.v[u] = reinterpret_cast<const uint4*>(sbase + (long)kb_at(sg, vi / VPB) * BLK)[vi % VPB];
-        }
-        return r;
-      };
-      // LDS copy with columns padded to SP elements (80-byte pitch for fp16):
-      // the 16 lanes of a lane group then read conflict-free
-      auto put = [&](int buf, const StageRegs r) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const int vi = tid + NT * u;
-          if (vi < NV16) {
-            const int slot = vi / VPB, w = vi % VPB, col = w / (32 / VEC), part = w % (32 / VEC);
-            *reinterpret_cast<uint4*>(bst + ((long)buf * KG + slot) * SBLK + col * SP + part * VEC) = r.v[u];
-          }
-        }
-      };
       auto load_b = [&](F (&Bf)[5], int buf, int slot) __attribute__((always_inline)) {
-        const E* bp = bst + ((long)buf * KG + slot) * SBLK + 8 * lg;
+        const E* bp = bst + (long)buf * SE + slot * DV * 32;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) frag_ld(Bf[n], bp + (16 * n + l16) * SP);
-        if (l16 == 0) frag_ld(Bf[4], bp + DV * SP);
+        for (int n = 0; n < 4; ++n) frag_ld(Bf[n], bp + swz(16 * n + l16, lg));
+        if (l16 == 0) frag_ld(Bf[4], bst + (long)buf * SE + KG * DV * 32 + slot * 32 + 8 * lg);
         else frag_zero(Bf[4]);
       };
       // linear K-blocks: (q_u ks) coef; their row factor 2^-f (the row's
@@ -1063,17 +1124,13 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
           for (int j = 0; j < HOWN; ++j) {
             const int hh = HS * j + kpar;
             const E* qrow = qh + ((long)hh * C + row) * DHP;
-            const E* cf = coef + ((long)hh * KB + kk) * 32 + 8 * lg;
+            const E* cf = coef + ((long)hh * (KB + 1) + kk) * 32 + 8 * lg;
             F A;
             if constexpr (IsBf16<T>::value) {
-              const _Float16 s16 = (_Float16)kscale[kk];
-              const h8 qv = *reinterpret_cast<const h8*>(qrow + uo);
-              const h8 cv = *reinterpret_cast<const h8*>(cf);
-              A.v = (qv * h8{s16, s16, s16, s16, s16, s16, s16, s16}) * cv;
+              A.v = *reinterpret_cast<const h8*>(qrow + uo) * *reinterpret_cast<const h8*>(cf);
             } else {
-              const float ks = kscale[kk];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) A.v[e] = (qrow[uo + e] * ks) * cf[e];
+              for (int e = 0; e < 8; ++e) A.v[e] = qrow[uo + e] * cf[e];
             }
 #pragma unroll
             for (int n = 0; n < 5; ++n) mma(acc[j][n], A, Bf[n]);
@@ -1082,26 +1139,45 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
       };
       // quadratic K-blocks: (q_r ks) q_t coef for r in {r0, r0 + 1}, t in
       // t0..t0+3; branch-free so that the accumulators update in place
+      // (prb, ptb): block pair of slot 0 of the next quadratic K-block
+      // (pairs are listed tb-major; K-block kk holds pairs 2 kk, 2 kk + 1)
+      int prb = 0, ptb = 0;
+      auto next_pair = [](int& rb, int& tb) __attribute__((always_inline)) {
+        if (rb == tb) {
+          ++tb;
+          rb = 0;
+        } else {
+          ++rb;
+        }
+      };
       auto compute_quad = [&](int sg, int buf) __attribute__((always_inline)) {
 #pragma unroll 1
         for (int slot = 0; slot < KG; ++slot) {
-          const int kk = kb_at(sg, slot);
-          const float ks = slot_live(sg, slot) ? kscale[kk] : 0.f;
+          const bool live = slot_live(sg, slot);
+          const int kk = live ? kb_at(sg, slot) : KB;  // KB: the zero block
           F Bf[5];
           load_b(Bf, buf, slot);
-          const int off = qoff[kk][lg];
-          const int r0 = off & 0xffff, t0 = off >> 16;
+          int rb1 = prb, tb1 = ptb;
+          next_pair(rb1, tb1);
+          // a padding slot reads row offset 0 (finite values times zero coefficients)
+          const int r0 = live ? 4 * (lg < 2 ? prb : rb1) + 2 * (lg & 1) : 0;
+          const int t0 = live ? 4 * (lg < 2 ? ptb : tb1) : 0;
+          prb = rb1;
+          ptb = tb1;
+          next_pair(prb, ptb);
+          // head slot HS j + kpar sits HS j whole blocks after slot kpar
+          const E* qr = qh + ((long)kpar * C + row) * DHP + r0;
+          const E* qt = qh + ((long)kpar * C + row) * DHP + t0;
+          const E* cb = coef + ((long)kpar * (KB + 1) + kk) * 32 + 8 * lg;
 #pragma unroll
           for (int j = 0; j < HOWN; ++j) {
-            const int hh = HS * j + kpar;
-            const E* qrow = qh + ((long)hh * C + row) * DHP;
-            const E* cf = coef + ((long)hh * KB + kk) * 32 + 8 * lg;
+            const E* qrow = qh + ((long)(HS * j + kpar) * C + row) * DHP;
+            const E* cf = cb + HS * j * (KB + 1) * 32;
             F A;
             if constexpr (IsBf16<T>::value) {
-              const _Float16 s16 = (_Float16)ks;
               const h8 cv = *reinterpret_cast<const h8*>(cf);
-              const h2 rs = *reinterpret_cast<const h2*>(qrow + r0) * h2{s16, s16};
-              const h4 tq = *reinterpret_cast<const h4*>(qrow + t0);
+              const h2 rs = *reinterpret_cast<const h2*>(qr + HS * j * C * DHP);
+              const h4 tq = *reinterpret_cast<const h4*>(qt + HS * j * C * DHP);
               const h2 t01 = h2{tq[0], tq[1]}, t23 = h2{tq[2], tq[3]};
               const h2 e0 = (rs.xx * t01) * h2{cv[0], cv[1]};
               const h2 e1 = (rs.xx * t23) * h2{cv[2], cv[3]};
@@ -1110,24 +1186,25 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
               A.v = h8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
             } else {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) A.v[e] = (qrow[r0 + e / 4] * ks) * qrow[t0 + e % 4] * cf[e];
+              for (int e = 0; e < 8; ++e) A.v[e] = qrow[r0 + e / 4] * qrow[t0 + e % 4] * cf[e];
             }
 #pragma unroll
             for (int n = 0; n < 5; ++n) mma(acc[j][n], A, Bf[n]);
           }
         }
       };
-      // pipeline: stage sg computes from LDS buffer sg & 1 while the loads of
-      // stages sg + 1 (registers, issued one stage earlier) and sg + 2
-      // (issued now) are in flight
-      StageRegs ra = fetch(0);
-      StageRegs rb2 = fetch(NSTAGE > 1 ? 1 : 0);
-      put(0, ra);
-      __syncthreads();
-      if (2 < NSTAGE) ra = fetch(2);
-      compute_lin(0);
-      put(1, rb2);
-      __syncthreads();
+      // pipeline over three LDS buffers: stage sg is read from buffer sg % 3
+      // while stage sg + 2 loads into buffer (sg + 2) % 3; before the barrier
+      // that ends step sg, each wave waits for its loads of stage sg + 1
+      // (issued one step earlier).  Stages 0 and 1 were issued at the start.
+      auto inter_step = [&](int sg) __attribute__((always_inline)) {
+        if (sg + 2 < NSTAGE) issue(sg + 2, (sg + 2) % 3);
+        if (sg == 0) compute_lin(0);
+        else compute_quad(sg, sg % 3);
+        stage_sync(sg + 2 < NSTAGE);
+      };
+      stage_sync(false);
+      inter_step(0);
       // linear K-blocks done: to quadratic units, 2^(tau_l - tau_q - f) per row
 #pragma unroll
       for (int j = 0; j < HOWN; ++j) {
@@ -1139,17 +1216,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
           for (int n = 0; n < 5; ++n) acc[j][n][e] *= fr;
         }
       }
-      for (int sg = 1; sg < NSTAGE; sg += 2) {
-        if (sg + 2 < NSTAGE) rb2 = fetch(sg + 2);
-        compute_quad(sg, 1);
-        if (sg + 1 < NSTAGE) put(0, ra);
-        __syncthreads();
-        if (sg + 1 >= NSTAGE) break;
-        if (sg + 3 < NSTAGE) ra = fetch(sg + 3);
-        compute_quad(sg + 1, 0);
-        if (sg + 2 < NSTAGE) put(1, rb2);
-        __syncthreads();
-      }
+      for (int sg = 1; sg < NSTAGE; ++sg) inter_step(sg);
     }
 
     // ---- normalise and store (one head at a time) ----
@@ -1224,13 +1291,16 @@ FwdWs<T, DH> fwd_ws(int B, int Hq, int Hkv, int N) {
   return w;
 }
 
-// Query heads per KV head served in one pass: 4 (two per wave; eight waves),
-// 2, or 1; the last pass of a head count that is not a multiple carries dead
-// slots.  fp32 activations use at most 2.
+// Query heads per KV head served in one pass: 8 or 4 (four or two per wave;
+// eight waves), 2, or 1; the last pass of a head count that is not a multiple
+// carries dead slots.  fp32 activations use at most 2.
 template <typename T, int DH>
 int pick_rg(int R) {
-  if (R >= 3 && IsBf16<T>::value && readout_lds<T, DH>(4).total <= 148 * 1024) return 4;
-  if (R >= 2 && readout_lds<T, DH>(2).total <= 148 * 1024) return 2;
+  // dynamic LDS limit: 160 KiB per workgroup less the static tables (< 9 KiB)
+  constexpr long lim = 151 * 1024 + 512 * 5;
+  if (R >= 5 && IsBf16<T>::value && readout_lds<T, DH>(8).total <= lim) return 8;
+  if (R >= 3 && IsBf16<T>::value && readout_lds<T, DH>(4).total <= lim) return 4;
+  if (R >= 2 && readout_lds<T, DH>(2).total <= lim) return 2;
   return 1;
 }
 
@@ -1270,7 +1340,7 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   const int has_in = a.state_in != nullptr;
 #define OAL_OUT(RM, NGV, PM)                                                                                    \
   do {                                                                                                          \
-    constexpr int NWV = (RM % 2 == 0 && RM <= 4) ? 8 : 4;                                                                         \
+    constexpr int NWV = RM % 2 == 0 ? 8 : 4;                                                                         \
     auto fn = readout_kernel<T, DH, RM, NGV, PM, NWV>;                                                          \
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),                                      \
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);                  \
@@ -1293,7 +1363,8 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
     switch (rg) {                            \
       case 1: OAL_OUT_NG(1, PM); break;      \
       case 2: OAL_OUT_NG(2, PM); break;      \
-      default: OAL_OUT_NG(4, PM); break;     \
+      case 4: OAL_OUT_NG(4, PM); break;      \
+      default: OAL_OUT_NG(8, PM); break;     \
     }                                        \
   } while (0)
   if constexpr (IsBf16<T>::value) {
