@@ -9,11 +9,11 @@
 //   (A_L + A_R, B_L + B_R + K_L A_R, K_L + K_R).
 //
 // Kernel 1 (partial): one CTA per (token block, KV head, prompt).  Its 256
-// threads are (d_h / 4) dimension quads x token slots; slot s scans a
-// contiguous run of the block's tokens (for bf16 d_h = 64 every row load is
-// one full 128-byte line), the slots of a wave are combined in order with
-// wavefront shuffles, the four waves through LDS, and the block triple goes
-// to the workspace.
+// threads are (d_h / 8) dimension octets x token slots; slot s scans a
+// contiguous run of the block's tokens with 16-byte loads (every load of a
+// token issued before its arithmetic), the slots of a wave are combined in
+// order with wavefront shuffles, the four waves through LDS, and the block
+// triple goes to the workspace.
 // Kernel 2 (combine): one CTA per query head folds the block triples of each
 // prompt in token order (four contiguous quarters, then an ordered combine
 // of the four), normalises, and averages over prompts with equal weights.
@@ -30,27 +30,40 @@ namespace oal {
 
 namespace {
 
-// Four consecutive activation values as floats.
-__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ float4 load4(const uint16_t* p) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
-                     __uint_as_float(w.y & 0xffff0000u));
+// n consecutive activations (n a multiple of 8) as floats, 16-byte loads.
+template <int n>
+__device__ __forceinline__ void load_vals(const uint16_t* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < n; i += 8) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p + i);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[i + 2 * j] = __uint_as_float(ws[j] << 16);
+      out[i + 2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
+    }
+  }
 }
-
-__device__ __forceinline__ void abs_acc(float (&a)[4], const float4 x) {
-  a[0] += fabsf(x.x);
-  a[1] += fabsf(x.y);
-  a[2] += fabsf(x.z);
-  a[3] += fabsf(x.w);
+template <int n>
+__device__ __forceinline__ void load_vals(const float* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < n; i += 4) {
+    const float4 w = *reinterpret_cast<const float4*>(p + i);
+    out[i] = w.x;
+    out[i + 1] = w.y;
+    out[i + 2] = w.z;
+    out[i + 3] = w.w;
+  }
 }
 
 }  // namespace
 
-// Tokens per partial block: the smallest power of two >= 64 that keeps the
-// number of blocks per prompt at or below 64.
-static int contrib_block_tokens(int N) {
+// Tokens per partial block: the smallest power of two that gives every token
+// slot of a CTA (256 threads over d_h / 8 dimension octets) at least one
+// token and keeps the number of blocks per prompt at or below 64.
+static int contrib_block_tokens(int N, int d_h) {
   int tb = 64;
+  while (tb < 256 / (d_h / 8)) tb *= 2;
   while ((long)tb * 64 < (long)N) tb *= 2;
   return tb;
 }
@@ -61,43 +74,51 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
                                                               const int32_t* __restrict__ seq_lens,
                                                               float* __restrict__ part, int Hq,
                                                               int Hkv, int N, int nblk, int TB) {
-  constexpr int NQ4 = DH / 4;                  // dimension quads per row
-  constexpr int TPQ = 256 / NQ4;               // token slots per CTA
-  constexpr int SPW = kWave / NQ4;             // token slots per wave
+  constexpr int NO = DH / 8;                   // dimension octets per row (16-byte loads)
+  constexpr int TPQ = 256 / NO;                // token slots per CTA
+  constexpr int SPW = kWave / NO;              // token slots per wave
   constexpr int NV = 2 * RMAX + 1;             // A[R], B[R], K
   __shared__ float xs[4][NV][DH];
 
   const int blk = blockIdx.x, kvh = blockIdx.y, p = blockIdx.z;
   const int R = Hq / Hkv;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int quad = lane % NQ4, wslot = lane / NQ4;
+  const int oct = lane % NO, wslot = lane / NO;
   const int slot = wave * SPW + wslot;
   int n = seq_lens ? seq_lens[p] : N;
   const bool badlen = n < 1 || n > N;
   if (badlen) n = 0;
 
-  float A[RMAX][4], Bs[RMAX][4], K[4] = {0.f, 0.f, 0.f, 0.f};
+  float A[RMAX][8], Bs[RMAX][8], K[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) K[e] = 0.f;
 #pragma unroll
   for (int hh = 0; hh < RMAX; ++hh)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) A[hh][e] = Bs[hh][e] = 0.f;
+    for (int e = 0; e < 8; ++e) A[hh][e] = Bs[hh][e] = 0.f;
 
   const int per = TB / TPQ;  // tokens per slot (a contiguous run)
   const int t0 = blk * TB + slot * per;
   const int t1 = min(t0 + per, n);
-  const T* kp = k + ((long)(p * Hkv + kvh) * N) * DH + 4 * quad;
-  const T* qp = q + ((long)(p * Hq + kvh * R) * N) * DH + 4 * quad;
+  const T* kp = k + ((long)(p * Hkv + kvh) * N) * DH + 8 * oct;
+  const T* qp = q + ((long)(p * Hq + kvh * R) * N) * DH + 8 * oct;
   for (int t = t0; t < t1; ++t) {
-    abs_acc(K, load4(kp + (long)t * DH));
+    // every load of the token first, then the arithmetic
+    float kx[8], qx[RMAX][8];
+    load_vals<8>(kp + (long)t * DH, kx);
+#pragma unroll
+    for (int hh = 0; hh < RMAX; ++hh)
+      if (hh < R) load_vals<8>(qp + ((long)hh * N + t) * DH, qx[hh]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) K[e] += fabsf(kx[e]);
 #pragma unroll
     for (int hh = 0; hh < RMAX; ++hh) {
       if (hh < R) {
-        const float4 x = load4(qp + ((long)hh * N + t) * DH);
-        const float qa[4] = {fabsf(x.x), fabsf(x.y), fabsf(x.z), fabsf(x.w)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          A[hh][e] += qa[e];
-          Bs[hh][e] += qa[e] * K[e];
+        for (int e = 0; e < 8; ++e) {
+          const float qa = fabsf(qx[hh][e]);
+          A[hh][e] += qa;
+          Bs[hh][e] += qa * K[e];
         }
       }
     }
@@ -106,9 +127,9 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
   // ordered combine of the slots of this wave: slot s absorbs slot s + 1,
   // then the pair at s + 2, ... (the lane of slot s is always the left part)
 #pragma unroll
-  for (int off = NQ4; off < kWave; off <<= 1) {
+  for (int off = NO; off < kWave; off <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 8; ++e) {
       const float Kr = __shfl_down(K[e], off);
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
@@ -124,8 +145,8 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
   }
   if (wslot == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * quad + e;
+    for (int e = 0; e < 8; ++e) {
+      const int r = 8 * oct + e;
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
         if (hh < R) {
@@ -179,12 +200,24 @@ __global__ __launch_bounds__(4 * DH) void contrib_combine_kernel(const float* __
     // contiguous quarter of the blocks for this part: [b0, b1)
     const int b0 = (nb_used * w) / 4, b1 = (nb_used * (w + 1)) / 4;
     float tA = 0.f, tB = 0.f, tK = 0.f;
-    for (int blk = b0; blk < b1; ++blk) {
-      const float* x = base + blk * stride;
-      const float Ab = x[hh * DH + r];
-      tB += x[(R + hh) * DH + r] + tK * Ab;
-      tA += Ab;
-      tK += x[2 * R * DH + r];
+    // eight blocks' loads in flight at a time, folded in order
+    for (int bb = b0; bb < b1; bb += 8) {
+      float xa[8], xb[8], xk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* x = base + (long)min(bb + u, b1 - 1) * stride;
+        xa[u] = x[hh * DH + r];
+        xb[u] = x[(R + hh) * DH + r];
+        xk[u] = x[2 * R * DH + r];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (bb + u < b1) {
+          tB += xb[u] + tK * xa[u];
+          tA += xa[u];
+          tK += xk[u];
+        }
+      }
     }
     // ordered combine of the four quarters
     __syncthreads();
@@ -219,7 +252,7 @@ __global__ __launch_bounds__(4 * DH) void contrib_combine_kernel(const float* __
 }
 
 size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h) {
-  const int TB = contrib_block_tokens(N);
+  const int TB = contrib_block_tokens(N, d_h);
   const long nblk = (N + TB - 1) / TB;
   const int R = Hq / Hkv;
   return (size_t)P * Hkv * nblk * (2 * R + 1) * d_h * sizeof(float);
@@ -227,7 +260,7 @@ size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h) {
 
 template <typename T, int DH, int RMAX>
 static hipError_t launch_contrib_r(const ContribLaunch& a, hipStream_t stream) {
-  const int TB = contrib_block_tokens(a.N);
+  const int TB = contrib_block_tokens(a.N, a.d_h);
   const int nblk = (a.N + TB - 1) / TB;
   float* part = reinterpret_cast<float*>(a.workspace);
   hipLaunchKernelGGL((contrib_partial_kernel<T, DH, RMAX>), dim3(nblk, a.Hkv, a.P), dim3(256), 0, stream,

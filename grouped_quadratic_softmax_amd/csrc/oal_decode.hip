@@ -102,6 +102,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   __shared__ float red[16][RMAX][DV];
   __shared__ float dred[RMAX][256 / kWave];
   __shared__ int bad;
+  __shared__ int gmap[RMAX][DH];  // group of each dimension (clamped; `bad` flags ids out of range)
 
   const int slice = blockIdx.x, nslice = gridDim.x;
   const int bh = blockIdx.y;
@@ -129,15 +130,19 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   for (int idx = tid; idx < R * DH; idx += blockDim.x) {
     const int g = group_of_dim[(kvh * R + idx / DH) * DH + idx % DH];
     if (g < 0 || g >= G) atomicOr(&bad, 1);
+    gmap[idx / DH][idx % DH] = min(max(g, 0), G - 1);
   }
   __syncthreads();
 
-  // feature values of the slice rows: const, linear r, pairs r <= t
+  // feature values of the slice rows: const, linear r, pairs r <= t; the
+  // coefficient of (r, t) is the symmetric c of the two groups (read from
+  // global memory, cached) times 2 off the diagonal
   const float inv_sqrt_d = 1.f / sqrtf((float)DH);
   for (int f = f0 + tid; f < f1; f += blockDim.x) {
     int r, t;
     feature_pair<DH>(f, r, t);
     phik[f - f0] = khat[r] * khat[t];
+#pragma unroll
     for (int hh = 0; hh < RMAX; ++hh) {
       if (hh >= R) break;
       const int h = kvh * R + hh;
@@ -145,11 +150,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
       if (r == DH) {
         cf = ca[h];
       } else if (t == DH) {
-        const int g = min(max(group_of_dim[h * DH + r], 0), G - 1);
-        cf = cb[h * G + g] * inv_sqrt_d;
+        cf = cb[h * G + gmap[hh][r]] * inv_sqrt_d;
       } else {
-        const int g1 = min(max(group_of_dim[h * DH + r], 0), G - 1);
-        const int g2 = min(max(group_of_dim[h * DH + t], 0), G - 1);
+        const int g1 = gmap[hh][r], g2 = gmap[hh][t];
         const float m = r == t ? 1.f : 2.f;
         cf = m * 0.5f * (cc[(h * G + g1) * G + g2] + cc[(h * G + g2) * G + g1]) / DH;
       }
@@ -166,13 +169,16 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
 #pragma unroll
   for (int hh = 0; hh < RMAX; ++hh) acc[hh][0] = acc[hh][1] = acc[hh][2] = acc[hh][3] = 0.f;
 
-  constexpr int U = 4;
+  constexpr int U = 8;
   for (int fb = f0 + rg; fb < f1; fb += 16 * U) {
     float4 hv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int f = fb + 16 * u;
-      if (f < f1) hv[u] = *reinterpret_cast<const float4*>(&sp[(long)f * DV + 4 * c4]);
+      if (f < f1) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(&sp[(long)f * DV + 4 * c4]);
+        hv[u] = make_float4(w[0], w[1], w[2], w[3]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
       x.y += pk * v4.y;
       x.z += pk * v4.z;
       x.w += pk * v4.w;
-      *reinterpret_cast<float4*>(&sp[(long)f * DV + 4 * c4]) = x;
+      *reinterpret_cast<f32x4*>(&sp[(long)f * DV + 4 * c4]) = f32x4{x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
         if (hh < R) {
@@ -255,6 +261,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(const float* __restr
   const int R = Hq / Hkv, kvh = h / R, hh = h % R;
   const long bh = (long)b * Hkv + kvh;
   float num = 0.f, den = 0.f;
+#pragma unroll 8
   for (int s = 0; s < nslice; ++s) {
     const float* x = part + ((bh * nslice + s) * R + hh) * NC;
     num += x[n];
