@@ -27,7 +27,7 @@ class OalDims(ctypes.Structure):
 
 class OalCoeffs(ctypes.Structure):
     _fields_ = [("group_of_dim", ctypes.c_void_p), ("a", ctypes.c_void_p), ("b", ctypes.c_void_p),
-                ("c", ctypes.c_void_p)]
+                ("c", ctypes.c_void_p), ("diagonal", ctypes.c_int32)]
 
 
 class OalPrep(ctypes.Structure):

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboal.so")
 
-HIP_SOURCES = ["oal_prefill_d64.hip", "oal_prefill_d32.hip", "oal_prefill_d16.hip", "oal_prefill.hip",
+HIP_SOURCES = ["oal_prefill_d64.hip", "oal_prefill_d32.hip", "oal_prefill_d16.hip", "oal_prefill.hip", "oal_diag.hip",
                "oal_decode.hip", "oal_contrib.hip"]
 HOST_SOURCES = ["oal_api.cpp"]
 

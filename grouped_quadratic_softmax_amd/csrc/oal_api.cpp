@@ -125,10 +125,13 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   const bool want_states = stages & 1, want_out = stages & 2;
   int st = check_dims(dims, true);
   if (st != OAL_OK) return st;
+  bool diagonal = false;
   if (want_out) {
     if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
     if ((st = check_coeff_ptrs(coeffs)) != OAL_OK) return st;
-    if (dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
+    diagonal = coeffs->diagonal != 0;
+    if (diagonal && !want_states) return OAL_ERR_UNSUPPORTED;  // the fused form has no separate stages
+    if (!diagonal && dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
   }
   if ((st = check_prep(prep)) != OAL_OK) return st;
   if (dims->batch == 0) return OAL_OK;
@@ -144,8 +147,10 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   if (k == nullptr || v == nullptr) return OAL_ERR_INVALID_ARG;
   if (want_out && (q == nullptr || y == nullptr)) return OAL_ERR_INVALID_ARG;
   if (want_states && state_out != nullptr && state_out == state_in) return OAL_ERR_INVALID_ARG;
-  const size_t need = oal_fwd_workspace_bytes(dims);
-  if (workspace == nullptr || workspace_bytes < need) return OAL_ERR_WORKSPACE;
+  if (!diagonal) {
+    const size_t need = oal_fwd_workspace_bytes(dims);
+    if (workspace == nullptr || workspace_bytes < need) return OAL_ERR_WORKSPACE;
+  }
 
   oal::FwdLaunch a{};
   a.B = dims->batch; a.Hq = dims->n_q_heads; a.Hkv = dims->n_kv_heads; a.N = dims->seq_len;
@@ -160,6 +165,8 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
     a.ln_eps = prep->ln_eps;
   }
   a.state_in = state_in; a.state_out = state_out; a.y = y; a.workspace = workspace;
+  a.diagonal = diagonal;
+  if (diagonal) return oal::launch_fwd_diag(a, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
   return oal::launch_fwd(a, stages, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
 }
 
@@ -209,6 +216,7 @@ int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const vo
   a.G = dims->n_groups; a.dtype = dims->dtype;
   a.q = q; a.k = k; a.v = v;
   a.group_of_dim = coeffs->group_of_dim; a.ca = coeffs->a; a.cb = coeffs->b; a.cc = coeffs->c;
+  a.diagonal = coeffs->diagonal != 0;
   a.premap = prep != nullptr;
   if (prep) {
     a.gamma_q = prep->gamma_q; a.beta_q = prep->beta_q; a.gamma_k = prep->gamma_k; a.beta_k = prep->beta_k;

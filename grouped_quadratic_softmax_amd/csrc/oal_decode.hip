@@ -72,8 +72,8 @@ __device__ __forceinline__ void feature_pair(int f, int& r, int& t) {
 }  // namespace
 
 // Rows per slice (a multiple of 16) and slice count for `states` states.
-void decode_slicing(int d_h, long states, int& rows, int& nslice) {
-  const int D = (int)packed_features(d_h);
+void decode_slicing(int d_h, long states, int& rows, int& nslice, bool diagonal) {
+  const int D = diagonal ? 1 + 2 * d_h : (int)packed_features(d_h);
   long want = (2048 + states - 1) / states;           // aim for >= 2048 CTAs
   want = want < 1 ? 1 : want;
   const long min_slices = (D + 1023) / 1024;           // at most 1024 rows per CTA
@@ -91,8 +91,15 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const float* __restrict__ cb, const float* __restrict__ cc, int G,
     const float* __restrict__ gamma_q, const float* __restrict__ beta_q,
     const float* __restrict__ gamma_k, const float* __restrict__ beta_k, float ln_eps,
-    float* __restrict__ state, float* __restrict__ part, T* __restrict__ y, int Hq, int Hkv, int rows) {
+    float* __restrict__ state, float* __restrict__ part, T* __restrict__ y, int Hq, int Hkv, int rows,
+    int diagonal) {
   constexpr int D = (int)packed_features(DH);
+  // rows of the state this step touches: all D features, or in the
+  // dimension-wise form the constant, linear and squared ones (1 + 2 d_h)
+  const int DN = diagonal ? 1 + 2 * DH : D;
+  auto row_of = [&](int u) __attribute__((always_inline)) {
+    return (diagonal && u > DH) ? (int)abi_index(DH, u - 1 - DH, u - 1 - DH) : u;
+  };
   extern __shared__ float smem[];
   float* phik = smem;                 // [rows]
   float* phiq = smem + rows;          // [RMAX][rows]
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int R = Hq / Hkv;
   const int tid = threadIdx.x;
-  const int f0 = slice * rows, f1 = min(f0 + rows, D);
+  const int f0 = slice * rows, f1 = min(f0 + rows, DN);
 
   if (tid == 0) bad = 0;
   if (tid < DH) khat[tid] = to_f32(k[(long)bh * DH + tid]);
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const float inv_sqrt_d = 1.f / sqrtf((float)DH);
   for (int f = f0 + tid; f < f1; f += blockDim.x) {
     int r, t;
-    feature_pair<DH>(f, r, t);
+    feature_pair<DH>(row_of(f), r, t);
     phik[f - f0] = khat[r] * khat[t];
 #pragma unroll
     for (int hh = 0; hh < RMAX; ++hh) {
@@ -151,6 +158,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
         cf = ca[h];
       } else if (t == DH) {
         cf = cb[h * G + gmap[hh][r]] * inv_sqrt_d;
+      } else if (diagonal) {
+        const int g1 = gmap[hh][r];
+        cf = r == t ? cc[(h * G + g1) * G + g1] / DH : 0.f;
       } else {
         const int g1 = gmap[hh][r], g2 = gmap[hh][t];
         const float m = r == t ? 1.f : 2.f;
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     for (int u = 0; u < U; ++u) {
       const int f = fb + 16 * u;
       if (f < f1) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(&sp[(long)f * DV + 4 * c4]);
+        const f32x4 w = *reinterpret_cast<const f32x4*>(&sp[(long)row_of(f) * DV + 4 * c4]);
         hv[u] = make_float4(w[0], w[1], w[2], w[3]);
       }
     }
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
       x.y += pk * v4.y;
       x.z += pk * v4.z;
       x.w += pk * v4.w;
-      *reinterpret_cast<f32x4*>(&sp[(long)f * DV + 4 * c4]) = f32x4{x.x, x.y, x.z, x.w};
+      *reinterpret_cast<f32x4*>(&sp[(long)row_of(f) * DV + 4 * c4]) = f32x4{x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
         if (hh < R) {
@@ -209,8 +219,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   for (int hh = 0; hh < RMAX; ++hh) dacc[hh] = 0.f;
   float* zp = sp + (long)D * DV;
   for (int f = f0 + tid; f < f1; f += blockDim.x) {
-    const float zn = zp[f] + phik[f - f0];
-    zp[f] = zn;
+    const int fr = row_of(f);
+    const float zn = zp[fr] + phik[f - f0];
+    zp[fr] = zn;
 #pragma unroll
     for (int hh = 0; hh < RMAX; ++hh)
       if (hh < R) dacc[hh] += phiq[hh * rows + (f - f0)] * zn;
@@ -272,7 +283,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(const float* __restr
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h) {
   int rows, nslice;
-  decode_slicing(d_h, (long)B * Hkv, rows, nslice);
+  decode_slicing(d_h, (long)B * Hkv, rows, nslice, false);  // bounds the dimension-wise form too
   if (nslice == 1) return 0;
   return (size_t)B * Hkv * nslice * (Hq / Hkv) * NC * sizeof(float);
 }
@@ -280,7 +291,7 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h) {
 template <typename T, int DH, int RMAX>
 static hipError_t launch_decode_r(const DecodeLaunch& a, hipStream_t stream) {
   int rows, nslice;
-  decode_slicing(DH, (long)a.B * a.Hkv, rows, nslice);
+  decode_slicing(DH, (long)a.B * a.Hkv, rows, nslice, a.diagonal);
   const size_t shm = (size_t)(1 + RMAX) * rows * sizeof(float);
   dim3 grid(nslice, a.B * a.Hkv);
   const T* qq = reinterpret_cast<const T*>(a.q);
@@ -291,11 +302,11 @@ static hipError_t launch_decode_r(const DecodeLaunch& a, hipStream_t stream) {
   if (a.premap)
     hipLaunchKernelGGL((decode_partial_kernel<T, DH, RMAX, true>), grid, dim3(256), shm, stream, qq, kk, vv,
                        a.group_of_dim, a.ca, a.cb, a.cc, a.G, a.gamma_q, a.beta_q, a.gamma_k, a.beta_k,
-                       a.ln_eps, a.state, part, yy, a.Hq, a.Hkv, rows);
+                       a.ln_eps, a.state, part, yy, a.Hq, a.Hkv, rows, (int)a.diagonal);
   else
     hipLaunchKernelGGL((decode_partial_kernel<T, DH, RMAX, false>), grid, dim3(256), shm, stream, qq, kk, vv,
                        a.group_of_dim, a.ca, a.cb, a.cc, a.G, nullptr, nullptr, nullptr, nullptr, 0.f,
-                       a.state, part, yy, a.Hq, a.Hkv, rows);
+                       a.state, part, yy, a.Hq, a.Hkv, rows, (int)a.diagonal);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nslice == 1) return err;
   const long total = (long)a.B * a.Hq * DV;

@@ -15,6 +15,7 @@ struct FwdLaunch {
   const void *q, *k, *v;
   const int32_t* group_of_dim;
   const float *ca, *cb, *cc;
+  bool diagonal;
   bool premap;
   const float *gamma_q, *beta_q, *gamma_k, *beta_k;
   float ln_eps;
@@ -29,6 +30,7 @@ struct DecodeLaunch {
   const void *q, *k, *v;
   const int32_t* group_of_dim;
   const float *ca, *cb, *cc;
+  bool diagonal;
   bool premap;
   const float *gamma_q, *beta_q, *gamma_k, *beta_k;
   float ln_eps;
@@ -49,8 +51,10 @@ struct ContribLaunch {
 size_t fwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d_h, int dtype);
 // stages: bit 0 = chunk states (scan), bit 1 = outputs (readout)
 hipError_t launch_fwd(const FwdLaunch& a, int stages, hipStream_t stream);
+// dimension-wise form (coefficients with `diagonal`): one fused kernel
+hipError_t launch_fwd_diag(const FwdLaunch& a, hipStream_t stream);
 hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStream_t stream);
-void decode_slicing(int d_h, long states, int& rows, int& nslice);
+void decode_slicing(int d_h, long states, int& rows, int& nslice, bool diagonal);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h);

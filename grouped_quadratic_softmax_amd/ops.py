@@ -51,7 +51,7 @@ class Coeffs:
     upload.
     """
 
-    def __init__(self, group_of_dim, a, b, c, device="cuda"):
+    def __init__(self, group_of_dim, a, b, c, device="cuda", diagonal=None):
         g = np.ascontiguousarray(np.asarray(group_of_dim, dtype=np.int32))
         a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
         b = np.ascontiguousarray(np.asarray(b, dtype=np.float32))
@@ -63,6 +63,13 @@ class Coeffs:
         L.check(L.lib().oal_check_coeffs(ctypes.byref(dims), g.ctypes.data_as(ctypes.c_void_p),
                                          c.ctypes.data_as(ctypes.c_void_p)), "oal_check_coeffs")
         self.n_heads, self.d_h, self.n_groups = Hq, d, G
+        if diagonal is None:
+            # the dimension-wise form is exact when every group is one
+            # dimension and c is diagonal; it is required beyond 8 groups
+            singletons = G == d and all(np.array_equal(np.sort(row), np.arange(d)) for row in g)
+            offdiag = c * (1.0 - np.eye(G, dtype=np.float32))
+            diagonal = bool(singletons and not np.any(offdiag))
+        self.diagonal = bool(diagonal)
         self.group_of_dim = torch.from_numpy(g).to(device)
         self.a = torch.from_numpy(a).to(device)
         self.b = torch.from_numpy(b).to(device)
@@ -70,7 +77,7 @@ class Coeffs:
 
     def struct(self):
         return L.OalCoeffs(self.group_of_dim.data_ptr(), self.a.data_ptr(), self.b.data_ptr(),
-                           self.c.data_ptr())
+                           self.c.data_ptr(), 1 if self.diagonal else 0)
 
 
 class Prep:
@@ -142,7 +149,8 @@ def fwd(q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None, ret
         _need(state_in.numel() == B * Hkv * sf, "state_in size")
     if return_state and state_out is None:
         state_out = torch.empty((B, Hkv, sf), dtype=torch.float32, device=q.device)
-    nbytes = int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(dims)))
+    # the dimension-wise form needs no workspace
+    nbytes = 0 if coeffs.diagonal else int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(dims)))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     cs = coeffs.struct()
@@ -214,6 +222,8 @@ class PrefillPlan:
 
     ``states()`` and ``outputs()`` enqueue the two stages of oal_fwd
     (``run()`` both) on the stream that is current at construction time.
+    Coefficients in the dimension-wise form run as one oal_fwd call
+    (``run()`` only).
     """
 
     def __init__(self, q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None,
@@ -227,7 +237,7 @@ class PrefillPlan:
         self.state_out = (torch.empty((B, Hkv, state_floats(d, dv)), dtype=torch.float32, device=q.device)
                           if with_state else None)
         self.dims = _dims(B, Hq, Hkv, N, d, dv, coeffs.n_groups, q.dtype)
-        nbytes = int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(self.dims)))
+        nbytes = 0 if coeffs.diagonal else int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(self.dims)))
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
         self._cs = coeffs.struct()
         self._ps = prep.struct() if prep is not None else None
@@ -238,6 +248,8 @@ class PrefillPlan:
                              *ws, st)
         self._out_args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(self._cs), pp,
                           _ptr(self.y), *ws, st)
+        self._fwd_args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(self._cs), pp,
+                          _ptr(state_in), _ptr(self.state_out), _ptr(self.y), *ws, st)
         self._lib = L.lib()
 
     def states(self):
@@ -247,8 +259,11 @@ class PrefillPlan:
         L.check(self._lib.oal_fwd_outputs(*self._out_args), "oal_fwd_outputs")
 
     def run(self):
-        self.states()
-        self.outputs()
+        if self.coeffs.diagonal:
+            L.check(self._lib.oal_fwd(*self._fwd_args), "oal_fwd")
+        else:
+            self.states()
+            self.outputs()
         return self.y
 
 

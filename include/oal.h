@@ -43,9 +43,10 @@
  *    H[f][l] = sum_j phi_f(k_j) v_jl and z[f] = sum_j phi_f(k_j), with
  *    phi = [1, k_r, k_r k_t]; the packed count is the one of the paper's
  *    App. D (139,425 floats at d_h = d_v = 64).
- *  - Supported shapes: d_h in {16, 32, 64}; d_v = 64; 1 <= G <= 8 with any
- *    group map, or G = d_h singleton groups with diagonal c (the ReBased
- *    elementwise-square reading).  Others return OAL_ERR_UNSUPPORTED.
+ *  - Supported shapes: d_h in {16, 32, 64}; d_v = 64; prefill: 1 <= G <= 8
+ *    with any group map, or any G <= d_h in the dimension-wise form
+ *    (oal_coeffs.diagonal); decode and chi: any G <= d_h.  Others return
+ *    OAL_ERR_UNSUPPORTED.
  *  - Every call returns a status; no exception or abort crosses the ABI.
  *    Arguments are validated on the host before anything is enqueued.  A
  *    zero-length batch or sequence is valid and enqueues nothing.
@@ -83,12 +84,25 @@ typedef struct oal_dims {
   int32_t dtype;      /* OAL_F32 or OAL_BF16 */
 } oal_dims;
 
-/* Grouped kernel coefficients, all device pointers (see conventions). */
+/* Grouped kernel coefficients, all device pointers (see conventions).
+ *
+ * diagonal != 0 selects the dimension-wise form
+ *     kappa = a + sum_r b_g(r) x_r + sum_r c_g(r)g(r) x_r^2,
+ * which is the grouped kernel when every group holds one dimension and c is
+ * diagonal (the ReBased feature map read as an elementwise square, "Linear
+ * Transformers with Learnable Kernel Functions", section on the learnable
+ * parabola); off-diagonal entries of c are then ignored and any G <= d_h is
+ * accepted.  Its features are [1, k_r, k_r^2] (1 + 2 d_h of them): oal_fwd
+ * then needs no workspace (it may be NULL), and oal_fwd and oal_decode_step
+ * read and write only the constant, linear and squared-dimension entries of
+ * a state (the other entries of state_out are not written).  The two-stage
+ * calls oal_fwd_states / oal_fwd_outputs do not support it. */
 typedef struct oal_coeffs {
   const int32_t* group_of_dim; /* [Hq, d_h] */
   const float* a;              /* [Hq] */
   const float* b;              /* [Hq, G] */
   const float* c;              /* [Hq, G, G] */
+  int32_t diagonal;            /* 0: grouped kernel; nonzero: dimension-wise form */
 } oal_coeffs;
 
 /* Optional ReBased pre-map x -> gamma * LayerNorm(x) + beta applied to q

@@ -104,3 +104,15 @@ def sample_rows(N, C, n_random, seed):
 
 def log(msg):
     print(msg, flush=True)
+
+
+def diag_form_mask(d, dv):
+    """Boolean mask over a packed state block of the entries the dimension-wise
+    form reads and writes: rows of the constant, linear and squared features
+    (H rows [D][dv], then z [D])."""
+    D = O.feature_count(d)
+    rows = np.zeros(D, bool)
+    rows[: 1 + d] = True
+    for r in range(d):
+        rows[1 + d + r * d - r * (r - 1) // 2] = True  # pair (r, r) in row-major upper-triangle order
+    return np.concatenate([np.repeat(rows, dv), rows])

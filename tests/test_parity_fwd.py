@@ -10,8 +10,8 @@ import pytest
 
 import oracle as O
 import synthetic as S
-from helpers import (TOL, gpu_coeffs, gpu_prep, log, oracle_coeffs, oracle_prep, rel_err, require_gpu,
-                     sample_rows, to_dev, to_np)
+from helpers import (TOL, diag_form_mask, gpu_coeffs, gpu_prep, log, oracle_coeffs, oracle_prep, rel_err,
+                     require_gpu, sample_rows, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,91 @@ def test_c3_taylor_d16_small():
 
 def test_c3_taylor_d16_fp32():
     _run_case(S.make(3, batch=1, n_q_heads=2, n_kv_heads=2, seq_len=200, dtype="f32"))
+
+
+def test_c4_rebased_elementwise_premap():
+    # the default ReBased reading: one singleton group per dimension, c = d I
+    wl = S.make(4, batch=2, n_q_heads=2, n_kv_heads=2, seq_len=150)
+    assert wl.n_groups == 64
+    _run_case(wl)
+
+
+def _diag_workload(d, dtype, seed, Hq=4, Hkv=2, N=200, B=2):
+    """Singleton groups (a permutation per head), diagonal c > 0 and b, with a
+    large enough that every kernel value is >= 0.05:
+    c x^2 + b x >= -b^2 / (4 c)."""
+    wl = S.make(2, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, seq_len=N, dtype=dtype)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, N, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, N, 64)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = S.bf16_round(q), S.bf16_round(k), S.bf16_round(v)
+    groups = np.stack([rng.permutation(d) for _ in range(Hq)]).astype(np.int32)
+    cd = rng.uniform(0.5, 2.0, (Hq, d))
+    b = rng.uniform(-1.0, 1.0, (Hq, d))
+    c = np.stack([np.diag(x) for x in cd])
+    # per-dimension terms in x = q k / sqrt(d): b/sqrt(d) x + c/d x^2
+    a = 0.05 + ((b / np.sqrt(d)) ** 2 / (4 * cd / d)).sum(axis=1)
+    wl.q, wl.k, wl.v, wl.d_h, wl.n_groups = q, k, v, d, d
+    wl.group_of_dim = groups
+    wl.coeff = {"kind": "abc", "a": a, "b": b, "c": c}
+    return wl
+
+
+@pytest.mark.parametrize("d", [16, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dimensionwise_form(d, dtype):
+    _run_case(_diag_workload(d, dtype, seed=d))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dimensionwise_state_and_continuation(dtype):
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    wl = _diag_workload(64, dtype, seed=7, N=170)
+    co = gpu_coeffs(wl, wl.group_of_dim)
+    assert co.diagonal
+    q, k, v = to_dev(wl.q, dtype), to_dev(wl.k, dtype), to_dev(wl.v, dtype)
+    n1 = 90
+    sf = oal.state_floats(64, 64)
+    sentinel = 7.0
+    s1 = torch.full((wl.batch, wl.n_kv_heads, sf), sentinel, device="cuda")
+    y1, _ = oal.fwd(q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(), co,
+                    return_state=True, state_out=s1)
+    s2 = torch.full_like(s1, sentinel)
+    y2, _ = oal.fwd(q[:, :, n1:].contiguous(), k[:, :, n1:].contiguous(), v[:, :, n1:].contiguous(), co,
+                    state_in=s1, return_state=True, state_out=s2)
+    a, b, c = oracle_coeffs(wl)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)
+    assert rel_err(np.concatenate([to_np(y1), to_np(y2)], axis=2), ref) <= TOL[dtype]
+    # state: the form's entries against the oracle's raw moments (bf16
+    # features: unit roundoff 2^-9 per feature value; fp32: 2^-24), the rest
+    # of state_out untouched
+    touched = diag_form_mask(64, 64)
+    u = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -24
+    N = wl.seq_len
+    for bi in range(wl.batch):
+        for kh in range(wl.n_kv_heads):
+            ref_s = O.abi_state_from_matrix(O.state_from_prefix(wl.k[bi, kh], wl.v[bi, kh]))
+            absum = O.abi_state_from_matrix(O.state_from_prefix(np.abs(wl.k[bi, kh]), np.abs(wl.v[bi, kh])))
+            bound = (3 * u + N * 2.0 ** -24) * absum + 2.0 ** -24 * absum.max()
+            got = to_np(s2)[bi, kh]
+            assert (np.abs(got - ref_s)[touched] <= bound[touched]).all(), (bi, kh)
+            assert (got[~touched] == sentinel).all()
+
+
+def test_dimensionwise_form_rejects_two_stage_calls():
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    wl = _diag_workload(16, "bf16", seed=3, N=64)
+    q, k, v = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+    plan = oal.PrefillPlan(q, k, v, gpu_coeffs(wl, wl.group_of_dim))
+    with pytest.raises(oal.OalError) as info:
+        plan.outputs()
+    assert info.value.status == -2  # OAL_ERR_UNSUPPORTED
+    plan.run()  # one oal_fwd call, no workspace
 
 
 def test_c4_rebased_squared_dot_premap():
