@@ -200,6 +200,19 @@ def run_secondary(args):
                                "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                "hbm_frac": io / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del pre, q, k, v
+    # ReBased elementwise-square prefill, B=16, H=8, N=2048 (dimension-wise
+    # form: features [1, k, k^2], HBM-bound)
+    wl = S.make(4)
+    q, k, v = device_inputs(wl)
+    p = wl.premap
+    pre = oal.PrefillPlan(q, k, v, coeffs_for(wl),
+                          oal.Prep(p["gamma_q"], p["beta_q"], p["gamma_k"], p["beta_k"], p["ln_eps"]))
+    ms = time_events(pre.run, steps, warm)
+    tok = wl.batch * wl.seq_len
+    io = tok * wl.n_q_heads * (2 * 64 * 2) + tok * wl.n_kv_heads * (2 * 64 * 2)
+    out["c4_rebased_prefill"] = {"ms": ms, "tokens_per_s": tok / (ms * 1e-3),
+                                 "hbm_frac": io / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del pre, q, k, v
     # 32k-token prefill, 16 heads, 8 contribution-sorted groups
     wl = S.make(5)
     q, k, v = device_inputs(wl)
@@ -234,8 +247,12 @@ def run_pmc_target(args):
     """Launch only one kernel repeatedly, for rocprofv3 counter passes.
 
     ``readout``: the chunk readout of the main workload (after one states
-    pass); ``states``: the chunk scan of the main workload; ``copy``: a plain device copy of 1 GiB (fp32), whose FETCH_SIZE and
-    WRITE_SIZE readings calibrate the counters against a known byte count."""
+    pass); ``states``: the chunk scan of the main workload; ``based16``: the
+    one-pass prefill of the d_h = 16 Based Taylor workload (B=8, H=16,
+    N=8192); ``rebased``: the one-pass prefill of the ReBased workload in the
+    dimension-wise form (B=16, H=8, N=2048); ``copy``: a plain device copy of
+    1 GiB (fp32), whose FETCH_SIZE and WRITE_SIZE readings calibrate the
+    counters against a known byte count."""
     import torch
     import grouped_quadratic_softmax_amd as oal
     import synthetic as S
@@ -250,6 +267,19 @@ def run_pmc_target(args):
         torch.cuda.synchronize()
         print(json.dumps({"pmc_target": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
                           "launches": args.steps}), flush=True)
+        return
+    if args.pmc_target in ("based16", "rebased"):
+        wl = S.make(3 if args.pmc_target == "based16" else 4)
+        q, k, v = device_inputs(wl)
+        p = wl.premap
+        prep = (oal.Prep(p["gamma_q"], p["beta_q"], p["gamma_k"], p["beta_k"], p["ln_eps"])
+                if p is not None else None)
+        pre = oal.PrefillPlan(q, k, v, coeffs_for(wl), prep)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            pre.run()
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": args.pmc_target, "launches": args.steps}), flush=True)
         return
     wl = S.make(2, seq_len=2048 + 1)
     N = wl.seq_len - 1
@@ -308,7 +338,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--pmc-target", choices=("readout", "states", "copy"), default=None,
+    ap.add_argument("--pmc-target", choices=("readout", "states", "based16", "rebased", "copy"), default=None,
                     help="only launch this kernel --steps times (for rocprofv3 counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -52,6 +52,7 @@ _SIGS = {
     "oal_coeffs_from_factor": ([ctypes.c_int32, ctypes.c_int32, ctypes.c_double, _P, _P, _P, _P], ctypes.c_int),
     "oal_check_coeffs": ([_P, _P, _P], ctypes.c_int),
     "oal_fwd_workspace_bytes": ([_P], ctypes.c_size_t),
+    "oal_fwd_workspace_bytes_for": ([_P, _P], ctypes.c_size_t),
     "oal_fwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_fwd_states": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_fwd_outputs": ([_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),

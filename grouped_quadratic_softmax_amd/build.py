@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboal.so")
 
-HIP_SOURCES = ["oal_prefill_d64.hip", "oal_prefill_d32.hip", "oal_prefill_d16.hip", "oal_prefill.hip", "oal_diag.hip",
+HIP_SOURCES = ["oal_prefill_d64.hip", "oal_prefill_d32.hip", "oal_prefill_d16.hip", "oal_prefill.hip", "oal_small.hip",
                "oal_decode.hip", "oal_contrib.hip"]
 HOST_SOURCES = ["oal_api.cpp"]
 
@@ -53,7 +53,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         steps.append([hipcc, *COMMON, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        steps.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        steps.append([hipcc, *COMMON, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, steps):
             if verbose and out.strip():

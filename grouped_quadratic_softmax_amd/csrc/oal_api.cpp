@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/oal.h"
 #include "oal_internal.h"
 #include "oal_layout.h"
@@ -12,6 +14,14 @@
 namespace {
 
 bool supported_dh(int d) { return d == 16 || d == 32 || d == 64; }
+
+// Activations, states and workspaces are read and written with 16-byte
+// vector accesses; a null pointer passes (nullness is checked separately).
+bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (((uintptr_t)p & 15) != 0) return false;
+  return true;
+}
 
 // Common shape checks.  `need_seq` is false for decode.
 int check_dims(const oal_dims* d, bool need_seq) {
@@ -115,6 +125,15 @@ size_t oal_fwd_workspace_bytes(const oal_dims* dims) {
                                  dims->dtype);
 }
 
+size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs) {
+  if (coeffs == nullptr || check_dims(dims, true) != OAL_OK) return 0;
+  const bool diagonal = coeffs->diagonal != 0;
+  if (!oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads))
+    return diagonal ? 0 : oal_fwd_workspace_bytes(dims);
+  return oal::small_workspace_bytes(dims->batch, dims->n_kv_heads, dims->seq_len, dims->d_h, diagonal,
+                                    dims->dtype);
+}
+
 namespace {
 
 // Shared validation and dispatch of oal_fwd and its two stages.
@@ -125,13 +144,16 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   const bool want_states = stages & 1, want_out = stages & 2;
   int st = check_dims(dims, true);
   if (st != OAL_OK) return st;
-  bool diagonal = false;
+  bool diagonal = false, small = false;
   if (want_out) {
     if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
     if ((st = check_coeff_ptrs(coeffs)) != OAL_OK) return st;
     diagonal = coeffs->diagonal != 0;
-    if (diagonal && !want_states) return OAL_ERR_UNSUPPORTED;  // the fused form has no separate stages
-    if (!diagonal && dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
+    // one-call prefill of a small feature space: the dimension-wise form, or
+    // the full space at d_h = 16
+    small = want_states && oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads);
+    if (diagonal && !small) return OAL_ERR_UNSUPPORTED;  // no separate stages for this form
+    if (!small && dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
   }
   if ((st = check_prep(prep)) != OAL_OK) return st;
   if (dims->batch == 0) return OAL_OK;
@@ -147,7 +169,8 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   if (k == nullptr || v == nullptr) return OAL_ERR_INVALID_ARG;
   if (want_out && (q == nullptr || y == nullptr)) return OAL_ERR_INVALID_ARG;
   if (want_states && state_out != nullptr && state_out == state_in) return OAL_ERR_INVALID_ARG;
-  if (!diagonal) {
+  if (!all_aligned16({q, k, v, y, state_in, state_out, workspace})) return OAL_ERR_INVALID_ARG;
+  if (!small) {  // the small path takes any workspace
     const size_t need = oal_fwd_workspace_bytes(dims);
     if (workspace == nullptr || workspace_bytes < need) return OAL_ERR_WORKSPACE;
   }
@@ -166,7 +189,10 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   }
   a.state_in = state_in; a.state_out = state_out; a.y = y; a.workspace = workspace;
   a.diagonal = diagonal;
-  if (diagonal) return oal::launch_fwd_diag(a, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
+  if (small)
+    return oal::launch_fwd_small(a, workspace ? workspace_bytes : 0, (hipStream_t)stream) == hipSuccess
+               ? OAL_OK
+               : OAL_ERR_HIP;
   return oal::launch_fwd(a, stages, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
 }
 
@@ -209,6 +235,7 @@ int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const vo
   if (dims->batch == 0) return OAL_OK;
   if (q == nullptr || k == nullptr || v == nullptr || state == nullptr || y == nullptr)
     return OAL_ERR_INVALID_ARG;
+  if (!all_aligned16({q, k, v, y, state, workspace})) return OAL_ERR_INVALID_ARG;
   const size_t need = oal_decode_workspace_bytes(dims);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return OAL_ERR_WORKSPACE;
   oal::DecodeLaunch a{};
@@ -241,6 +268,7 @@ int oal_contrib(const oal_dims* dims, const void* q, const void* k, const int32_
   if (dims->n_q_heads / dims->n_kv_heads > 16) return OAL_ERR_UNSUPPORTED;
   if (dims->batch < 1 || dims->seq_len < 1) return OAL_ERR_INVALID_ARG;
   if (q == nullptr || k == nullptr || chi_mean == nullptr) return OAL_ERR_INVALID_ARG;
+  if (!all_aligned16({q, k, workspace})) return OAL_ERR_INVALID_ARG;
   const size_t need = oal_contrib_workspace_bytes(dims);
   if (workspace == nullptr || workspace_bytes < need) return OAL_ERR_WORKSPACE;
   oal::ContribLaunch a{};

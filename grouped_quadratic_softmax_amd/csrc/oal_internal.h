@@ -51,8 +51,14 @@ struct ContribLaunch {
 size_t fwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d_h, int dtype);
 // stages: bit 0 = chunk states (scan), bit 1 = outputs (readout)
 hipError_t launch_fwd(const FwdLaunch& a, int stages, hipStream_t stream);
-// dimension-wise form (coefficients with `diagonal`): one fused kernel
-hipError_t launch_fwd_diag(const FwdLaunch& a, hipStream_t stream);
+// Small feature spaces (the dimension-wise form, or the full space at
+// d_h = 16): state kept in one CTA, sequences cut into segments that use the
+// workspace for their sums (one segment without a workspace).
+bool small_path_supported(int d_h, bool diagonal, int Hq, int Hkv);
+size_t small_segment_bytes(int d_h, bool diagonal);
+// workspace that lets the small path use its full number of segments
+size_t small_workspace_bytes(int B, int Hkv, int N, int d_h, bool diagonal, int dtype);
+hipError_t launch_fwd_small(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStream_t stream);
 void decode_slicing(int d_h, long states, int& rows, int& nslice, bool diagonal);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h);

@@ -27,6 +27,9 @@
  *  - Activations are contiguous row-major: q [B, Hq, N, d_h], k [B, Hkv, N,
  *    d_h], v [B, Hkv, N, d_v], y [B, Hq, N, d_v].  q, k, v and y share the
  *    element type `dtype` (OAL_F32: float; OAL_BF16: bfloat16 bits).
+ *    Activations, states and workspaces start on a 16-byte boundary
+ *    (OAL_ERR_INVALID_ARG otherwise): the kernels move them in 16-byte
+ *    vectors.
  *    Coefficients, pre-map parameters and states are always float32.
  *  - Query head h reads KV head h / (Hq / Hkv) (GQA with consecutive query
  *    heads per KV head; the paper's App. B uses the model's native map).
@@ -92,11 +95,12 @@ typedef struct oal_dims {
  * diagonal (the ReBased feature map read as an elementwise square, "Linear
  * Transformers with Learnable Kernel Functions", section on the learnable
  * parabola); off-diagonal entries of c are then ignored and any G <= d_h is
- * accepted.  Its features are [1, k_r, k_r^2] (1 + 2 d_h of them): oal_fwd
- * then needs no workspace (it may be NULL), and oal_fwd and oal_decode_step
- * read and write only the constant, linear and squared-dimension entries of
- * a state (the other entries of state_out are not written).  The two-stage
- * calls oal_fwd_states / oal_fwd_outputs do not support it. */
+ * accepted.  Its features are [1, k_r, k_r^2] (1 + 2 d_h of them); oal_fwd
+ * and oal_decode_step read and write only the constant, linear and
+ * squared-dimension entries of a state (the other entries of state_out are
+ * not written).  Prefill of this form needs Hq / Hkv <= 8 and runs as one
+ * oal_fwd call; the two-stage calls oal_fwd_states / oal_fwd_outputs do not
+ * support it. */
 typedef struct oal_coeffs {
   const int32_t* group_of_dim; /* [Hq, d_h] */
   const float* a;              /* [Hq] */
@@ -144,8 +148,23 @@ int oal_coeffs_from_factor(int32_t n_heads, int32_t n_groups, double eps, const 
  * OAL_OK or OAL_ERR_INVALID_ARG. */
 int oal_check_coeffs(const oal_dims* dims, const int32_t* group_of_dim_host, const float* c_host);
 
-/* Bytes of device workspace oal_fwd needs for `dims` (0 if invalid). */
+/* Bytes of device workspace oal_fwd needs for `dims` (0 if invalid), for
+ * any coefficients; also what oal_fwd_states / oal_fwd_outputs need. */
 size_t oal_fwd_workspace_bytes(const oal_dims* dims);
+
+/* Bytes of device workspace that let oal_fwd run at full parallelism with
+ * coefficients of this kind (only coeffs->diagonal is read; the pointers in
+ * *coeffs are not touched).  0 if invalid, or if none is needed.
+ *
+ * Small feature spaces -- the dimension-wise form at any d_h, and the full
+ * grouped kernel at d_h = 16 (153 features), both with Hq / Hkv <= 8 -- are
+ * prefilled by oal_fwd in one pass that keeps each prefix state on chip and
+ * cuts every sequence into segments; the workspace holds per-segment sums
+ * (an F x 65 fp32 block per segment and batch x KV head).  For these, oal_fwd
+ * accepts any workspace, including none: a smaller one only means fewer
+ * segments (the results are the same up to fp32 rounding order).  For every
+ * other case the figure is oal_fwd_workspace_bytes(dims). */
+size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs);
 
 /* Causal prefill (paper, Eqs. (5)-(6), evaluated chunk by chunk).
  *   q, k, v, y: activations (see conventions); y is written for all N rows.
@@ -154,16 +173,20 @@ size_t oal_fwd_workspace_bytes(const oal_dims* dims);
  *               states, so that a call continues an earlier prefix.
  *   state_out:  NULL or [B, Hkv, oal_state_floats]; receives the states after
  *               the last token (may not alias state_in).
- *   workspace:  device scratch of at least oal_fwd_workspace_bytes(dims);
- *               its contents are undefined after the call.
+ *   workspace:  device scratch of at least oal_fwd_workspace_bytes(dims)
+ *               (for the small feature spaces named above, any size: see
+ *               oal_fwd_workspace_bytes_for); undefined after the call.
  * Calls that share a workspace must be ordered on one stream. */
 int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v,
             const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, float* state_out,
             void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two stages of oal_fwd, for callers that schedule or time them
- * separately.  oal_fwd(...) is exactly oal_fwd_states(...) followed by
- * oal_fwd_outputs(...) on the same stream with the same workspace.
+ * separately.  Outside the small feature spaces (see
+ * oal_fwd_workspace_bytes_for), oal_fwd(...) is exactly oal_fwd_states(...)
+ * followed by oal_fwd_outputs(...) on the same stream with the same
+ * workspace; for the full kernel at d_h = 16 the two give the same results
+ * up to rounding.
  *   oal_fwd_states:  the prefix states of Eq. (5) at every chunk start, kept
  *                    in the workspace (and the final state in state_out).
  *   oal_fwd_outputs: the Eq. (6) readout against those states plus the

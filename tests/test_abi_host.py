@@ -90,6 +90,11 @@ def test_check_coeffs(L):
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
 
 
+def _mis(off):
+    """A fake device pointer off the 16-byte grid."""
+    return ctypes.c_void_p(0x1000 + off)
+
+
 def _fwd(L, dims, coeffs=True, ws=(FAKE, 1 << 40), q=FAKE, y=FAKE, state_in=None, state_out=None, prep=None):
     lib = L.lib()
     cs = L.OalCoeffs(0x1000, 0x1000, 0x1000, 0x1000) if coeffs else None
@@ -119,6 +124,9 @@ def test_fwd_validation_errors(L):
     assert need > 0
     assert _fwd(L, _dims(L), ws=(FAKE, need - 1)) == W
     assert _fwd(L, _dims(L), state_in=FAKE, state_out=FAKE) == E  # aliasing
+    assert _fwd(L, _dims(L), q=_mis(2)) == E                      # 16-byte alignment
+    assert _fwd(L, _dims(L), y=_mis(8)) == E
+    assert _fwd(L, _dims(L), state_out=_mis(4)) == E
     bad_prep = L.OalPrep(0x1000, 0, 0x1000, 0x1000, 1e-5)
     assert _fwd(L, _dims(L), prep=bad_prep) == E
     assert _fwd(L, _dims(L, B=0)) == L.OAL_OK                     # empty batch: nothing enqueued
@@ -159,7 +167,11 @@ def test_decode_and_contrib_validation(L):
     assert need > 0
     assert lib.oal_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(cs), None, FAKE, FAKE, FAKE,
                                ctypes.c_size_t(need - 1), None) == L.OAL_ERR_WORKSPACE
+    assert lib.oal_decode_step(ctypes.byref(d), FAKE, _mis(2), FAKE, ctypes.byref(cs), None, FAKE, FAKE, FAKE,
+                               ctypes.c_size_t(need), None) == L.OAL_ERR_INVALID_ARG
     ws = ctypes.c_size_t(1 << 30)
+    assert lib.oal_contrib(ctypes.byref(d), _mis(8), FAKE, None, None, FAKE, FAKE, ws, None) == \
+        L.OAL_ERR_INVALID_ARG
     assert lib.oal_contrib(ctypes.byref(_dims(L, B=0)), FAKE, FAKE, None, None, FAKE, FAKE, ws, None) == \
         L.OAL_ERR_INVALID_ARG
     assert lib.oal_contrib(ctypes.byref(d), FAKE, FAKE, None, None, None, FAKE, ws, None) == L.OAL_ERR_INVALID_ARG

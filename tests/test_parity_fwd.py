@@ -140,7 +140,7 @@ def test_dimensionwise_form_rejects_two_stage_calls():
     with pytest.raises(oal.OalError) as info:
         plan.outputs()
     assert info.value.status == -2  # OAL_ERR_UNSUPPORTED
-    plan.run()  # one oal_fwd call, no workspace
+    plan.run()  # one oal_fwd call
 
 
 def test_c4_rebased_squared_dot_premap():
@@ -227,6 +227,50 @@ def test_state_out_and_continuation(dtype):
     assert to_np(s_full).shape[-1] == D * 65
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_space_segments(dtype):
+    """d_h = 16 full space through the one-pass small path: the segmented
+    launch (default workspace), one segment (no room for segment sums) and
+    the two-stage chunk path all match the oracle; the final state matches
+    Eq. (5) and carries a continuation across a ragged split."""
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    wl = S.make(3, batch=2, n_q_heads=4, n_kv_heads=2, seq_len=1500, dtype=dtype)
+    co = gpu_coeffs(wl, wl.group_of_dim)
+    q, k, v = to_dev(wl.q, dtype), to_dev(wl.k, dtype), to_dev(wl.v, dtype)
+    a, b, c = oracle_coeffs(wl)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)
+    y_seg, s_seg = oal.fwd(q, k, v, co, return_state=True)
+    tiny = torch.empty(1, dtype=torch.uint8, device="cuda")
+    y_one, s_one = oal.fwd(q, k, v, co, return_state=True, workspace=tiny)
+    plan = oal.PrefillPlan(q, k, v, co)
+    plan.states()
+    plan.outputs()
+    torch.cuda.synchronize()
+    for name, y in (("segments", y_seg), ("one segment", y_one), ("two stages", plan.y)):
+        err = rel_err(to_np(y), ref)
+        log(f"[fwd]   small path {name}: max rel err {err:.3e}")
+        assert err <= TOL[dtype], name
+    n1 = 700
+    y1, s1 = oal.fwd(q[:, :, :n1].contiguous(), k[:, :, :n1].contiguous(), v[:, :, :n1].contiguous(), co,
+                     return_state=True)
+    y2, s2 = oal.fwd(q[:, :, n1:].contiguous(), k[:, :, n1:].contiguous(), v[:, :, n1:].contiguous(), co,
+                     state_in=s1, return_state=True)
+    assert rel_err(np.concatenate([to_np(y1), to_np(y2)], axis=2), ref) <= TOL[dtype]
+    # state bound as in the chunk path's test, with bf16 feature values
+    # (u = 2^-9) in place of fp16 ones
+    u = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -24
+    N = wl.seq_len
+    for bi in range(wl.batch):
+        for kh in range(wl.n_kv_heads):
+            ref_s = O.abi_state_from_matrix(O.state_from_prefix(wl.k[bi, kh], wl.v[bi, kh]))
+            absum = O.abi_state_from_matrix(O.state_from_prefix(np.abs(wl.k[bi, kh]), np.abs(wl.v[bi, kh])))
+            bound = (2 * u + N * 2.0 ** -24) * absum + 2.0 ** -24 * absum.max()
+            for got in (s_seg, s_one, s2, plan.state_out):
+                assert (np.abs(to_np(got)[bi, kh] - ref_s) <= bound).all(), (bi, kh)
+
+
 def test_zero_length_passes_state_through():
     require_gpu()
     import torch
@@ -252,6 +296,13 @@ def test_c2_full_size_sampled():
 def test_c3_full_size_sampled():
     wl = S.make(3)
     _run_case(wl, rows=sample_rows(wl.seq_len, 512, 48, seed=3))
+
+
+def test_c4_full_size_sampled():
+    # ReBased elementwise workload at full size (dimension-wise form, one
+    # fused launch as the benchmark runs it)
+    wl = S.make(4)
+    _run_case(wl, rows=sample_rows(wl.seq_len, 512, 16, seed=4))
 
 
 def test_c5_full_size_sampled():
