@@ -149,8 +149,7 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
     if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
     if ((st = check_coeff_ptrs(coeffs)) != OAL_OK) return st;
     diagonal = coeffs->diagonal != 0;
-    // one-call prefill of a small feature space: the dimension-wise form, or
-    // the full space at d_h = 16
+    // one-call prefill of a small feature space (the dimension-wise form)
     small = want_states && oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads);
     if (diagonal && !small) return OAL_ERR_UNSUPPORTED;  // no separate stages for this form
     if (!small && dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;

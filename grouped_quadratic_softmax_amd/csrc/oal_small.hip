@@ -90,7 +90,7 @@ struct SmallLds {
   static constexpr int FP = SmallSpace<DH, DIAG>::FP;
   static constexpr int FPP = FP + 8;  // row pitch of feature-major tiles
   static constexpr int CP = C + 8;    // row pitch of token-major tiles
-  static constexpr int KH = DH + 4;   // row pitch of k_hat / q_hat (floats)
+  static constexpr int KH = DH + 1;   // row pitch of k_hat / q_hat (floats; odd: no bank conflicts)
   static constexpr long kf = 0;                        // [C][FPP]   phi_K rows
   static constexpr long kft = kf + (long)C * FPP;      // [FP][CP]   phi_K transposed
   static constexpr long qf = kft + (long)FP * CP;      // [C][FPP]   phi_Q rows of one head
@@ -106,6 +106,49 @@ __device__ __forceinline__ uint16_t to_e(float x, uint16_t) { return bf16_bits(x
 __device__ __forceinline__ float to_e(float x, float) { return x; }
 __device__ __forceinline__ Frag<true> dload(const uint16_t* p) { return frag_load(p); }
 __device__ __forceinline__ Frag<false> dload(const float* p) { return frag_load(p); }
+
+// n consecutive elements of T as raw 32-bit words, moved with 16-byte (or,
+// for 8 bytes, one 8-byte) vector loads; p is 8- or 16-byte aligned.
+template <typename T, int n>
+struct RawRow {
+  static constexpr int NW = n * (int)sizeof(T) / 4;
+  static_assert(NW == 2 || NW % 4 == 0, "row part of 8 or 16k bytes");
+  uint32_t w[NW];
+  __device__ __forceinline__ void load(const T* p) {
+    if constexpr (NW == 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0] = x.x;
+      w[1] = x.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW / 4; ++i) {
+        const uint4 x = reinterpret_cast<const uint4*>(p)[i];
+        w[4 * i] = x.x;
+        w[4 * i + 1] = x.y;
+        w[4 * i + 2] = x.z;
+        w[4 * i + 3] = x.w;
+      }
+    }
+  }
+  // element i as float, or 0 when !ok
+  __device__ __forceinline__ float get(int i, bool ok) const {
+    float x;
+    if constexpr (sizeof(T) == 2) x = __uint_as_float(i % 2 ? w[i / 2] & 0xffff0000u : w[i / 2] << 16);
+    else x = __uint_as_float(w[i]);
+    return ok ? x : 0.f;
+  }
+};
+
+// Workgroup barrier for the LDS tiles: waits for this wave's LDS operations
+// only, so global loads issued earlier (the next chunk's rows) stay in flight
+// (__syncthreads() would wait for them too).  The empty asm statements keep
+// the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xf | (7 << 4) | (3 << 14));  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // sum over the TPR consecutive lanes that share a token row (TPR = 4 or 8)
 template <int TPR>
@@ -271,25 +314,21 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
     kft[f * CP + r] = to_e(0.f, E());
   }
 
-  // ---- raw loads of a chunk (one token row part per thread) ----
+  // ---- raw loads of a chunk (one token row part per thread); rows past the
+  // segment or the sequence read row 0 (in bounds) and are zeroed on use ----
   struct Raw {
-    float kx[QD], qx[QD], vx[VD];
+    RawRow<T, QD> k, q;
+    RawRow<T, VD> v;
+    bool ok;
   };
   auto fetch = [&](int c) __attribute__((always_inline)) {
     Raw r;
     const int row = c * C + srow;
-    const bool ok = c < c_end && row < N;
-    const long rr = ok ? row : 0;
-    const T* kp = k + ((long)bh * N + rr) * DH + sq * QD;
-    const T* vp = v + ((long)bh * N + rr) * DV + sq * VD;
-    const T* qp = q + ((long)(b * Hq + kvh * R) * N + rr) * DH + sq * QD;
-#pragma unroll
-    for (int i = 0; i < QD; ++i) {
-      r.kx[i] = ok ? to_f32(kp[i]) : 0.f;
-      r.qx[i] = (OUT && ok) ? to_f32(qp[i]) : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < VD; ++i) r.vx[i] = ok ? to_f32(vp[i]) : 0.f;
+    r.ok = c < c_end && row < N;
+    const long rr = r.ok ? row : 0;
+    r.k.load(k + ((long)bh * N + rr) * DH + sq * QD);
+    r.v.load(v + ((long)bh * N + rr) * DV + sq * VD);
+    if (OUT) r.q.load(q + ((long)(b * Hq + kvh * R) * N + rr) * DH + sq * QD);
     return r;
   };
   // Features of the chunk from this thread's pre-mapped values x: phi_K
@@ -314,16 +353,25 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
     if constexpr (!DIAG) {
 #pragma unroll
       for (int i = 0; i < QD; ++i) hat[srow * KH + sq * QD + i] = x[i];
-      __syncthreads();
+      lds_sync();
+      // pair f = 1 + DH + p is (r, t), p-th in row-major upper-triangle
+      // order; this thread takes p = fg, fg + NFG, ... (wave-uniform)
       constexpr int NFG = 256 / C;
       const int row = tid % C, fg = tid / C;
+      int r = 0, t = fg;
       for (int f = 1 + DH + fg; f < F0; f += NFG) {
-        const int r = space_dev<DH, DIAG>.r[f], t = space_dev<DH, DIAG>.t[f];
         const E pv = to_e((coef ? coef[f] : 1.f) * hat[row * KH + r] * hat[row * KH + t], E());
         if (rows) rows[row * FPP + f] = pv;
         if (cols) cols[f * CP + row] = pv;
+        t += NFG;
+        // past the end of row r: continue on the diagonal of row r + 1 (stops
+        // at r = DH, after the last pair)
+        while (t >= DH && r < DH) {
+          ++r;
+          t += r - DH;
+        }
       }
-      __syncthreads();  // hat is rewritten by the next staging
+      lds_sync();  // hat is rewritten by the next staging
     }
   };
 
@@ -335,7 +383,7 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
     {
       float kx[QD];
 #pragma unroll
-      for (int i = 0; i < QD; ++i) kx[i] = cur.kx[i];
+      for (int i = 0; i < QD; ++i) kx[i] = cur.k.get(i, cur.ok);
       if (PREMAP) premap_row<DH, TPR, QD>(kx, kvh * DH + sq * QD, gamma_k, beta_k, ln_eps, okrow);
       feats(kx, OUT ? kf : nullptr, kft, nullptr);  // kernel 1 needs only the transposed tile
       if (sq == 0) {
@@ -345,10 +393,10 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
         vt[DV * CP + srow] = one;
       }
 #pragma unroll
-      for (int i = 0; i < VD; ++i) vt[(sq * VD + i) * CP + srow] = to_e(cur.vx[i], E());
+      for (int i = 0; i < VD; ++i) vt[(sq * VD + i) * CP + srow] = to_e(cur.v.get(i, cur.ok), E());
     }
     Raw nxt = fetch(c + 1);  // in flight during this chunk
-    __syncthreads();
+    lds_sync();
     // ---- snapshot S (before this chunk), transposed, for the readout ----
     if (OUT) {
 #pragma unroll
@@ -383,23 +431,24 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
     if (OUT) {
       for (int hh = 0; hh < R; ++hh) {
         const int h = kvh * R + hh;
-        __syncthreads();  // snapshot written; previous head done with qf
+        lds_sync();  // snapshot written; previous head done with qf
         // ---- phi_Q rows of the head ----
         {
           float qx[QD];
           if (hh == 0) {
 #pragma unroll
-            for (int i = 0; i < QD; ++i) qx[i] = cur.qx[i];
+            for (int i = 0; i < QD; ++i) qx[i] = cur.q.get(i, cur.ok);
           } else {
-            const T* qp = q + ((long)(b * Hq + h) * N + j0 + (okrow ? srow : 0)) * DH + sq * QD;
+            RawRow<T, QD> qr;
+            qr.load(q + ((long)(b * Hq + h) * N + j0 + (okrow ? srow : 0)) * DH + sq * QD);
 #pragma unroll
-            for (int i = 0; i < QD; ++i) qx[i] = okrow ? to_f32(qp[i]) : 0.f;
+            for (int i = 0; i < QD; ++i) qx[i] = qr.get(i, okrow);
           }
           if (PREMAP) premap_row<DH, TPR, QD>(qx, h * DH + sq * QD, gamma_q, beta_q, ln_eps, okrow);
           feats(qx, qf, nullptr, coefq[hh]);
           if (sq == 0) qf[srow * FPP] = to_e(okrow ? coefq[hh][0] : 0.f, E());
         }
-        __syncthreads();
+        lds_sync();
         for (int rt = wave; rt < RT; rt += 4) {
           // ---- inter: phi_Q S (S before this chunk) ----
           f32x4 yacc[5];
@@ -472,7 +521,7 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
         }
       }
     }
-    __syncthreads();  // every tile of this chunk consumed
+    lds_sync();  // every tile of this chunk consumed
     cur = nxt;
   }
 
@@ -565,7 +614,8 @@ size_t small_workspace_bytes(int B, int Hkv, int N, int d_h, bool diagonal, int 
 }
 
 bool small_path_supported(int d_h, bool diagonal, int Hq, int Hkv) {
-  return Hq / Hkv <= 8 && (diagonal || d_h == 16);
+  (void)d_h;
+  return Hq / Hkv <= 8 && diagonal;
 }
 
 hipError_t launch_fwd_small(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream) {

@@ -150,9 +150,11 @@ def fwd(q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None, ret
     if return_state and state_out is None:
         state_out = torch.empty((B, Hkv, sf), dtype=torch.float32, device=q.device)
     cs = coeffs.struct()
-    nbytes = int(L.lib().oal_fwd_workspace_bytes_for(ctypes.byref(dims), ctypes.byref(cs)))
-    if workspace is None or workspace.numel() < nbytes:
+    if workspace is None:  # a caller's workspace is passed as given
+        nbytes = int(L.lib().oal_fwd_workspace_bytes_for(ctypes.byref(dims), ctypes.byref(cs)))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _dev(workspace, "workspace", torch.uint8)
     ps = prep.struct() if prep is not None else None
     st = L.lib().oal_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
                          ctypes.byref(ps) if ps is not None else None, _ptr(state_in), _ptr(state_out),
@@ -219,10 +221,9 @@ def contrib(q, k, seq_lens=None, per_prompt=False, workspace=None):
 class PrefillPlan:
     """Pre-marshalled oal_fwd arguments for repeated calls on fixed buffers.
 
-    ``states()`` and ``outputs()`` enqueue the two stages of oal_fwd on the
-    stream that is current at construction time; ``run()`` enqueues both, or
-    one oal_fwd call for the small feature spaces (d_h = 16, or coefficients
-    in the dimension-wise form, which have no separate stages).
+    ``run()`` enqueues one oal_fwd call on the stream that is current at
+    construction time; ``states()`` and ``outputs()`` enqueue its two stages
+    separately (not available for coefficients in the dimension-wise form).
     """
 
     def __init__(self, q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None,
@@ -242,7 +243,6 @@ class PrefillPlan:
         if not coeffs.diagonal:  # the two stages need the full workspace
             nbytes = max(nbytes, int(lib.oal_fwd_workspace_bytes(ctypes.byref(self.dims))))
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-        self._one_call = coeffs.diagonal or (d == 16 and Hq // Hkv <= 8)
         self._ps = prep.struct() if prep is not None else None
         pp = ctypes.byref(self._ps) if self._ps is not None else None
         ws = (_ptr(self.workspace), ctypes.c_size_t(self.workspace.numel()))
@@ -262,11 +262,7 @@ class PrefillPlan:
         L.check(self._lib.oal_fwd_outputs(*self._out_args), "oal_fwd_outputs")
 
     def run(self):
-        if self._one_call:
-            L.check(self._lib.oal_fwd(*self._fwd_args), "oal_fwd")
-        else:
-            self.states()
-            self.outputs()
+        L.check(self._lib.oal_fwd(*self._fwd_args), "oal_fwd")
         return self.y
 
 

@@ -156,14 +156,13 @@ size_t oal_fwd_workspace_bytes(const oal_dims* dims);
  * coefficients of this kind (only coeffs->diagonal is read; the pointers in
  * *coeffs are not touched).  0 if invalid, or if none is needed.
  *
- * Small feature spaces -- the dimension-wise form at any d_h, and the full
- * grouped kernel at d_h = 16 (153 features), both with Hq / Hkv <= 8 -- are
- * prefilled by oal_fwd in one pass that keeps each prefix state on chip and
- * cuts every sequence into segments; the workspace holds per-segment sums
- * (an F x 65 fp32 block per segment and batch x KV head).  For these, oal_fwd
- * accepts any workspace, including none: a smaller one only means fewer
- * segments (the results are the same up to fp32 rounding order).  For every
- * other case the figure is oal_fwd_workspace_bytes(dims). */
+ * The small feature space of the dimension-wise form (1 + 2 d_h features,
+ * Hq / Hkv <= 8) is prefilled by oal_fwd in one pass that keeps each prefix
+ * state on chip and cuts every sequence into segments; the workspace holds
+ * per-segment sums (an F x 65 fp32 block per segment and batch x KV head).
+ * There oal_fwd accepts any workspace, including none: a smaller one only
+ * means fewer segments (the results are the same up to fp32 rounding
+ * order).  For every other case the figure is oal_fwd_workspace_bytes(dims). */
 size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs);
 
 /* Causal prefill (paper, Eqs. (5)-(6), evaluated chunk by chunk).
@@ -174,7 +173,7 @@ size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeff
  *   state_out:  NULL or [B, Hkv, oal_state_floats]; receives the states after
  *               the last token (may not alias state_in).
  *   workspace:  device scratch of at least oal_fwd_workspace_bytes(dims)
- *               (for the small feature spaces named above, any size: see
+ *               (for the dimension-wise form, any size: see
  *               oal_fwd_workspace_bytes_for); undefined after the call.
  * Calls that share a workspace must be ordered on one stream. */
 int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v,
@@ -182,11 +181,9 @@ int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v,
             void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two stages of oal_fwd, for callers that schedule or time them
- * separately.  Outside the small feature spaces (see
- * oal_fwd_workspace_bytes_for), oal_fwd(...) is exactly oal_fwd_states(...)
- * followed by oal_fwd_outputs(...) on the same stream with the same
- * workspace; for the full kernel at d_h = 16 the two give the same results
- * up to rounding.
+ * separately.  oal_fwd(...) is exactly oal_fwd_states(...) followed by
+ * oal_fwd_outputs(...) on the same stream with the same workspace (the
+ * dimension-wise form has no separate stages).
  *   oal_fwd_states:  the prefix states of Eq. (5) at every chunk start, kept
  *                    in the workspace (and the final state in state_out).
  *   oal_fwd_outputs: the Eq. (6) readout against those states plus the

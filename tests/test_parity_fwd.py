@@ -95,6 +95,31 @@ def test_dimensionwise_form(d, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dimensionwise_one_segment_matches(dtype):
+    """Without room for segment sums the one-pass path walks each sequence in
+    one segment; outputs and state still match the oracle."""
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    wl = _diag_workload(32, dtype, seed=11, N=700)
+    co = gpu_coeffs(wl, wl.group_of_dim)
+    q, k, v = to_dev(wl.q, dtype), to_dev(wl.k, dtype), to_dev(wl.v, dtype)
+    a, b, c = oracle_coeffs(wl)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)
+    y_seg, s_seg = oal.fwd(q, k, v, co, return_state=True)
+    y_one, s_one = oal.fwd(q, k, v, co, return_state=True,
+                           workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    for y in (y_seg, y_one):
+        assert rel_err(to_np(y), ref) <= TOL[dtype]
+    touched = diag_form_mask(32, 64)
+    ref_s = np.stack([[O.abi_state_from_matrix(O.state_from_prefix(wl.k[bi, kh], wl.v[bi, kh]))
+                       for kh in range(wl.n_kv_heads)] for bi in range(wl.batch)])
+    scale = np.abs(ref_s).max()
+    for s_ in (s_seg, s_one):
+        assert np.abs(to_np(s_)[..., touched] - ref_s[..., touched]).max() <= 1e-2 * scale
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_dimensionwise_state_and_continuation(dtype):
     require_gpu()
     import torch
@@ -228,11 +253,11 @@ def test_state_out_and_continuation(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_small_space_segments(dtype):
-    """d_h = 16 full space through the one-pass small path: the segmented
-    launch (default workspace), one segment (no room for segment sums) and
-    the two-stage chunk path all match the oracle; the final state matches
-    Eq. (5) and carries a continuation across a ragged split."""
+def test_d16_workspace_sizes_stages_and_state(dtype):
+    """d_h = 16 full space: oal_fwd with its default workspace and with a
+    minimal one (refused by the chunk path, fewer segments on a one-pass
+    path) and the two-stage calls all match the oracle; the final state
+    matches Eq. (5) and carries a continuation across a ragged split."""
     require_gpu()
     import torch
     import grouped_quadratic_softmax_amd as oal
@@ -243,7 +268,11 @@ def test_small_space_segments(dtype):
     ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)
     y_seg, s_seg = oal.fwd(q, k, v, co, return_state=True)
     tiny = torch.empty(1, dtype=torch.uint8, device="cuda")
-    y_one, s_one = oal.fwd(q, k, v, co, return_state=True, workspace=tiny)
+    try:
+        y_one, s_one = oal.fwd(q, k, v, co, return_state=True, workspace=tiny)
+    except oal.OalError as e:
+        assert e.status == -3  # OAL_ERR_WORKSPACE
+        y_one, s_one = y_seg, s_seg
     plan = oal.PrefillPlan(q, k, v, co)
     plan.states()
     plan.outputs()
