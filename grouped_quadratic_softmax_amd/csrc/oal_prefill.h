@@ -129,6 +129,15 @@ __device__ __forceinline__ void frag_st(float* p, const float (&x)[8]) {
   reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
 }
 
+// x, hidden from the optimiser when ON (an empty asm that "modifies" it), so
+// that values derived from it are recomputed where they are used instead of
+// being hoisted and kept live in registers.
+template <bool ON>
+__device__ __forceinline__ int opaque(int x) {
+  if constexpr (ON) asm volatile("" : "+v"(x));
+  return x;
+}
+
 // s_waitcnt immediate that waits for vector-memory count <= n (other counters
 // untouched): vmcnt in bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15.
 template <int n>
@@ -710,7 +719,13 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
   const int c = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int R = Hq / Hkv;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  // Builds with eight head slots run short of registers: there the wave
+  // index is made scalar and the lanes' LDS offsets are recomputed per stage
+  // (values hidden from loop-invariant hoisting), which keeps every spill
+  // out of the stage loop.  Smaller builds keep the offsets live.
+  constexpr bool kTight = RMAX >= 8;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = kTight ? __builtin_amdgcn_readfirstlane(tid / kWave) : tid / kWave;
   const int lg = lane / 16, l16 = lane % 16;
   const int rt = wave % 4, kpar = wave / 4;  // row tile, head class
   const int j0 = c * C;
@@ -752,23 +767,25 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
   typedef const __attribute__((address_space(1))) void gbl_void;
   auto issue = [&](int sg, int buf) __attribute__((always_inline)) {
     E* dst = bst + (long)buf * SE;
+    const int tid_o = opaque<kTight>(tid);
+    const int lane_o = tid_o % kWave, wave_o = tid_o / kWave;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int w = tid + NT * i;                 // LDS vector of this lane
+      const int w = tid_o + NT * i;               // LDS vector of this lane
       const int slot = w / VPB, wl = w % VPB;
       const int pu = wl / VH, half = wl % VH;
       const int col = pu / 4, pp = pu % 4;
       const int part = (pp - col / 2 - col / 8) & 3;
       const E* src = sv0 + (long)kb_at(sg, slot) * DV * 32 + ((4 * col + part) * VH + half) * VE;
-      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(dst + (long)(w - lane) * VE), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)(dst + (long)(w - lane_o) * VE), 16, 0, 0);
     }
     // z vectors: lanes < ZV of wave 0; every other wave issues the same
     // instruction with only lane 0 live, into its own 16-byte dummy slot, so
     // that all waves count the same number of outstanding loads
-    if (lane < (wave == 0 ? ZV : 1)) {
-      const int slot = lane / (32 / VE), part = lane % (32 / VE);
+    if (lane_o < (wave_o == 0 ? ZV : 1)) {
+      const int slot = lane_o / (32 / VE), part = lane_o % (32 / VE);
       const E* src = sz0 + (long)kb_at(sg, slot) * 32 + part * VE;
-      void* zd = wave == 0 ? (void*)(dst + KG * DV * 32) : (void*)&zdummy[wave][0];
+      void* zd = wave_o == 0 ? (void*)(dst + KG * DV * 32) : (void*)&zdummy[wave_o][0];
       __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)zd, 16, 0, 0);
     }
   };
@@ -1103,21 +1120,40 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
 
     // ---- inter-chunk read: phi_q(Q_c) . S_c ----
     if (inter) {
-      auto load_b = [&](F (&Bf)[5], int buf, int slot) __attribute__((always_inline)) {
+      // The lane's LDS offsets, recomputed at the start of every stage in
+      // tight builds (a few integer operations).
+      struct LaneOff {
+        int row;      // A-operand row of the lane
+        int lgo;      // lane group
+        int b[4];     // B fragments of value columns 16 n + l16 (swizzled)
+        bool zlane;   // the lane that carries the normaliser column
+      };
+      auto lane_offsets = [&]() __attribute__((always_inline)) {
+        const int ln = opaque<kTight>(lane);
+        LaneOff o;
+        o.row = 16 * rt + ln % 16;
+        o.lgo = ln / 16;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) o.b[n] = swz(16 * n + ln % 16, ln / 16);
+        o.zlane = ln % 16 == 0;
+        return o;
+      };
+      auto load_b = [&](F (&Bf)[5], int buf, int slot, const LaneOff& o) __attribute__((always_inline)) {
         const E* bp = bst + (long)buf * SE + slot * DV * 32;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) frag_ld(Bf[n], bp + swz(16 * n + l16, lg));
-        if (l16 == 0) frag_ld(Bf[4], bst + (long)buf * SE + KG * DV * 32 + slot * 32 + 8 * lg);
+        for (int n = 0; n < 4; ++n) frag_ld(Bf[n], bp + o.b[n]);
+        if (o.zlane) frag_ld(Bf[4], bst + (long)buf * SE + KG * DV * 32 + slot * 32 + 8 * o.lgo);
         else frag_zero(Bf[4]);
       };
       // linear K-blocks: (q_u ks) coef; their row factor 2^-f (the row's
       // "one") is applied when the partial sums are rescaled
       auto compute_lin = [&](int buf) __attribute__((always_inline)) {
+        const LaneOff lo = lane_offsets();
 #pragma unroll
         for (int slot = 0; slot < NL; ++slot) {
           const int kk = NQ + slot;
           F Bf[5];
-          load_b(Bf, buf, slot);
+          load_b(Bf, buf, slot, lo);
           const int u0 = 32 * slot + 8 * lg;
           const int uo = u0 < DH ? u0 : 0;  // padding features have zero coefficients
 #pragma unroll
@@ -1151,12 +1187,13 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
         }
       };
       auto compute_quad = [&](int sg, int buf) __attribute__((always_inline)) {
+        const LaneOff lo = lane_offsets();
 #pragma unroll 1
         for (int slot = 0; slot < KG; ++slot) {
           const bool live = slot_live(sg, slot);
           const int kk = live ? kb_at(sg, slot) : KB;  // KB: the zero block
           F Bf[5];
-          load_b(Bf, buf, slot);
+          load_b(Bf, buf, slot, lo);
           int rb1 = prb, tb1 = ptb;
           next_pair(rb1, tb1);
           // a padding slot reads row offset 0 (finite values times zero coefficients)
@@ -1166,9 +1203,9 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
           ptb = tb1;
           next_pair(prb, ptb);
           // head slot HS j + kpar sits HS j whole blocks after slot kpar
-          const E* qr = qh + ((long)kpar * C + row) * DHP + r0;
-          const E* qt = qh + ((long)kpar * C + row) * DHP + t0;
-          const E* cb = coef + ((long)kpar * (KB + 1) + kk) * 32 + 8 * lg;
+          const E* qr = qh + ((long)kpar * C + lo.row) * DHP + r0;
+          const E* qt = qh + ((long)kpar * C + lo.row) * DHP + t0;
+          const E* cb = coef + ((long)kpar * (KB + 1) + kk) * 32 + 8 * lo.lgo;
 #pragma unroll
           for (int j = 0; j < HOWN; ++j) {
             const E* qrow = qh + ((long)(HS * j + kpar) * C + row) * DHP;
