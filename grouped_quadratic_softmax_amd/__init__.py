@@ -5,7 +5,7 @@ this package is its thin torch binding plus host-side grouping utilities.
 """
 
 from ._lib import OalError, lib  # noqa: F401
-from .grouping import groups_from_contribution  # noqa: F401
+from .grouping import bootstrap_indices, group_dims, group_dims_budget, groups_from_contribution  # noqa: F401
 from .ops import (  # noqa: F401
     Coeffs,
     ContribPlan,

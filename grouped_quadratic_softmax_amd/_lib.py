@@ -35,6 +35,11 @@ class OalPrep(ctypes.Structure):
                 ("beta_k", ctypes.c_void_p), ("ln_eps", ctypes.c_float)]
 
 
+class OalGroupParams(ctypes.Structure):
+    _fields_ = [("alpha", ctypes.c_double), ("gamma", ctypes.c_double), ("tau", ctypes.c_double),
+                ("eps", ctypes.c_double), ("g_min", ctypes.c_int32)]
+
+
 class OalError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
@@ -60,6 +65,8 @@ _SIGS = {
     "oal_decode_step": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_contrib_workspace_bytes": ([_P], ctypes.c_size_t),
     "oal_contrib": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "oal_group_dims": ([ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
+    "oal_group_dims_budget": ([ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_double, _P], ctypes.c_int),
 }
 
 

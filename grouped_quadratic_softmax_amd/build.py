@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "liboal.so")
 
 HIP_SOURCES = ["oal_prefill_d64.hip", "oal_prefill_d32.hip", "oal_prefill_d16.hip", "oal_prefill.hip", "oal_small.hip",
                "oal_decode.hip", "oal_contrib.hip"]
-HOST_SOURCES = ["oal_api.cpp"]
+HOST_SOURCES = ["oal_api.cpp", "oal_grouping.cpp"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", CSRC]

@@ -234,6 +234,51 @@ int oal_contrib(const oal_dims* dims, const void* q, const void* k, const int32_
                 float* chi_per_prompt, float* chi_mean, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/* ---- dimension grouping (host functions; every pointer below is HOST) ---- */
+
+/* Settings of the outlier-aware grouping (paper, App. B, "Grouping
+ * settings"): tail fraction alpha, minimum bootstrap support gamma, gap
+ * threshold tau (1.5 in the paper), division guard eps (> 0), and the
+ * minimum group count g_min (2 in the paper). */
+typedef struct oal_group_params {
+  double alpha;
+  double gamma;
+  double tau;
+  double eps;
+  int32_t g_min;
+} oal_group_params;
+
+/* Outlier-aware grouping of one query head's dimensions (paper, App. B,
+ * "Dimension grouping"; the bootstrap separation R_k^(b) as defined on the
+ * discussion deck's backup slide on bootstrap support).
+ *   chi_pp [P, d_h]: per-prompt contribution scores chi_{p,r} (>= 0, finite),
+ *                    e.g. one head's rows of oal_contrib's chi_per_prompt.
+ *   boot [B, P]:     prompt indices in [0, P) of B >= 1 bootstrap replicates,
+ *                    drawn by the caller with replacement (repeats count).
+ *   group_of_dim [d_h] (out): group ids 0..G-1; group 0 is the
+ *                    low-contribution bulk, higher ids refine the tail.
+ *   rho, support [d_h] (out, each may be NULL): for every candidate cut k
+ *                    (entry k), the gap ratio rho_k and the bootstrap
+ *                    support S_k; NaN at positions that are not candidates.
+ * Steps: chi_r = mean over prompts; stable ascending order pi; candidate
+ * cuts k = max(1, d_h - ceil(alpha d_h)) .. d_h - 1 (a cut at k separates
+ * sorted positions 1..k from k+1..d_h); rho_k = chi_{pi_{k+1}} /
+ * max(chi_{pi_k}, eps); S_k = fraction of replicates whose bootstrap scores
+ * (mean over the sampled prompts, pi fixed) keep min(upper) / max(max(lower),
+ * eps) >= tau; natural cuts have rho_k >= tau and S_k >= gamma; below g_min
+ * groups, unused candidates are added by descending (S_k, rho_k), ties in
+ * candidate order.  All arithmetic is fp64 in a fixed order.
+ * Returns G >= 1, or OAL_ERR_INVALID_ARG. */
+int oal_group_dims(int32_t d_h, int32_t P, const float* chi_pp, int32_t B, const int32_t* boot,
+                   const oal_group_params* params, int32_t* group_of_dim, double* rho, double* support);
+
+/* Fixed-budget grouping (paper, App. B, "Group-budget diagnostic"): the
+ * n_groups - 1 largest adjacent gaps rho_k (k = 1..d_h-1, as above) of the
+ * stably sorted profile chi [d_h] become the boundaries; equal gaps are taken
+ * in cut order.  group_of_dim [d_h] (out) as above; 1 <= n_groups <= d_h.
+ * Returns n_groups, or OAL_ERR_INVALID_ARG. */
+int oal_group_dims_budget(int32_t d_h, const float* chi, int32_t n_groups, double eps, int32_t* group_of_dim);
+
 #ifdef __cplusplus
 }
 #endif

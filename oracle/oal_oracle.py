@@ -70,6 +70,8 @@ __all__ = [
     "chi_separable",
     "abi_state_from_matrix",
     "matrix_from_abi_state",
+    "group_dims_bootstrap",
+    "group_dims_budget",
 ]
 
 
@@ -434,3 +436,104 @@ def chi_separable(Q, K, lengths=None):
             pre = np.cumsum(np.abs(K[p, kh, :n]), axis=0)
             per[p, h] = (np.abs(Q[p, h, :n]) * pre).sum(axis=0) / (math.sqrt(d) * npairs)
     return per, per.mean(axis=0)
+
+
+# --------------------------------------------------------------------------
+# outlier-aware dimension grouping ([OAL] App. B, "Dimension grouping")
+# --------------------------------------------------------------------------
+
+def _sorted_order(chi):
+    """pi: dimension indices by ascending chi, ties kept in index order (a
+    stable sort, [OAL] App. B)."""
+    return sorted(range(len(chi)), key=lambda r: chi[r])
+
+
+def _groups_from_cuts(pi, cuts):
+    """Group id of every dimension for retained cuts k_1 < ... < k_{G-1}:
+    group g (0-based) holds sorted positions k_{g-1}+1 .. k_g (1-based
+    positions, k_0 = 0, k_G = d_h), mapped back to dimension indices."""
+    d = len(pi)
+    bounds = [0] + sorted(cuts) + [d]
+    gid = [0] * d
+    for g in range(len(bounds) - 1):
+        for pos in range(bounds[g], bounds[g + 1]):
+            gid[pi[pos]] = g
+    return gid
+
+
+def group_dims_bootstrap(chi_pp, boot, alpha, gamma, tau=1.5, g_min=2, eps=1e-12):
+    """Outlier-aware grouping of one query head ([OAL] App. B).
+
+    chi_pp: [P][d] per-prompt contribution scores chi_{p,r} (Eq. (2)).
+    boot:   [B][P] prompt indices of the B bootstrap replicates (drawn with
+            replacement by the caller; repeated indices count repeatedly).
+    Steps, in the appendix's order:
+      1. chi_r = equal-weight mean over prompts; pi = stable ascending order.
+      2. m = ceil(alpha d); candidate cuts k = d - m .. d - 1 (and k >= 1), a
+         cut at k separating sorted positions 1..k from k+1..d.
+      3. rho_k = chi_{pi_{k+1}} / max(chi_{pi_k}, eps).
+      4. per replicate b, chi^(b) = mean of chi_p over the sampled prompts (pi
+         kept fixed); R_k^(b) = min over the upper side of chi^(b) / max(max
+         over the lower side of chi^(b), eps) (the deck's backup slide on
+         bootstrap support); S_k = fraction of replicates with R_k^(b) >= tau.
+      5. natural cuts: rho_k >= tau and S_k >= gamma.
+      6. fewer than g_min groups: add unused candidates in descending
+         lexicographic order of (S_k, rho_k), ties in candidate order, until
+         g_min groups or no candidate is left.
+      7. groups = contiguous runs of the sorted order between the cuts.
+    Returns (group id per dimension, G, {k: rho_k}, {k: S_k}), in fp64.
+    """
+    P = len(chi_pp)
+    d = len(chi_pp[0])
+    chi = []
+    for r in range(d):
+        tot = 0.0
+        for p in range(P):
+            tot += float(chi_pp[p][r])
+        chi.append(tot / P)
+    pi = _sorted_order(chi)
+    m = math.ceil(alpha * d)
+    cands = [k for k in range(d - m, d) if k >= 1]
+    rho, sup = {}, {}
+    for k in cands:
+        rho[k] = chi[pi[k]] / max(chi[pi[k - 1]], eps)  # 1-based pi_{k+1} / pi_k
+    counts = {k: 0 for k in cands}
+    for idx in boot:
+        chib = []
+        for r in range(d):
+            tot = 0.0
+            for i in idx:
+                tot += float(chi_pp[int(i)][r])
+            chib.append(tot / len(idx))
+        for k in cands:
+            lo = max(chib[pi[pos]] for pos in range(k))
+            up = min(chib[pi[pos]] for pos in range(k, d))
+            if up / max(lo, eps) >= tau:
+                counts[k] += 1
+    for k in cands:
+        sup[k] = counts[k] / len(boot)
+    cuts = [k for k in cands if rho[k] >= tau and sup[k] >= gamma]
+    if len(cuts) + 1 < g_min:
+        rest = [k for k in cands if k not in cuts]
+        rest = sorted(rest, key=lambda k: (-sup[k], -rho[k]))  # stable: ties in candidate order
+        for k in rest:
+            if len(cuts) + 1 >= g_min:
+                break
+            cuts.append(k)
+    gid = _groups_from_cuts(pi, cuts)
+    return gid, len(cuts) + 1, rho, sup
+
+
+def group_dims_budget(chi, n_groups, eps=1e-12):
+    """Fixed-budget grouping ([OAL] App. B, "Group-budget diagnostic"): the
+    G - 1 largest adjacent gaps of the stably sorted profile become the
+    boundaries.  The gap at cut k is the appendix's adjacent contribution gap
+    rho_k = chi_{pi_{k+1}} / max(chi_{pi_k}, eps), over every k = 1..d-1;
+    equal gaps are taken in cut order.  Returns (group id per dimension, rho)."""
+    d = len(chi)
+    chi = [float(x) for x in chi]
+    pi = _sorted_order(chi)
+    rho = {k: chi[pi[k]] / max(chi[pi[k - 1]], eps) for k in range(1, d)}
+    order = sorted(range(1, d), key=lambda k: -rho[k])  # stable
+    cuts = order[:n_groups - 1]
+    return _groups_from_cuts(pi, cuts), rho

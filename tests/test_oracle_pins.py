@@ -376,3 +376,76 @@ def test_chi_gaussian_expectation():
     P, H, N, d = 4, 2, 400, 16
     _, m = O.chi_separable(_rand(rng, P, H, N, d), _rand(rng, P, H, N, d))
     assert abs(m.mean() - (2 / math.pi) / math.sqrt(d)) < 0.03 * (2 / math.pi) / math.sqrt(d)
+
+
+# ---------------------------------------------------------------- grouping
+# Hand-worked cases of the outlier-aware grouping ([OAL] App. B; the
+# bootstrap separation R_k^(b) of the deck's backup slide on bootstrap
+# support).  Expected partitions, gap ratios and supports are derived in the
+# comments, not by the oracle's own arithmetic.
+
+def test_grouping_stable_outliers_become_tail_groups():
+    # means: dims 0..5 ~ 1, dim 6 = 10, dim 7 = 30; alpha = 0.25 -> m = 2,
+    # candidate cuts k = 6, 7.  rho_6 = 10 / 1, rho_7 = 30 / 10 = 3.  In every
+    # replicate min(dims 6, 7) / max(dims 0..5) >= 9 / 1.1 and dim 7 / max(dims
+    # 0..6) >= 89/3 / (31/3) > 2.8, so S_6 = S_7 = 1: both cuts are natural.
+    chi_pp = [[1, 1, 1, 1, 1, 1, 10, 30], [1.1, 0.9, 1, 1, 1, 1, 11, 29], [0.9, 1.1, 1, 1, 1, 1, 9, 31]]
+    boot = [[0, 1, 2], [0, 0, 1], [2, 2, 2], [1, 2, 0]]
+    gid, G, rho, sup = O.group_dims_bootstrap(chi_pp, boot, alpha=0.25, gamma=0.9)
+    assert gid == [0, 0, 0, 0, 0, 0, 1, 2] and G == 3
+    assert sorted(rho) == [6, 7]
+    assert rho[6] == pytest.approx(10.0, rel=1e-12) and rho[7] == pytest.approx(3.0, rel=1e-12)
+    assert sup == {6: 1.0, 7: 1.0}
+
+
+def test_grouping_unstable_gap_is_not_a_natural_cut():
+    # dim 3 is large only in prompt 0: mean 28.1875 against dim 2 = 4, so
+    # rho_3 = 7.046875 >= tau, but the replicates that miss prompt 0 see
+    # 4.25 / 4 < 1.5: S_3 = 2/4 < gamma.  The cut k = 2 (dims {0,1} | {2,3})
+    # has rho_2 = 4 / 2 = 2 and R_2 = 4 / 2 in every replicate: natural.
+    chi_pp = [[1, 2, 4, 100], [1, 2, 4, 4.25], [1, 2, 4, 4.25], [1, 2, 4, 4.25]]
+    boot = [[0, 0, 1, 2], [1, 2, 3, 1], [1, 1, 2, 3], [0, 1, 2, 3]]
+    gid, G, rho, sup = O.group_dims_bootstrap(chi_pp, boot, alpha=0.5, gamma=0.9)
+    assert gid == [0, 0, 1, 1] and G == 2
+    assert rho == {2: 2.0, 3: 28.1875 / 4}
+    assert sup == {2: 1.0, 3: 0.5}
+    # with three groups required, the remaining candidate is added
+    gid3, G3, _, _ = O.group_dims_bootstrap(chi_pp, boot, alpha=0.5, gamma=0.9, g_min=3)
+    assert gid3 == [0, 0, 1, 2] and G3 == 3
+
+
+def test_grouping_flat_profile_falls_back_to_first_candidate():
+    # all scores equal: rho = 1 < tau and R = 1 < tau everywhere, so no natural
+    # cut; every candidate ties on (S, rho) = (0, 1) and the first candidate
+    # cut, k = d - ceil(alpha d) = 3, is taken: G_min = 2 groups.
+    chi_pp = [[1.0] * 6, [1.0] * 6]
+    gid, G, rho, sup = O.group_dims_bootstrap(chi_pp, [[0, 1], [1, 1]], alpha=0.5, gamma=0.5)
+    assert gid == [0, 0, 0, 1, 1, 1] and G == 2
+    assert rho == {3: 1.0, 4: 1.0, 5: 1.0} and sup == {3: 0.0, 4: 0.0, 5: 0.0}
+
+
+def test_grouping_fallback_prefers_support_over_gap():
+    # means [1, 2.05, 4.65]: rho_1 = 2.05, rho_2 = 4.65 / 2.05.  Replicates:
+    # p0 alone [1, 3, 3.3]: R_1 = 3, R_2 = 1.1; p1 alone [1, 1.1, 6]: R_1 =
+    # 1.1, R_2 = 6 / 1.1; the mean: R_1 = 2.05, R_2 = 2.27.  With replicates
+    # (p0 p0), (p1 p1), (p0 p1), (p0 p0): S_1 = 3/4, S_2 = 2/4, both below
+    # gamma = 0.9.  The fallback takes k = 1 (higher S) although rho_1 < rho_2.
+    chi_pp = [[1, 3, 3.3], [1, 1.1, 6]]
+    boot = [[0, 0], [1, 1], [0, 1], [0, 0]]
+    gid, G, rho, sup = O.group_dims_bootstrap(chi_pp, boot, alpha=1.0, gamma=0.9)
+    assert sup == {1: 0.75, 2: 0.5}
+    assert rho[1] < rho[2]
+    assert gid == [0, 1, 1] and G == 2
+
+
+def test_grouping_budget_rule():
+    # sorted values 1, 2, 3, 4, 30 (dims 0, 1, 2, 4, 3): gaps rho_1..4 = 2,
+    # 1.5, 4/3, 7.5; the two largest are k = 4 and k = 1.
+    gid, rho = O.group_dims_budget([1, 2, 3, 30, 4], 3)
+    assert gid == [0, 1, 1, 2, 1]
+    assert rho == pytest.approx({1: 2.0, 2: 1.5, 3: 4 / 3, 4: 7.5})
+    assert O.group_dims_budget([1, 2, 3, 30, 4], 1)[0] == [0] * 5
+    # a group per dimension: the group id is the rank
+    assert O.group_dims_budget([1, 2, 3, 30, 4], 5)[0] == [0, 1, 2, 4, 3]
+    # equal scores keep index order: sorted dims 1, 3, 0, 2; one gap of 5
+    assert O.group_dims_budget([5, 1, 5, 1], 2)[0] == [1, 0, 1, 0]

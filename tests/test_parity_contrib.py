@@ -79,3 +79,28 @@ def test_contrib_bad_length_gives_nan_for_that_prompt_only():
     k = rng.standard_normal((2, 2, 20, 16)).astype(np.float32)
     _, chip = _contrib(q, k, [20, 21], "f32")
     assert np.isfinite(chip[0]).all() and np.isnan(chip[1]).all()
+
+
+def test_grouping_from_gpu_scores():
+    """oal_contrib's per-prompt scores feed the App. B grouping: on prompts
+    with two planted outlier dimensions per head (x10 in q, as in the
+    Qwen-shaped workload), the paper's settings put both outliers outside the
+    bulk group, and the partition equals the oracle's grouping of the oracle's
+    scores (the scores agree to ~1e-6, far inside every gap here)."""
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    rng = np.random.default_rng(77)
+    P, Hq, Hkv, N, d = 8, 4, 2, 96, 64
+    q = rng.standard_normal((P, Hq, N, d)).astype(np.float32)
+    k = rng.standard_normal((P, Hkv, N, d)).astype(np.float32)
+    outl = np.stack([rng.choice(d, 2, replace=False) for _ in range(Hq)])
+    for h in range(Hq):
+        q[:, h, :, outl[h]] *= 10.0
+    _, chip = _contrib(q, k, None, "f32")
+    per, _ = O.chi_separable(q, k)
+    boot = oal.bootstrap_indices(P, 400, seed=9)
+    gid, ng = oal.group_dims(chip, 0.25, 0.9, boot=boot)
+    for h in range(Hq):
+        assert (gid[h, outl[h]] > 0).all(), (h, gid[h, outl[h]])
+        og, oG, _, _ = O.group_dims_bootstrap(per[:, h, :].tolist(), boot.tolist(), 0.25, 0.9)
+        assert gid[h].tolist() == og and ng[h] == oG
