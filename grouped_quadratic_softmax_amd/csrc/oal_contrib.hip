@@ -10,13 +10,13 @@
 //
 // Kernel 1 (partial): one CTA per (token block, KV head, prompt).  Its 256
 // threads are (d_h / 8) dimension octets x token slots; slot s scans a
-// contiguous run of the block's tokens with 16-byte loads (every load of a
-// token issued before its arithmetic), the slots of a wave are combined in
+// contiguous run of the block's tokens with 16-byte loads (every load of two
+// tokens issued before their arithmetic), the slots of a wave are combined in
 // order with wavefront shuffles, the four waves through LDS, and the block
 // triple goes to the workspace.
 // Kernel 2 (combine): one CTA per query head folds the block triples of each
-// prompt in token order (four contiguous quarters, then an ordered combine
-// of the four), normalises, and averages over prompts with equal weights.
+// prompt in token order (one thread per (prompt, dimension)), normalises,
+// and averages over prompts with equal weights, in prompt order.
 // All terms are non-negative, so fp32 accumulation has no cancellation; the
 // result is deterministic.
 #include <hip/hip_runtime.h>
@@ -30,31 +30,35 @@ namespace oal {
 
 namespace {
 
-// n consecutive activations (n a multiple of 8) as floats, 16-byte loads.
-template <int n>
-__device__ __forceinline__ void load_vals(const uint16_t* p, float* out) {
-#pragma unroll
-  for (int i = 0; i < n; i += 8) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p + i);
+// Eight consecutive activations kept as raw 16-byte (bf16) or 32-byte (fp32)
+// vectors until they are needed as floats.
+template <typename T>
+struct Octet;
+template <>
+struct Octet<uint16_t> {
+  uint4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      out[i + 2 * j] = __uint_as_float(ws[j] << 16);
-      out[i + 2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
+      x[2 * j] = __uint_as_float(ws[j] << 16);
+      x[2 * j + 1] = __uint_as_float(ws[j] & 0xffff0000u);
     }
   }
-}
-template <int n>
-__device__ __forceinline__ void load_vals(const float* p, float* out) {
-#pragma unroll
-  for (int i = 0; i < n; i += 4) {
-    const float4 w = *reinterpret_cast<const float4*>(p + i);
-    out[i] = w.x;
-    out[i + 1] = w.y;
-    out[i + 2] = w.z;
-    out[i + 3] = w.w;
+};
+template <>
+struct Octet<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
   }
-}
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
 
 }  // namespace
 
@@ -102,23 +106,37 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
   const int t1 = min(t0 + per, n);
   const T* kp = k + ((long)(p * Hkv + kvh) * N) * DH + 8 * oct;
   const T* qp = q + ((long)(p * Hq + kvh * R) * N) * DH + 8 * oct;
-  for (int t = t0; t < t1; ++t) {
-    // every load of the token first, then the arithmetic
-    float kx[8], qx[RMAX][8];
-    load_vals<8>(kp + (long)t * DH, kx);
+  // TU tokens per step: every load of the step is issued (raw 16-byte
+  // vectors) before any arithmetic, which then runs in token order
+  constexpr int TU = 2;
+  for (int t = t0; t < t1; t += TU) {
+    Octet<T> kr[TU], qr[TU][RMAX];
 #pragma unroll
-    for (int hh = 0; hh < RMAX; ++hh)
-      if (hh < R) load_vals<8>(qp + ((long)hh * N + t) * DH, qx[hh]);
+    for (int u = 0; u < TU; ++u) {
+      const int tt = min(t + u, t1 - 1);  // in range; a dead token is skipped below
+      kr[u].load(kp + (long)tt * DH);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) K[e] += fabsf(kx[e]);
+      for (int hh = 0; hh < RMAX; ++hh)
+        if (hh < R) qr[u][hh].load(qp + ((long)hh * N + tt) * DH);
+    }
 #pragma unroll
-    for (int hh = 0; hh < RMAX; ++hh) {
-      if (hh < R) {
+    for (int u = 0; u < TU; ++u) {
+      if (t + u >= t1) break;
+      float kx[8];
+      kr[u].get(kx);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float qa = fabsf(qx[hh][e]);
-          A[hh][e] += qa;
-          Bs[hh][e] += qa * K[e];
+      for (int e = 0; e < 8; ++e) K[e] += fabsf(kx[e]);
+#pragma unroll
+      for (int hh = 0; hh < RMAX; ++hh) {
+        if (hh < R) {
+          float qx[8];
+          qr[u][hh].get(qx);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float qa = fabsf(qx[e]);
+            A[hh][e] += qa;
+            Bs[hh][e] += qa * K[e];
+          }
         }
       }
     }
@@ -176,9 +194,10 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
   }
 }
 
-// One CTA per query head, 4 x DH threads: part w folds the w-th contiguous
-// quarter of a prompt's blocks in token order, then the four quarter triples
-// are combined in order.
+// One CTA per query head, 4 x DH threads: thread (w, r) takes prompts
+// w, w + 4, ... and folds all block triples of its prompt in token order
+// (sixteen blocks' loads in flight at a time); the prompt means are then
+// added in prompt order.
 template <int DH>
 __global__ __launch_bounds__(4 * DH) void contrib_combine_kernel(const float* __restrict__ part,
                                                                  const int32_t* __restrict__ seq_lens,
@@ -190,63 +209,45 @@ __global__ __launch_bounds__(4 * DH) void contrib_combine_kernel(const float* __
   const int r = threadIdx.x % DH, w = threadIdx.x / DH;
   const int R = Hq / Hkv, kvh = h / R, hh = h % R;
   const float inv_sqrt_d = 1.f / sqrtf((float)DH);
+  const long stride = (long)(2 * R + 1) * DH;
+  constexpr int U = 16;
   float mean = 0.f;
-  for (int p = 0; p < P; ++p) {
-    const int n = seq_lens ? seq_lens[p] : N;
-    const bool badlen = n < 1 || n > N;
-    const int nb_used = badlen ? nblk : (n + TB - 1) / TB;
-    const float* base = part + ((long)p * Hkv + kvh) * nblk * (2 * R + 1) * DH;
-    const long stride = (long)(2 * R + 1) * DH;
-    // contiguous quarter of the blocks for this part: [b0, b1)
-    const int b0 = (nb_used * w) / 4, b1 = (nb_used * (w + 1)) / 4;
-    float tA = 0.f, tB = 0.f, tK = 0.f;
-    // eight blocks' loads in flight at a time, folded in order
-    for (int bb = b0; bb < b1; bb += 8) {
-      float xa[8], xb[8], xk[8];
+  for (int p0 = 0; p0 < P; p0 += 4) {
+    const int p = p0 + w;
+    float chi = 0.f;
+    if (p < P) {
+      const int n = seq_lens ? seq_lens[p] : N;
+      const bool badlen = n < 1 || n > N;
+      const int nb_used = badlen ? nblk : (n + TB - 1) / TB;
+      const float* base = part + ((long)p * Hkv + kvh) * nblk * stride;
+      float tA = 0.f, tB = 0.f, tK = 0.f;
+      for (int bb = 0; bb < nb_used; bb += U) {
+        float xa[U], xb[U], xk[U];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float* x = base + (long)min(bb + u, b1 - 1) * stride;
-        xa[u] = x[hh * DH + r];
-        xb[u] = x[(R + hh) * DH + r];
-        xk[u] = x[2 * R * DH + r];
-      }
+        for (int u = 0; u < U; ++u) {
+          const float* x = base + (long)min(bb + u, nb_used - 1) * stride;
+          xa[u] = x[hh * DH + r];
+          xb[u] = x[(R + hh) * DH + r];
+          xk[u] = x[2 * R * DH + r];
+        }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (bb + u < b1) {
-          tB += xb[u] + tK * xa[u];
-          tA += xa[u];
-          tK += xk[u];
+        for (int u = 0; u < U; ++u) {
+          if (bb + u < nb_used) {
+            tB += xb[u] + tK * xa[u];
+            tA += xa[u];
+            tK += xk[u];
+          }
         }
       }
-    }
-    // ordered combine of the four quarters
-    __syncthreads();
-    red[w][r] = tA;
-    __syncthreads();
-    float qa[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qa[i] = red[i][r];
-    __syncthreads();
-    red[w][r] = tB;
-    __syncthreads();
-    float qb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qb[i] = red[i][r];
-    __syncthreads();
-    red[w][r] = tK;
-    __syncthreads();
-    if (w == 0) {
-      float cB = 0.f, cK = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        cB += qb[i] + cK * qa[i];
-        cK += red[i][r];
-      }
       const float pairs = 0.5f * (float)n * (float)(n + 1);
-      const float chi = (badlen || cK != cK) ? __builtin_nanf("") : cB * inv_sqrt_d / pairs;
+      chi = (badlen || tK != tK) ? __builtin_nanf("") : tB * inv_sqrt_d / pairs;
       if (chi_per_prompt) chi_per_prompt[((long)p * Hq + h) * DH + r] = chi;
-      mean += chi;
     }
+    __syncthreads();  // previous group's means consumed
+    red[w][r] = chi;
+    __syncthreads();
+    if (w == 0)
+      for (int i = 0; i < 4 && p0 + i < P; ++i) mean += red[i][r];
   }
   if (w == 0) chi_mean[(long)h * DH + r] = mean / (float)P;
 }
