@@ -8,12 +8,12 @@
 // and two adjacent segments L, R combine in order as
 //   (A_L + A_R, B_L + B_R + K_L A_R, K_L + K_R).
 //
-// Kernel 1 (partial): one CTA per (token block, KV head, prompt).  Its 256
-// threads are (d_h / 8) dimension octets x token slots; slot s scans a
-// contiguous run of the block's tokens with 16-byte loads (every load of two
-// tokens issued before their arithmetic), the slots of a wave are combined in
-// order with wavefront shuffles, the four waves through LDS, and the block
-// triple goes to the workspace.
+// Kernel 1 (partial): one CTA per (token block, KV head and pair of its
+// query heads, prompt).  Its 256 threads are (d_h / 8) dimension octets x
+// token slots; slot s scans a contiguous run of the block's tokens with
+// 16-byte loads (every load of four tokens issued before their arithmetic),
+// the slots of a wave are combined in order with wavefront shuffles, the four
+// waves through LDS, and the block triples go to the workspace.
 // Kernel 2 (combine): one CTA per query head folds the block triples of each
 // prompt in token order (one thread per (prompt, dimension)), normalises,
 // and averages over prompts with equal weights, in prompt order.
@@ -62,11 +62,12 @@ struct Octet<float> {
 
 }  // namespace
 
-// Tokens per partial block: the smallest power of two that gives every token
-// slot of a CTA (256 threads over d_h / 8 dimension octets) at least one
-// token and keeps the number of blocks per prompt at or below 64.
+// Tokens per partial block: a power of two of at least 128 (measured best on
+// gfx950 for 2k-token prompts: fewer block triples to fold), enough to give
+// every token slot of a CTA (256 threads over d_h / 8 dimension octets) one
+// token, and large enough to keep the blocks per prompt at or below 64.
 static int contrib_block_tokens(int N, int d_h) {
-  int tb = 64;
+  int tb = 128;
   while (tb < 256 / (d_h / 8)) tb *= 2;
   while ((long)tb * 64 < (long)N) tb *= 2;
   return tb;
@@ -84,8 +85,11 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
   constexpr int NV = 2 * RMAX + 1;             // A[R], B[R], K
   __shared__ float xs[4][NV][DH];
 
-  const int blk = blockIdx.x, kvh = blockIdx.y, p = blockIdx.z;
-  const int R = Hq / Hkv;
+  // blockIdx.y = KV head x head group: this CTA serves query heads
+  // hg*RMAX .. of the KV head (local index hh = hg*RMAX + j)
+  const int R = Hq / Hkv, NHG = (R + RMAX - 1) / RMAX;
+  const int blk = blockIdx.x, kvh = blockIdx.y / NHG, hg = blockIdx.y % NHG, p = blockIdx.z;
+  const int h0 = hg * RMAX, RH = min(RMAX, R - h0);  // heads of this CTA
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int oct = lane % NO, wslot = lane / NO;
   const int slot = wave * SPW + wslot;
@@ -105,10 +109,10 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
   const int t0 = blk * TB + slot * per;
   const int t1 = min(t0 + per, n);
   const T* kp = k + ((long)(p * Hkv + kvh) * N) * DH + 8 * oct;
-  const T* qp = q + ((long)(p * Hq + kvh * R) * N) * DH + 8 * oct;
+  const T* qp = q + ((long)(p * Hq + kvh * R + h0) * N) * DH + 8 * oct;
   // TU tokens per step: every load of the step is issued (raw 16-byte
   // vectors) before any arithmetic, which then runs in token order
-  constexpr int TU = 2;
+  constexpr int TU = 4;
   for (int t = t0; t < t1; t += TU) {
     Octet<T> kr[TU], qr[TU][RMAX];
 #pragma unroll
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
       kr[u].load(kp + (long)tt * DH);
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh)
-        if (hh < R) qr[u][hh].load(qp + ((long)hh * N + tt) * DH);
+        if (hh < RH) qr[u][hh].load(qp + ((long)hh * N + tt) * DH);
     }
 #pragma unroll
     for (int u = 0; u < TU; ++u) {
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
       for (int e = 0; e < 8; ++e) K[e] += fabsf(kx[e]);
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
-        if (hh < R) {
+        if (hh < RH) {
           float qx[8];
           qr[u][hh].get(qx);
 #pragma unroll
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
       const float Kr = __shfl_down(K[e], off);
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
-        if (hh < R) {
+        if (hh < RH) {
           const float Ar = __shfl_down(A[hh][e], off);
           const float Br = __shfl_down(Bs[hh][e], off);
           Bs[hh][e] += Br + K[e] * Ar;
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
       const int r = 8 * oct + e;
 #pragma unroll
       for (int hh = 0; hh < RMAX; ++hh) {
-        if (hh < R) {
+        if (hh < RH) {
           xs[wave][hh][r] = A[hh][e];
           xs[wave][RMAX + hh][r] = Bs[hh][e];
         }
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
   __syncthreads();
   // ordered combine of the four waves: one thread per (head, dimension)
   float* out = part + (((long)p * Hkv + kvh) * nblk + blk) * (2 * R + 1) * DH;
-  for (int idx = threadIdx.x; idx < R * DH; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < RH * DH; idx += blockDim.x) {
     const int hh = idx / DH, r = idx % DH;
     float cA = 0.f, cB = 0.f, cK = 0.f;
 #pragma unroll
@@ -188,9 +192,9 @@ __global__ __launch_bounds__(256) void contrib_partial_kernel(const T* __restric
       cA += Ar;
       cK += xs[w][2 * RMAX][r];
     }
-    out[hh * DH + r] = cA;
-    out[(R + hh) * DH + r] = cB;
-    if (hh == 0) out[2 * R * DH + r] = badlen ? __builtin_nanf("") : cK;
+    out[(h0 + hh) * DH + r] = cA;
+    out[(R + h0 + hh) * DH + r] = cB;
+    if (hg == 0 && hh == 0) out[2 * R * DH + r] = badlen ? __builtin_nanf("") : cK;
   }
 }
 
@@ -264,7 +268,8 @@ static hipError_t launch_contrib_r(const ContribLaunch& a, hipStream_t stream) {
   const int TB = contrib_block_tokens(a.N, a.d_h);
   const int nblk = (a.N + TB - 1) / TB;
   float* part = reinterpret_cast<float*>(a.workspace);
-  hipLaunchKernelGGL((contrib_partial_kernel<T, DH, RMAX>), dim3(nblk, a.Hkv, a.P), dim3(256), 0, stream,
+  const int nhg = (a.Hq / a.Hkv + RMAX - 1) / RMAX;
+  hipLaunchKernelGGL((contrib_partial_kernel<T, DH, RMAX>), dim3(nblk, a.Hkv * nhg, a.P), dim3(256), 0, stream,
                      reinterpret_cast<const T*>(a.q), reinterpret_cast<const T*>(a.k), a.seq_lens, part,
                      a.Hq, a.Hkv, a.N, nblk, TB);
   hipError_t err = hipGetLastError();
@@ -276,12 +281,11 @@ static hipError_t launch_contrib_r(const ContribLaunch& a, hipStream_t stream) {
 
 template <typename T, int DH>
 static hipError_t launch_contrib_d(const ContribLaunch& a, hipStream_t stream) {
+  // at most two query heads per CTA: more CTAs in flight, fewer live
+  // accumulators per thread (the keys are re-read per head pair)
   const int R = a.Hq / a.Hkv;
   if (R <= 1) return launch_contrib_r<T, DH, 1>(a, stream);
-  if (R <= 2) return launch_contrib_r<T, DH, 2>(a, stream);
-  if (R <= 4) return launch_contrib_r<T, DH, 4>(a, stream);
-  if (R <= 8) return launch_contrib_r<T, DH, 8>(a, stream);
-  return launch_contrib_r<T, DH, 16>(a, stream);
+  return launch_contrib_r<T, DH, 2>(a, stream);
 }
 
 hipError_t launch_contrib(const ContribLaunch& a, hipStream_t stream) {
