@@ -44,32 +44,37 @@ constexpr int DV = 64;
 constexpr int NCOL = DV + 1;
 
 // Feature list of a small space: (r, t) over k_hat = [k_0 .. k_{d-1}, 1, 0]
-// (index d is the constant 1, d + 1 a zero used for padding).  The order is
-// the library's packed order (constant, linear terms, then the pairs r <= t
-// row-major) restricted to the features the space has.
+// (index d is the constant 1, d + 1 a zero used for padding).  Internal
+// order: the full space keeps the library's packed order (constant, linear
+// terms, pairs r <= t row-major); the dimension-wise space lists the linear
+// terms, then the squares, then the constant (LIN, SQ, CF below), so that a
+// thread's dimensions map to contiguous features.
 template <int DH, bool DIAG>
 struct SmallSpace {
   static constexpr int F = DIAG ? 1 + 2 * DH : (int)packed_features(DH);
   static constexpr int FP = (F + 31) / 32 * 32;
+  static constexpr int LIN = DIAG ? 0 : 1;   // feature of linear term r: LIN + r
+  static constexpr int SQ = DH;              // dimension-wise: square of r at SQ + r
+  static constexpr int CF = DIAG ? 2 * DH : 0;  // the constant feature
   unsigned char r[FP], t[FP];
 };
 template <int DH, bool DIAG>
 constexpr SmallSpace<DH, DIAG> make_space() {
-  SmallSpace<DH, DIAG> s{};
-  int f = 0;
-  s.r[f] = DH;
-  s.t[f] = DH;
-  ++f;
-  for (int r = 0; r < DH; ++r, ++f) {
-    s.r[f] = (unsigned char)r;
-    s.t[f] = DH;
+  typedef SmallSpace<DH, DIAG> S;
+  S s{};
+  s.r[S::CF] = DH;
+  s.t[S::CF] = DH;
+  for (int r = 0; r < DH; ++r) {
+    s.r[S::LIN + r] = (unsigned char)r;
+    s.t[S::LIN + r] = DH;
   }
+  int f = DIAG ? S::SQ : 1 + DH;
   for (int r = 0; r < DH; ++r)
     for (int t = r; t < (DIAG ? r + 1 : DH); ++t, ++f) {
       s.r[f] = (unsigned char)r;
       s.t[f] = (unsigned char)t;
     }
-  for (; f < SmallSpace<DH, DIAG>::FP; ++f) {
+  for (f = S::F; f < S::FP; ++f) {
     s.r[f] = DH + 1;
     s.t[f] = DH + 1;
   }
@@ -149,6 +154,38 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xf | (7 << 4) | (3 << 14));  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// n floats as n consecutive elements (bf16 bits or float) with 8- and
+// 16-byte stores; p is aligned to the run's size (at most 16 bytes).
+template <int n>
+__device__ __forceinline__ void store_run(uint16_t* p, const float (&x)[n]) {
+  static_assert(n % 4 == 0, "runs of 4k elements");
+  if constexpr (n % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < n; i += 8) {
+      uint4 w;
+      w.x = (uint32_t)bf16_bits(x[i]) | ((uint32_t)bf16_bits(x[i + 1]) << 16);
+      w.y = (uint32_t)bf16_bits(x[i + 2]) | ((uint32_t)bf16_bits(x[i + 3]) << 16);
+      w.z = (uint32_t)bf16_bits(x[i + 4]) | ((uint32_t)bf16_bits(x[i + 5]) << 16);
+      w.w = (uint32_t)bf16_bits(x[i + 6]) | ((uint32_t)bf16_bits(x[i + 7]) << 16);
+      *reinterpret_cast<uint4*>(p + i) = w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < n; i += 4) store4(p + i, f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]});
+  }
+}
+template <int n>
+__device__ __forceinline__ void store_run(float* p, const float (&x)[n]) {
+  static_assert(n % 2 == 0, "runs of 2k elements");
+  if constexpr (n % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < n; i += 4) store4(p + i, f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]});
+  } else {
+#pragma unroll
+    for (int i = 0; i < n; i += 2) *reinterpret_cast<float2*>(p + i) = make_float2(x[i], x[i + 1]);
+  }
 }
 
 // sum over the TPR consecutive lanes that share a token row (TPR = 4 or 8)
@@ -233,7 +270,8 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
 
   // packed (library) index of feature f of the space
   auto abi_f = [](int f) __attribute__((always_inline)) {
-    return (DIAG && f > DH) ? abi_index(DH, f - 1 - DH, f - 1 - DH) : (long)f;
+    if constexpr (!DIAG) return (long)f;
+    return f < DH ? 1L + f : f < 2 * DH ? abi_index(DH, f - DH, f - DH) : 0L;
   };
 
   // ---- query-side coefficients of every head of the KV head ----
@@ -339,19 +377,35 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
   // dimensions are written directly; the pair features of the full space are
   // formed from the rows gathered in LDS, wave-uniform feature by feature.
   auto feats = [&](float (&x)[QD], E* rows, E* cols, const float* coef) __attribute__((always_inline)) {
+    if constexpr (DIAG) {
+      // the thread's QD dimensions are contiguous runs of features, stored as
+      // 8- or 16-byte vectors in the row-major tile
+      float lin[QD], sqv[QD];
 #pragma unroll
-    for (int i = 0; i < QD; ++i) {
-      const int r = sq * QD + i;
-      const E lin = to_e(coef ? coef[1 + r] * x[i] : x[i], E());
-      if (rows) rows[srow * FPP + 1 + r] = lin;
-      if (cols) cols[(1 + r) * CP + srow] = lin;
-      if constexpr (DIAG) {
-        const E sqv = to_e(coef ? coef[1 + DH + r] * x[i] * x[i] : x[i] * x[i], E());
-        if (rows) rows[srow * FPP + 1 + DH + r] = sqv;
-        if (cols) cols[(1 + DH + r) * CP + srow] = sqv;
+      for (int i = 0; i < QD; ++i) {
+        const int r = sq * QD + i;
+        lin[i] = coef ? coef[SP::LIN + r] * x[i] : x[i];
+        sqv[i] = coef ? coef[SP::SQ + r] * x[i] * x[i] : x[i] * x[i];
       }
-    }
-    if constexpr (!DIAG) {
+      if (rows) {
+        store_run<QD>(rows + srow * FPP + SP::LIN + sq * QD, lin);
+        store_run<QD>(rows + srow * FPP + SP::SQ + sq * QD, sqv);
+      }
+      if (cols)
+#pragma unroll
+        for (int i = 0; i < QD; ++i) {
+          const int r = sq * QD + i;
+          cols[(SP::LIN + r) * CP + srow] = to_e(lin[i], E());
+          cols[(SP::SQ + r) * CP + srow] = to_e(sqv[i], E());
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < QD; ++i) {
+        const int r = sq * QD + i;
+        const E lin = to_e(coef ? coef[SP::LIN + r] * x[i] : x[i], E());
+        if (rows) rows[srow * FPP + SP::LIN + r] = lin;
+        if (cols) cols[(SP::LIN + r) * CP + srow] = lin;
+      }
 #pragma unroll
       for (int i = 0; i < QD; ++i) hat[srow * KH + sq * QD + i] = x[i];
       lds_sync();
@@ -389,8 +443,8 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
       feats(kx, OUT ? kf : nullptr, kft, nullptr);  // kernel 1 needs only the transposed tile
       if (sq == 0) {
         const E one = to_e(okrow ? 1.f : 0.f, E());
-        if (OUT) kf[srow * FPP] = one;
-        kft[srow] = one;
+        if (OUT) kf[srow * FPP + SP::CF] = one;
+        kft[SP::CF * CP + srow] = one;
         vt[DV * CP + srow] = one;
       }
 #pragma unroll
@@ -404,13 +458,11 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
       for (int i = 0; i < MTW; ++i) {
         const int m = wave + 4 * i;
         if (m >= MT) continue;
+        // a lane's four rows 4 lg + e are consecutive features: one store each
+        const int f0 = 16 * m + 4 * lg;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int f = 16 * m + 4 * lg + e;
-#pragma unroll
-          for (int n = 0; n < 4; ++n) st[(16 * n + l16) * FPP + f] = to_e(acc[i][n][e], E());
-          if (l16 == 0) st[DV * FPP + f] = to_e(acc[i][4][e], E());
-        }
+        for (int n = 0; n < 4; ++n) store4(&st[(16 * n + l16) * FPP + f0], acc[i][n]);
+        if (l16 == 0) store4(&st[DV * FPP + f0], acc[i][4]);
       }
     }
     // ---- S += phi_K^T [V | 1] ----
@@ -447,7 +499,7 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
           }
           if (PREMAP) premap_row<DH, TPR, QD>(qx, h * DH + sq * QD, gamma_q, beta_q, ln_eps, okrow);
           feats(qx, qf, nullptr, coefq[hh]);
-          if (sq == 0) qf[srow * FPP] = to_e(okrow ? coefq[hh][0] : 0.f, E());
+          if (sq == 0) qf[srow * FPP + SP::CF] = to_e(okrow ? coefq[hh][SP::CF] : 0.f, E());
         }
         lds_sync();
         for (int rt = wave; rt < RT; rt += 4) {
@@ -491,15 +543,23 @@ __global__ __launch_bounds__(256) void small_fwd_kernel(
             const int ja = 16 * jt0 + 4 * lg, jb = ja + 16;
 #pragma unroll
             for (int n = 0; n < 5; ++n) {
-              float vb[8];
+              // values of keys ja..ja+3 and jb..jb+3, straight from the tile
               const E* vr = vt + (n < 4 ? 16 * n + l16 : DV) * CP;
               const bool live = n < 4 || l16 == 0;
+              F Bv;
+              if constexpr (IsBf16<T>::value) {
+                uint2 lo = *reinterpret_cast<const uint2*>(vr + ja);
+                uint2 hi = *reinterpret_cast<const uint2*>(vr + jb);
+                if (!live) lo = hi = make_uint2(0u, 0u);
+                Bv.v = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+              } else {
+                const float4 lo = *reinterpret_cast<const float4*>(vr + ja);
+                const float4 hi = *reinterpret_cast<const float4*>(vr + jb);
+                const float vb[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                vb[e] = live ? to_f32(vr[ja + e]) : 0.f;
-                vb[4 + e] = live ? to_f32(vr[jb + e]) : 0.f;
+                for (int e = 0; e < 8; ++e) Bv.v[e] = live ? vb[e] : 0.f;
               }
-              mma(yacc[n], A, frag_from<IsBf16<T>::value>(vb));
+              mma(yacc[n], A, Bv);
             }
           }
           // ---- y = num / den via the wave's output tile ----
