@@ -947,6 +947,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
         const float mu = (float)(fe >> 14);
 #pragma unroll
         for (int hh = 0; hh < nh; ++hh) {
+          if (hh >= nreal) break;  // dead slots are never read
           const int ce = cexp[hh];
           float val = 0.f;
           if (fe != kPadFeature && ce != kBadHead) {
@@ -1005,6 +1006,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
 #pragma unroll 1
     for (int j = 0; j < HOWN; ++j) {
       const int hh = HS * j + kpar;
+      if (hh >= nreal) break;  // dead slots (wave-uniform): no work, zero accumulators
       const float* pcr = pc[hh];  // LDS
       // masked query fragments per group (B operand of the transposed scores)
       F Bq[NG][STEPS];
@@ -1159,6 +1161,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
 #pragma unroll
           for (int j = 0; j < HOWN; ++j) {
             const int hh = HS * j + kpar;
+            if (hh >= nreal) break;  // dead slots (wave-uniform)
             const E* qrow = qh + ((long)hh * C + row) * DHP;
             const E* cf = coef + ((long)hh * (KB + 1) + kk) * 32 + 8 * lg;
             F A;
@@ -1208,6 +1211,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
           const E* cb = coef + ((long)kpar * (KB + 1) + kk) * 32 + 8 * lo.lgo;
 #pragma unroll
           for (int j = 0; j < HOWN; ++j) {
+            if (HS * j + kpar >= nreal) break;  // dead slots (wave-uniform)
             const E* qrow = qh + ((long)(HS * j + kpar) * C + row) * DHP;
             const E* cf = cb + HS * j * (KB + 1) * 32;
             F A;
