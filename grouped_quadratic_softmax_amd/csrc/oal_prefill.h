@@ -313,11 +313,18 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   const int nu = kb < NQ ? 2 : (kb < KB ? 1 : 0);  // key-exponent multiplicity of the wave's features
   const bool lead = blockIdx.x == 0 && tid == 0;
   const long nsnap = (long)nchunks * BH;  // snapshots in the workspace
-  // loader role: token ltok, units lhalf + 2 i (dimensions 8 unit ..)
+  // loader role.  With the pre-map: token ltok, units lhalf + 2 i
+  // (dimensions 8 unit ..), so that a token's statistics stay in two lanes.
+  // Without it: tokens 4 tg .. 4 tg + 3 of unit lu, so that each staged row
+  // segment of four tokens leaves the lane as one 8- or 16-byte store.
   const int lw = wave - kScanCompute;
   const bool kload = loader && lw < 2;
   const int ltok = 32 * (lw & 1) + (lane & 31);
   const int lhalf = lane >> 5;
+  const int lsid = 64 * (lw & 1) + lane;
+  const int tg = lsid % 16, lu = lsid / 16;
+  const bool ulive = lu < (kload ? DH : DV) / 8;
+  static_assert(UL == 4, "four tokens per loader lane");
 
   if (PREMAP)
     for (int i = tid; i < 2 * DH; i += blockDim.x) gb[i / DH][i % DH] = (i < DH ? gamma_k : beta_k)[kvh * DH + i % DH];
@@ -355,6 +362,22 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   };
   auto fetch = [&](int c) __attribute__((always_inline)) {
     RawSet r;
+    if constexpr (!PREMAP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = c * C + 4 * tg + i;
+        const long rr = row < N ? row : N - 1;
+        if (ulive) {
+          ld8(r.u[i], kload ? kp + rr * DH + 8 * lu : vp + rr * DV + 8 * lu);
+          if (row >= N) zero8(r.u[i]);
+        } else {
+          zero8(r.u[i]);
+        }
+      }
+      r.mu = 0.f;
+      r.inv = 0.f;
+      return r;
+    }
     const int row = c * C + ltok;
     const long rr = row < N ? row : N - 1;
 #pragma unroll
@@ -382,6 +405,19 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   };
   // pre-map statistics and this wave's maximum into wmx[slot]
   auto convert = [&](RawSet& r, int c, int slot) __attribute__((always_inline)) {
+    if constexpr (!PREMAP) {  // tokens past the end were loaded as zeros
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x[8];
+        unpack8(r.u[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+      }
+      m = wave_max(m);
+      if (lane == 0) wmx[slot][lw] = m;
+      return;
+    }
     const bool valid = c * C + ltok < N;
     if (PREMAP && kload) {
       float s = 0.f;
@@ -421,8 +457,28 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   // scaled chunk -> staging buffer: k / 2^ekx, v / 2^evx, transposed
   auto stage = [&](const RawSet& r, int c, int buf, int ekx, int evx) __attribute__((always_inline)) {
     E* tb = tile[buf];
-    const bool valid = c * C + ltok < N;
     const float sc = pow2(kload ? -ekx : -evx);
+    if constexpr (!PREMAP) {
+      typedef E E4 __attribute__((ext_vector_type(4)));
+      if (ulive) {
+        float x[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unpack8(r.u[i], x[i]);
+        const int r0 = (kload ? 0 : VROW) + 8 * lu;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<E4*>(&tb[(r0 + e) * KP + 4 * tg]) =
+              E4{(E)(x[0][e] * sc), (E)(x[1][e] * sc), (E)(x[2][e] * sc), (E)(x[3][e] * sc)};
+      }
+      if (kload && lu < 2) {  // the row of ones (valid tokens) and the row of zeros
+        E4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (lu == 0 && c * C + 4 * tg + i < N) ? (E)1.f : (E)0.f;
+        *reinterpret_cast<E4*>(&tb[(lu == 0 ? ONE : ZERO) * KP + 4 * tg]) = o;
+      }
+      return;
+    }
+    const bool valid = c * C + ltok < N;
 #pragma unroll
     for (int i = 0; i < UL; ++i) {
       if (kload && i >= KUL) continue;
