@@ -362,6 +362,9 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   };
   auto fetch = [&](int c) __attribute__((always_inline)) {
     RawSet r;
+    // Rows past the sequence end load the last row (in bounds) and are
+    // zeroed where the values are used: a select right after the load would
+    // make every prefetch wait for its data.
     if constexpr (!PREMAP) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -369,7 +372,6 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
         const long rr = row < N ? row : N - 1;
         if (ulive) {
           ld8(r.u[i], kload ? kp + rr * DH + 8 * lu : vp + rr * DV + 8 * lu);
-          if (row >= N) zero8(r.u[i]);
         } else {
           zero8(r.u[i]);
         }
@@ -385,7 +387,6 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
       const int unit = lhalf + 2 * i;
       if (kload ? i < KUL : true) {
         ld8(r.u[i], kload ? kp + rr * DH + 8 * unit : vp + rr * DV + 8 * unit);
-        if (row >= N) zero8(r.u[i]);
       } else {
         zero8(r.u[i]);
       }
@@ -405,14 +406,15 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   };
   // pre-map statistics and this wave's maximum into wmx[slot]
   auto convert = [&](RawSet& r, int c, int slot) __attribute__((always_inline)) {
-    if constexpr (!PREMAP) {  // tokens past the end were loaded as zeros
+    if constexpr (!PREMAP) {
       float m = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const bool valid = c * C + 4 * tg + i < N;
         float x[8];
         unpack8(r.u[i], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, valid ? fabsf(x[e]) : 0.f);
       }
       m = wave_max(m);
       if (lane == 0) wmx[slot][lw] = m;
@@ -463,7 +465,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
       if (ulive) {
         float x[4][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) unpack8(r.u[i], x[i]);
+        for (int i = 0; i < 4; ++i) {
+          unpack8(r.u[i], x[i]);
+          if (c * C + 4 * tg + i >= N)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+        }
         const int r0 = (kload ? 0 : VROW) + 8 * lu;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
