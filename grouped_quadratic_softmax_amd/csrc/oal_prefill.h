@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "oal_device.h"
 #include "oal_internal.h"
 
@@ -504,10 +506,14 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
 
   // ---- prologue: chunk 0 staged, maxima of chunk 1 reduced ----
   RawSet R[NR];
+  // Every fetch, convert and stage is issued unconditionally (chunk indices
+  // past the end are clamped for loads, and rows past the end stage as
+  // zeros into a buffer nobody reads), and the loader and compute roles run
+  // separate loops: straight-line code lets the compiler's memory-counter
+  // waits cover exactly the chunk being staged, so NR chunks stay in flight.
   if (loader) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i)
-      if (i < nchunks) R[i] = fetch(i);
+    for (int i = 0; i < NR; ++i) R[i] = fetch(min(i, nchunks - 1));
     convert(R[0], 0, 0);
   }
   __syncthreads();
@@ -562,8 +568,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   }
   if (loader) {
     stage(R[0], 0, 0, Ek, Ev + beta);
-    if (nchunks > 1) convert(R[1], 1, 1);
-    if (NR < nchunks) R[0] = fetch(NR);
+    convert(R[1], 1, 1);
+    R[0] = fetch(min(NR, nchunks - 1));
   }
   __syncthreads();
 
@@ -579,7 +585,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
 
   // Chunk c.  Loader registers: rs = chunk c+1 (staged now, then refilled
   // with chunk c+1+NR), rc = chunk c+2 (maxima reduced now).
-  auto step = [&](int c, RawSet& rs, RawSet& rc) __attribute__((always_inline)) {
+  auto step = [&](auto role, int c, RawSet& rs, RawSet& rc) __attribute__((always_inline)) {
+    constexpr bool LOADER = decltype(role)::value;
     int Ek1 = Ek, Ev1 = Ev;  // exponents of chunk c+1
     if (c + 1 < nchunks) {
       int ek, ev;
@@ -587,10 +594,10 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
       Ek1 = max(Ek, ek);
       Ev1 = max(Ev, ev);
     }
-    if (loader) {
-      if (c + 1 < nchunks) stage(rs, c + 1, (c + 1) & 1, Ek1, Ev1 + beta);
-      if (c + 2 < nchunks) convert(rc, c + 2, c & 1);
-      if (c + 1 + NR < nchunks) rs = fetch(c + 1 + NR);
+    if constexpr (LOADER) {
+      stage(rs, c + 1, (c + 1) & 1, Ek1, Ev1 + beta);
+      convert(rc, c + 2, c & 1);
+      rs = fetch(min(c + 1 + NR, nchunks - 1));
     } else {
       // ---- snapshot S_c: raw = stored * 2^(beta + nu Ek) (* 2^Ev for H) ----
       const long sidx = (long)c * BH + bh;
@@ -666,11 +673,18 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     Ev = Ev1;
     __syncthreads();
   };
-  for (int c0 = 0; c0 < nchunks; c0 += NR) {
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    int c0 = 0;
+    for (; c0 + NR <= nchunks; c0 += NR) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i)
-      if (c0 + i < nchunks) step(c0 + i, R[(i + 1) % NR], R[(i + 2) % NR]);
-  }
+      for (int i = 0; i < NR; ++i) step(role, c0 + i, R[(i + 1) % NR], R[(i + 2) % NR]);
+    }
+#pragma unroll
+    for (int i = 0; i + 1 < NR; ++i)
+      if (c0 + i < nchunks) step(role, c0 + i, R[(i + 1) % NR], R[(i + 2) % NR]);
+  };
+  if (loader) run(std::true_type{});
+  else run(std::false_type{});
 
   // ---- final state -> ABI layout (raw moments, each packed entry once) ----
   if (state_out != nullptr) {
