@@ -230,20 +230,22 @@ __device__ __forceinline__ void premap4(float* x, int d0, const float* __restric
 // kernel 1: chunk scan (state update + snapshots)
 // --------------------------------------------------------------------------
 
-// One CTA per (eight K-blocks, batch x KV head), twelve waves in two roles:
-//  * compute waves 0..7: wave w keeps K-block 8 blockIdx.x + w of S in fp32
-//    MFMA accumulators (the wave after the last K-block keeps the constant
-//    feature's row [sum v, n]); per chunk it writes the snapshot S_c and adds
-//    phi_k(K_c)^T [V_c | 1].  They issue only stores to global memory.
-//  * loader waves 8..11: lane = token, each holding 16 or 32 dimensions of
-//    the keys (waves 8, 9) or values (10, 11); they load chunks ahead, reduce
-//    the chunk maxima that set the scaling exponents, apply the pre-map, and
-//    write the scaled tiles transposed into LDS (double-buffered).  They issue
-//    only loads, so their waits never cover the snapshot stores.
+// One CTA per (NCW K-blocks, batch x KV head), twelve waves in two roles:
+//  * compute waves 0..NCW-1 (NCW = 4 or 8): wave w keeps K-block
+//    NCW blockIdx.x + w of S in fp32 MFMA accumulators (the wave after the
+//    last K-block keeps the constant feature's row [sum v, n]); per chunk it
+//    writes the snapshot S_c and adds phi_k(K_c)^T [V_c | 1].  They issue
+//    only stores to global memory.
+//  * loader waves: the first half keys, the second half values; they load
+//    chunks ahead, reduce the chunk maxima that set the scaling exponents,
+//    apply the pre-map, and write the scaled tiles transposed into LDS
+//    (double-buffered).  They issue only loads, so their waits never cover
+//    the snapshot stores.
 // One barrier per chunk separates staging chunk c+1 from reading chunk c.
-constexpr int kScanCompute = 8;
-constexpr int kScanLoad = 4;
-constexpr int kScanWaves = kScanCompute + kScanLoad;
+// NCW = 4 keeps the MFMA work per SIMD and chunk at one K-block and splits
+// the staging eight ways; it takes twice the CTAs of NCW = 8, which the host
+// picks when the NCW = 4 grid would not fit on the compute units at once.
+constexpr int kScanWaves = 12;
 
 // Eight consecutive activations of one row, as loaded.
 template <typename T>
@@ -279,7 +281,7 @@ __device__ __forceinline__ void unpack8(const Raw8<float>& r, float (&x)[8]) {
   x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
 }
 
-template <typename T, int DH, bool PREMAP>
+template <typename T, int DH, bool PREMAP, int NCW>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gamma_k,
     const float* __restrict__ beta_k, float ln_eps, const float* __restrict__ state_in,
@@ -298,8 +300,13 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   constexpr int KUL = DH / 16;             // key units (8 dimensions) per loader lane
   constexpr int UL = DV / 16;              // value units per loader lane (>= KUL)
   constexpr int NR = IsBf16<T>::value ? 3 : 2;  // chunks held in loader registers
+  constexpr int kScanCompute = NCW;
+  constexpr int kScanLoad = kScanWaves - NCW;
+  constexpr int LWR = kScanLoad / 2;           // loader waves per role (keys, values)
+  constexpr int TPL = 8 / LWR;                 // tokens per loader lane without the pre-map
+  static_assert(NCW == 4 || NCW == 8, "four or eight compute waves");
   __shared__ __align__(16) E tile[2][BUF];
-  __shared__ float wmx[2][kScanLoad];      // [slot][loader wave]: max |k| (waves 0, 1), |v| (2, 3)
+  __shared__ float wmx[2][kScanLoad];      // [slot][loader wave]: max |k| (first half), |v| (second half)
   __shared__ float wm_in[kScanCompute];
   __shared__ __align__(16) float gb[2][DH];  // pre-map gamma, beta of the KV head
 
@@ -315,18 +322,20 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   const int nu = kb < NQ ? 2 : (kb < KB ? 1 : 0);  // key-exponent multiplicity of the wave's features
   const bool lead = blockIdx.x == 0 && tid == 0;
   const long nsnap = (long)nchunks * BH;  // snapshots in the workspace
-  // loader role.  With the pre-map: token ltok, units lhalf + 2 i
-  // (dimensions 8 unit ..), so that a token's statistics stay in two lanes.
-  // Without it: tokens 4 tg .. 4 tg + 3 of unit lu, so that each staged row
-  // segment of four tokens leaves the lane as one 8- or 16-byte store.
+  // loader role.  With the pre-map: the first two loader waves of each role,
+  // token ltok, units lhalf + 2 i (dimensions 8 unit ..), so that a token's
+  // statistics stay in two lanes; further loader waves idle.  Without it:
+  // tokens TPL tg .. TPL tg + TPL - 1 of unit lu, so that each staged row
+  // segment of TPL tokens leaves the lane as one store.
   const int lw = wave - kScanCompute;
-  const bool kload = loader && lw < 2;
-  const int ltok = 32 * (lw & 1) + (lane & 31);
+  const bool kload = loader && lw < LWR;
+  const bool lidle = PREMAP && loader && (lw % LWR) >= 2;
+  const int ltok = 32 * ((lw % LWR) & 1) + (lane & 31);
   const int lhalf = lane >> 5;
-  const int lsid = 64 * (lw & 1) + lane;
-  const int tg = lsid % 16, lu = lsid / 16;
+  const int lsid = 64 * (lw % LWR) + lane;
+  const int tg = lsid % (64 / TPL), lu = lsid / (64 / TPL);
   const bool ulive = lu < (kload ? DH : DV) / 8;
-  static_assert(UL == 4, "four tokens per loader lane");
+  static_assert(UL == 4, "four units per pre-map loader lane");
 
   if (PREMAP)
     for (int i = tid; i < 2 * DH; i += blockDim.x) gb[i / DH][i % DH] = (i < DH ? gamma_k : beta_k)[kvh * DH + i % DH];
@@ -369,8 +378,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     // make every prefetch wait for its data.
     if constexpr (!PREMAP) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = c * C + 4 * tg + i;
+      for (int i = 0; i < TPL; ++i) {
+        const int row = c * C + TPL * tg + i;
         const long rr = row < N ? row : N - 1;
         if (ulive) {
           ld8(r.u[i], kload ? kp + rr * DH + 8 * lu : vp + rr * DV + 8 * lu);
@@ -387,7 +396,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
 #pragma unroll
     for (int i = 0; i < UL; ++i) {
       const int unit = lhalf + 2 * i;
-      if (kload ? i < KUL : true) {
+      if (!lidle && (kload ? i < KUL : true)) {
         ld8(r.u[i], kload ? kp + rr * DH + 8 * unit : vp + rr * DV + 8 * unit);
       } else {
         zero8(r.u[i]);
@@ -411,8 +420,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     if constexpr (!PREMAP) {
       float m = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = c * C + 4 * tg + i < N;
+      for (int i = 0; i < TPL; ++i) {
+        const bool valid = c * C + TPL * tg + i < N;
         float x[8];
         unpack8(r.u[i], x);
 #pragma unroll
@@ -422,7 +431,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
       if (lane == 0) wmx[slot][lw] = m;
       return;
     }
-    const bool valid = c * C + ltok < N;
+    const bool valid = !lidle && c * C + ltok < N;
     if (PREMAP && kload) {
       float s = 0.f;
 #pragma unroll
@@ -463,30 +472,34 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     E* tb = tile[buf];
     const float sc = pow2(kload ? -ekx : -evx);
     if constexpr (!PREMAP) {
-      typedef E E4 __attribute__((ext_vector_type(4)));
+      typedef E EV __attribute__((ext_vector_type(TPL)));
       if (ulive) {
-        float x[4][8];
+        float x[TPL][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < TPL; ++i) {
           unpack8(r.u[i], x[i]);
-          if (c * C + 4 * tg + i >= N)
+          if (c * C + TPL * tg + i >= N)
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
         }
         const int r0 = (kload ? 0 : VROW) + 8 * lu;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<E4*>(&tb[(r0 + e) * KP + 4 * tg]) =
-              E4{(E)(x[0][e] * sc), (E)(x[1][e] * sc), (E)(x[2][e] * sc), (E)(x[3][e] * sc)};
+        for (int e = 0; e < 8; ++e) {
+          EV o;
+#pragma unroll
+          for (int i = 0; i < TPL; ++i) o[i] = (E)(x[i][e] * sc);
+          *reinterpret_cast<EV*>(&tb[(r0 + e) * KP + TPL * tg]) = o;
+        }
       }
       if (kload && lu < 2) {  // the row of ones (valid tokens) and the row of zeros
-        E4 o;
+        EV o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (lu == 0 && c * C + 4 * tg + i < N) ? (E)1.f : (E)0.f;
-        *reinterpret_cast<E4*>(&tb[(lu == 0 ? ONE : ZERO) * KP + 4 * tg]) = o;
+        for (int i = 0; i < TPL; ++i) o[i] = (lu == 0 && c * C + TPL * tg + i < N) ? (E)1.f : (E)0.f;
+        *reinterpret_cast<EV*>(&tb[(lu == 0 ? ONE : ZERO) * KP + TPL * tg]) = o;
       }
       return;
     }
+    if (lidle) return;
     const bool valid = c * C + ltok < N;
 #pragma unroll
     for (int i = 0; i < UL; ++i) {
@@ -500,8 +513,14 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     if (kload) tb[(lhalf ? ZERO : ONE) * KP + ltok] = (!lhalf && valid) ? (E)1.f : (E)0.f;
   };
   auto chunk_exps = [&](int slot, int& ek, int& ev) __attribute__((always_inline)) {
-    ek = exp_above(fmaxf(wmx[slot][0], wmx[slot][1]));
-    ev = exp_above(fmaxf(wmx[slot][2], wmx[slot][3]));
+    float mk = 0.f, mv = 0.f;
+#pragma unroll
+    for (int w = 0; w < LWR; ++w) {
+      mk = fmaxf(mk, wmx[slot][w]);
+      mv = fmaxf(mv, wmx[slot][LWR + w]);
+    }
+    ek = exp_above(mk);
+    ev = exp_above(mv);
   };
 
   // ---- prologue: chunk 0 staged, maxima of chunk 1 reduced ----
@@ -1440,13 +1459,23 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   const T* vv = reinterpret_cast<const T*>(a.v);
   T* yy = reinterpret_cast<T*>(a.y);
   if (stages & 1) {
-    dim3 grid((KB + 1 + kScanCompute - 1) / kScanCompute, BH);  // K-blocks + the constant row
-    if (a.premap)
-      hipLaunchKernelGGL((scan_kernel<T, DH, true>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv, a.gamma_k,
-                         a.beta_k, a.ln_eps, a.state_in, a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks);
-    else
-      hipLaunchKernelGGL((scan_kernel<T, DH, false>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv, nullptr,
-                         nullptr, 0.f, a.state_in, a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks);
+    // four compute waves per CTA when that grid fits on the 256 compute
+    // units in one round (one CTA per unit), else eight
+    const bool four = (long)((KB + 1 + 3) / 4) * BH <= 256;
+    const int ncw = four ? 4 : 8;
+    dim3 grid((KB + 1 + ncw - 1) / ncw, BH);  // K-blocks + the constant row
+#define OAL_SCAN(PM, NC)                                                                                       \
+    hipLaunchKernelGGL((scan_kernel<T, DH, PM, NC>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv,            \
+                       PM ? a.gamma_k : nullptr, PM ? a.beta_k : nullptr, PM ? a.ln_eps : 0.f, a.state_in,     \
+                       a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks)
+    if (a.premap) {
+      if (four) OAL_SCAN(true, 4);
+      else OAL_SCAN(true, 8);
+    } else {
+      if (four) OAL_SCAN(false, 4);
+      else OAL_SCAN(false, 8);
+    }
+#undef OAL_SCAN
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

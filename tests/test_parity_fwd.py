@@ -215,6 +215,34 @@ def test_c5_eight_groups_small():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_many_kv_heads_eight_wave_scan(dtype):
+    # 16 (sequence, KV head) pairs at d_h = 64: the scan grid with four
+    # K-blocks per CTA would need 18 x 16 = 288 CTAs, more than the compute
+    # units, so the library takes eight K-blocks per CTA; outputs and the
+    # final state must match as in the four-K-block layout
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    wl = S.make(2, batch=2, n_q_heads=16, n_kv_heads=8, seq_len=170, dtype=dtype)
+    assert ((70 + 1 + 3) // 4) * wl.batch * wl.n_kv_heads > 256
+    co = gpu_coeffs(wl, wl.group_of_dim)
+    q, k, v = to_dev(wl.q, dtype), to_dev(wl.k, dtype), to_dev(wl.v, dtype)
+    y, st = oal.fwd(q, k, v, co, return_state=True)
+    a, b, c = oracle_coeffs(wl)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)
+    err = rel_err(to_np(y), ref)
+    log(f"[fwd] eight-wave scan {dtype}: max rel err {err:.3e}")
+    assert err <= TOL[dtype]
+    # final state: the same derived bound as the continuation test
+    u = 2.0 ** -11 if dtype == "bf16" else 2.0 ** -24
+    for bi in range(wl.batch):
+        for kh in range(wl.n_kv_heads):
+            ref_s = O.abi_state_from_matrix(O.state_from_prefix(wl.k[bi, kh], wl.v[bi, kh]))
+            absum = O.abi_state_from_matrix(O.state_from_prefix(np.abs(wl.k[bi, kh]), np.abs(wl.v[bi, kh])))
+            bound = (2 * u + wl.seq_len * 2.0 ** -24) * absum + 2.0 ** -24 * absum.max()
+            assert (np.abs(to_np(st)[bi, kh] - ref_s) <= bound).all(), (bi, kh)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_state_out_and_continuation(dtype):
     require_gpu()
     import grouped_quadratic_softmax_amd as oal
