@@ -368,8 +368,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
 
   // ---- loader helpers ----
   struct RawSet {
-    Raw8<T> u[UL];
-    float mu, inv;  // pre-map statistics of the token (keys)
+    Raw8<T> u[PREMAP ? UL : TPL];  // units of one token (pre-map) or one unit of TPL tokens
+    float mu, inv;                  // pre-map statistics of the token (keys)
   };
   auto fetch = [&](int c) __attribute__((always_inline)) {
     RawSet r;
