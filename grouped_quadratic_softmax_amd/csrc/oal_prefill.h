@@ -281,12 +281,63 @@ __device__ __forceinline__ void unpack8(const Raw8<float>& r, float (&x)[8]) {
   x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
 }
 
+// Chunk exponents (one CTA per chunk and batch x KV head): ek, ev with
+// |k| < 2^ek over the chunk's keys (after the pre-map) and |v| < 2^ev over its
+// values (kNegExp for all zeros).  The scan reads them from this table
+// instead of every CTA of a sequence reducing the same chunk maxima.
+template <typename T, int DH, bool PREMAP>
+__global__ __launch_bounds__(256) void chunk_exp_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                        const float* __restrict__ gamma_k,
+                                                        const float* __restrict__ beta_k, float ln_eps,
+                                                        int2* __restrict__ kvexp, int Hkv, int N, int nchunks) {
+  constexpr int QD = DH / 4, QV = DV / 4;
+  __shared__ float wm[2][4];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int kvh = bh % Hkv;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int srow = tid / 4, sq = tid % 4;  // token of the chunk, quarter of its dimensions
+  const int row = c * C + srow;
+  const bool valid = row < N;
+  float kx[QD], vx[QV];
+#pragma unroll
+  for (int i = 0; i < QD; ++i) kx[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < QV; ++i) vx[i] = 0.f;
+  if (valid) {
+    load_vals<QD>(k + ((long)bh * N + row) * DH + sq * QD, kx);
+    load_vals<QV>(v + ((long)bh * N + row) * DV + sq * QV, vx);
+  }
+  if (PREMAP) {
+    premap4<DH, QD>(kx, sq * QD, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
+    if (!valid)
+#pragma unroll
+      for (int i = 0; i < QD; ++i) kx[i] = 0.f;
+  }
+  float mk = 0.f, mv = 0.f;
+#pragma unroll
+  for (int i = 0; i < QD; ++i) mk = fmaxf(mk, fabsf(kx[i]));
+#pragma unroll
+  for (int i = 0; i < QV; ++i) mv = fmaxf(mv, fabsf(vx[i]));
+  mk = wave_max(mk);
+  mv = wave_max(mv);
+  if (lane == 0) {
+    wm[0][wave] = mk;
+    wm[1][wave] = mv;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    mk = fmaxf(fmaxf(wm[0][0], wm[0][1]), fmaxf(wm[0][2], wm[0][3]));
+    mv = fmaxf(fmaxf(wm[1][0], wm[1][1]), fmaxf(wm[1][2], wm[1][3]));
+    kvexp[(long)bh * nchunks + c] = make_int2(exp_above(mk), exp_above(mv));
+  }
+}
+
 template <typename T, int DH, bool PREMAP, int NCW>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gamma_k,
     const float* __restrict__ beta_k, float ln_eps, const float* __restrict__ state_in,
     float* __restrict__ state_out, typename Cx<T>::E* __restrict__ snap, int* __restrict__ sexp,
-    float* __restrict__ sconst, int Hkv, int N, int nchunks) {
+    float* __restrict__ sconst, const int2* __restrict__ kvexp, int Hkv, int N, int nchunks) {
   typedef typename Cx<T>::E E;
   typedef typename Cx<T>::Frag F;
   constexpr int KB = n_kblocks(DH);
@@ -512,15 +563,11 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     }
     if (kload) tb[(lhalf ? ZERO : ONE) * KP + ltok] = (!lhalf && valid) ? (E)1.f : (E)0.f;
   };
-  auto chunk_exps = [&](int slot, int& ek, int& ev) __attribute__((always_inline)) {
-    float mk = 0.f, mv = 0.f;
-#pragma unroll
-    for (int w = 0; w < LWR; ++w) {
-      mk = fmaxf(mk, wmx[slot][w]);
-      mv = fmaxf(mv, wmx[slot][LWR + w]);
-    }
-    ek = exp_above(mk);
-    ev = exp_above(mv);
+  // exponents of chunk c, from the chunk exponent table
+  auto chunk_exps = [&](int c, int& ek, int& ev) __attribute__((always_inline)) {
+    const int2 e = kvexp[(long)bh * nchunks + c];
+    ek = e.x;
+    ev = e.y;
   };
 
   // ---- prologue: chunk 0 staged, maxima of chunk 1 reduced ----
@@ -533,7 +580,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   if (loader) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) R[i] = fetch(min(i, nchunks - 1));
-    convert(R[0], 0, 0);
+    if (PREMAP) convert(R[0], 0, 0);  // the pre-map statistics of the keys
   }
   __syncthreads();
   int Ek = 0, Ev = 0, beta = 0;
@@ -587,7 +634,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
   }
   if (loader) {
     stage(R[0], 0, 0, Ek, Ev + beta);
-    convert(R[1], 1, 1);
+    if (PREMAP) convert(R[1], 1, 1);
     R[0] = fetch(min(NR, nchunks - 1));
   }
   __syncthreads();
@@ -609,13 +656,13 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     int Ek1 = Ek, Ev1 = Ev;  // exponents of chunk c+1
     if (c + 1 < nchunks) {
       int ek, ev;
-      chunk_exps((c + 1) & 1, ek, ev);
+      chunk_exps(c + 1, ek, ev);
       Ek1 = max(Ek, ek);
       Ev1 = max(Ev, ev);
     }
     if constexpr (LOADER) {
       stage(rs, c + 1, (c + 1) & 1, Ek1, Ev1 + beta);
-      convert(rc, c + 2, c & 1);
+      if (PREMAP) convert(rc, c + 2, c & 1);
       rs = fetch(min(c + 1 + NR, nchunks - 1));
     } else {
       // ---- snapshot S_c: raw = stored * 2^(beta + nu Ek) (* 2^Ev for H) ----
@@ -1410,7 +1457,7 @@ namespace {
 
 template <typename T, int DH>
 struct FwdWs {
-  long snap_bytes, exp_off, const_off, total;
+  long snap_bytes, exp_off, const_off, kvexp_off, total;
 };
 
 template <typename T, int DH>
@@ -1424,7 +1471,8 @@ FwdWs<T, DH> fwd_ws(int B, int Hq, int Hkv, int N) {
   w.snap_bytes = snaps * KB * NCOL * 32 * (long)sizeof(E);
   w.exp_off = up(w.snap_bytes);
   w.const_off = w.exp_off + up(snaps * (KB + 2) * 4);
-  w.total = w.const_off + up(snaps * NCOL * 4);
+  w.kvexp_off = w.const_off + up(snaps * NCOL * 4);
+  w.total = w.kvexp_off + up(snaps * 8);  // chunk exponents
   return w;
 }
 
@@ -1459,6 +1507,18 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   const T* vv = reinterpret_cast<const T*>(a.v);
   T* yy = reinterpret_cast<T*>(a.y);
   if (stages & 1) {
+    int2* kvexp = reinterpret_cast<int2*>(ws + w.kvexp_off);
+    {
+      const dim3 egrid(nchunks, BH);
+      if (a.premap)
+        hipLaunchKernelGGL((chunk_exp_kernel<T, DH, true>), egrid, dim3(256), 0, stream, kk, vv, a.gamma_k, a.beta_k,
+                           a.ln_eps, kvexp, a.Hkv, a.N, nchunks);
+      else
+        hipLaunchKernelGGL((chunk_exp_kernel<T, DH, false>), egrid, dim3(256), 0, stream, kk, vv, nullptr, nullptr,
+                           0.f, kvexp, a.Hkv, a.N, nchunks);
+      hipError_t e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
+    }
     // four compute waves per CTA when that grid fits on the 256 compute
     // units in one round (one CTA per unit), else eight
     const bool four = (long)((KB + 1 + 3) / 4) * BH <= 256;
@@ -1467,7 +1527,7 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
 #define OAL_SCAN(PM, NC)                                                                                       \
     hipLaunchKernelGGL((scan_kernel<T, DH, PM, NC>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv,            \
                        PM ? a.gamma_k : nullptr, PM ? a.beta_k : nullptr, PM ? a.ln_eps : 0.f, a.state_in,     \
-                       a.state_out, snap, sexp, sconst, a.Hkv, a.N, nchunks)
+                       a.state_out, snap, sexp, sconst, kvexp, a.Hkv, a.N, nchunks)
     if (a.premap) {
       if (four) OAL_SCAN(true, 4);
       else OAL_SCAN(true, 8);
