@@ -172,6 +172,14 @@ def test_c4_rebased_squared_dot_premap():
     _run_case(S.make(4, batch=2, n_q_heads=2, n_kv_heads=2, seq_len=150, rebased_reading="d"))
 
 
+def test_c4_rebased_squared_dot_premap_many_heads():
+    # pre-map in the scan's eight-compute-wave layout: 16 (sequence, KV head)
+    # pairs at d_h = 64 need more than 256 CTAs with four K-blocks per CTA
+    wl = S.make(4, batch=2, n_q_heads=8, n_kv_heads=8, seq_len=140, rebased_reading="d")
+    assert ((70 + 1 + 3) // 4) * wl.batch * wl.n_kv_heads > 256
+    _run_case(wl)
+
+
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 129])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_edge_lengths(N, dtype):
