@@ -223,7 +223,7 @@ size_t small_segment_bytes(int d_h, bool diagonal) {
 
 // OUT = false: segment sums (kernel 1); OUT = true: outputs (kernel 2).
 template <typename T, int DH, bool DIAG, bool PREMAP, bool OUT>
-__global__ __launch_bounds__(256) void small_fwd_kernel(
+__global__ __launch_bounds__(256, 2) void small_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ group_of_dim, const float* __restrict__ ca, const float* __restrict__ cb,
     const float* __restrict__ cc, int G, const float* __restrict__ gamma_q, const float* __restrict__ beta_q,
