@@ -363,8 +363,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on a single GPU; figures for more GPUs are not produced "
-              "(see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py: the OAL library and this benchmark run on one GPU; no figures for more GPUs are "
+              "produced (batch x KV-head sharding needs no communication and is not implemented).",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
