@@ -211,9 +211,10 @@ int oal_fwd_states(const oal_dims* dims, const void* k, const void* v, const oal
 }
 
 int oal_fwd_outputs(const oal_dims* dims, const void* q, const void* k, const void* v,
-                    const oal_coeffs* coeffs, const oal_prep* prep, void* y, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  return fwd_stages(dims, q, k, v, coeffs, prep, nullptr, nullptr, y, workspace, workspace_bytes, stream, 2);
+                    const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, void* y,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  // state_in only tells the first chunk whether there is an initial state to read
+  return fwd_stages(dims, q, k, v, coeffs, prep, state_in, nullptr, y, workspace, workspace_bytes, stream, 2);
 }
 
 size_t oal_decode_workspace_bytes(const oal_dims* dims) {

@@ -250,7 +250,7 @@ class PrefillPlan:
         self._states_args = (ctypes.byref(self.dims), _ptr(k), _ptr(v), pp, _ptr(state_in), _ptr(self.state_out),
                              *ws, st)
         self._out_args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(self._cs), pp,
-                          _ptr(self.y), *ws, st)
+                          _ptr(state_in), _ptr(self.y), *ws, st)
         self._fwd_args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(self._cs), pp,
                           _ptr(state_in), _ptr(self.state_out), _ptr(self.y), *ws, st)
         self._lib = L.lib()

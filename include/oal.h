@@ -189,14 +189,17 @@ int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v,
  *   oal_fwd_outputs: the Eq. (6) readout against those states plus the
  *                    within-chunk pairs, normalised into y.  The workspace
  *                    must hold the states of a preceding oal_fwd_states call
- *                    with the same dims, k, v, prep and state_in.
+ *                    with the same dims, k, v, prep and state_in.  Its
+ *                    state_in must be that call's pointer: only whether it
+ *                    is null is read (the first chunk then skips the read of
+ *                    the initial state), not the memory behind it.
  * Arguments and errors as for oal_fwd. */
 int oal_fwd_states(const oal_dims* dims, const void* k, const void* v, const oal_prep* prep,
                    const float* state_in, float* state_out, void* workspace, size_t workspace_bytes,
                    void* stream);
 int oal_fwd_outputs(const oal_dims* dims, const void* q, const void* k, const void* v,
-                    const oal_coeffs* coeffs, const oal_prep* prep, void* y, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, void* y,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace oal_decode_step needs for `dims` (0 when none
  * is needed or `dims` is invalid). */

@@ -392,3 +392,30 @@ def test_stages_compose_to_fwd_bitwise():
     plan.outputs()
     torch.cuda.synchronize()
     assert torch.equal(plan.y, y) and torch.equal(plan.state_out, st)
+
+
+def test_stages_compose_with_initial_state():
+    """The two stages given an initial state: the first chunk of the outputs
+    stage must read it (it is not re-read, only whether it exists), so that
+    states() + outputs() equals one fwd call bit for bit and continues a
+    split sequence as the oracle's direct Eq. (6) does."""
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    wl = S.make(2, batch=2, n_q_heads=4, n_kv_heads=2, seq_len=230)
+    co = gpu_coeffs(wl, wl.group_of_dim)
+    q, k, v = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+    n1 = 90
+    head = [t[:, :, :n1].contiguous() for t in (q, k, v)]
+    tail = [t[:, :, n1:].contiguous() for t in (q, k, v)]
+    y1, s1 = oal.fwd(*head, co, return_state=True)
+    y2, s2 = oal.fwd(*tail, co, state_in=s1, return_state=True)
+    plan = oal.PrefillPlan(*tail, co, state_in=s1)
+    plan.states()
+    plan.outputs()
+    torch.cuda.synchronize()
+    assert torch.equal(plan.y, y2) and torch.equal(plan.state_out, s2)
+    a, b, c = oracle_coeffs(wl)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)
+    got = np.concatenate([to_np(y1), to_np(plan.y)], axis=2)
+    assert rel_err(got, ref) <= TOL["bf16"]
