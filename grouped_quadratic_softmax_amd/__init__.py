@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     DecodePlan,
     PrefillPlan,
     Prep,
+    StepPlan,
     coeffs_from_factor,
     contrib,
     decode_step,

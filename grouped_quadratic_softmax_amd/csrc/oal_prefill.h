@@ -54,14 +54,17 @@ namespace {
 constexpr int DV = 64;        // value head dimension handled by these kernels
 constexpr int NCOL = DV + 1;  // value columns + normaliser column
 constexpr int C = kChunk;     // tokens per chunk
-constexpr int KG = 2;         // snapshot K-blocks staged per pipeline step
 // LDS column pitch (elements) of a staged snapshot K-block: 80 bytes (fp16)
 // or 144 bytes (fp32), so that 16 lanes reading 16 bytes each hit distinct banks
-// Elements of one staged group of KG snapshot K-blocks in LDS: KG value
-// blocks of 64 columns x 32 features, then KG z blocks of 32.
-template <typename E>
-__host__ __device__ constexpr int stage_elems() {
-  return KG * (DV * 32 + 32);
+// Snapshot K-blocks the readout stages per pipeline step: two, or three for
+// fp16 snapshots read by a single head slot per pass.  There a two-block
+// stage is 8 KB, so the per-stage wait and barrier rather than the bytes set
+// the pace; three blocks still leave room for two workgroups per compute unit.
+__host__ __device__ constexpr int stage_kblocks(int rmax, int esize) { return rmax == 1 && esize == 2 ? 3 : 2; }
+// Elements of one staged group of kg snapshot K-blocks in LDS: kg value
+// blocks of 64 columns x 32 features, then kg z blocks of 32.
+__host__ __device__ constexpr int stage_elems(int kg) {
+  return kg * (DV * 32 + 32);
 }
 constexpr int kNegExp = -200; // exponent of an all-zero block
 
@@ -814,13 +817,16 @@ __host__ __device__ inline ReadoutLds readout_lds(int RG) {
   L.kh = L.coef + (long)RG * (KB + 1) * 32 * sizeof(E);
   L.vt = L.kh + (long)C * DHP * sizeof(E);
   L.bst = L.vt + (long)DV * (C + 8) * sizeof(T);
-  // three stage buffers of KG K-blocks: value columns, then the z column
-  L.total = L.bst + 3L * stage_elems<E>() * sizeof(E);
+  // three stage buffers of stage_kblocks K-blocks: value columns, then z
+  L.total = L.bst + 3L * stage_elems(stage_kblocks(RG, (int)sizeof(E))) * sizeof(E);
   return L;
 }
 
+// With one head slot a workgroup is four waves and its LDS leaves room for a
+// second one on the compute unit; the register budget of two waves per SIMD
+// lets both run.
 template <typename T, int DH, int RMAX, int NG, bool PREMAP, int NW>
-__global__ __launch_bounds__(64 * NW) void readout_kernel(
+__global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) void readout_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ ca, const float* __restrict__ cb, const float* __restrict__ cc, int G,
     const float* __restrict__ gamma_q, const float* __restrict__ beta_q, const float* __restrict__ gamma_k,
@@ -840,6 +846,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
   constexpr int QD = DH / 4;
   constexpr int NT = 64 * NW;
   constexpr int HS = NW / 4;  // head split between the waves of a row tile
+  constexpr int KG = stage_kblocks(RMAX, (int)sizeof(typename Cx<T>::E));  // K-blocks per stage
 
   extern __shared__ __align__(16) unsigned char lds[];
   const ReadoutLds LL = readout_lds<T, DH>(RMAX);
@@ -892,7 +899,7 @@ __global__ __launch_bounds__(64 * NW) void readout_kernel(
   constexpr int LPT = KG * VPB / NT;            // value vectors per thread and stage
   constexpr int ZV = KG * 32 / VE;              // z vectors per stage (wave 0)
   static_assert(KG * VPB % NT == 0 && ZV <= kWave, "stage split");
-  constexpr int SE = stage_elems<E>();
+  constexpr int SE = stage_elems(KG);
   static_assert(NL <= KG, "one linear stage");
   constexpr int NSTAGE = 1 + (NQ + KG - 1) / KG;
   auto kb_at = [&](int sg, int slot) __attribute__((always_inline)) {

@@ -310,3 +310,37 @@ class ContribPlan:
     def run(self):
         L.check(self._lib.oal_contrib(*self._args), "oal_contrib")
         return self.chi
+
+
+class StepPlan:
+    """One pass of the hot path on fixed buffers, spread over two streams.
+
+    A batch of prompts ``q, k, v [B, H, N, d]`` is prefilled (chunk scan,
+    then the chunk readout), each sequence then decodes one token
+    ``qn, kn, vn [B, H, d]`` on the prefill's final state, and chi (the
+    per-dimension contribution of the prompts' q and k) is reduced.
+
+    The scan, the readout and the decode step run in that order on the stream
+    current at construction.  Chi reads only q and k, so a second stream of
+    default priority runs it from the start of the step, on the compute units
+    that the scan's few workgroups leave idle.  ``run()`` ends with the first
+    stream waiting for the second.  (The decode step stays behind the readout:
+    when the readout has one workgroup per compute unit, a decode launched
+    beside it holds compute units that the readout then waits for.)
+    """
+
+    def __init__(self, q, k, v, qn, kn, vn, coeffs: Coeffs, prep: Optional[Prep] = None):
+        import torch
+        self.main = torch.cuda.current_stream()
+        self.side = torch.cuda.Stream()
+        self.prefill = PrefillPlan(q, k, v, coeffs, prep)
+        self.decode = DecodePlan(qn, kn, vn, coeffs, self.prefill.state_out, prep)
+        with torch.cuda.stream(self.side):
+            self.chi = ContribPlan(q, k)
+
+    def run(self):
+        self.prefill.states()
+        self.chi.run()
+        self.prefill.outputs()
+        self.decode.run()
+        self.main.wait_stream(self.side)

@@ -1,11 +1,11 @@
 """GPU check of the benchmark's step schedule against the fp64 oracle.
 
-The step enqueues chi on a second stream right after the chunk scan, then the
-readout and one decode step per sequence on the main stream, and joins the
-streams at the end of the step (steps may overlap the previous step's side
-work).  Several steps run back to back; every output of the last one must
-match the oracle: chi, the prefill outputs, and the decoded token (whose
-state is the scan's final state plus that token).
+The step (``StepPlan``) runs the chunk scan, the readout and the decode step
+on the main stream; a second stream runs chi from the start of the step, and
+the main stream waits for it at the end of the step.  Several steps run back
+to back; every output of the last one must match the oracle: chi, the
+prefill outputs, and the decoded token (whose state is the scan's final state
+plus that token).
 """
 
 import numpy as np
@@ -30,19 +30,11 @@ def test_two_stream_step_matches_oracle():
     a, b, c = oal.coeffs_from_factor(wl.coeff["eps"], wl.coeff["L"])
     co = oal.Coeffs(wl.group_of_dim, a, b, c)
 
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    pre = oal.PrefillPlan(q, k, v, co)
-    dec = oal.DecodePlan(qn, kn, vn, co, pre.state_out)
-    with torch.cuda.stream(side):
-        chi_plan = oal.ContribPlan(q, k)
+    plan = oal.StepPlan(q, k, v, qn, kn, vn, co)
     for _ in range(5):
-        pre.states()
-        chi_plan.run()
-        pre.outputs()
-        dec.run()
-        main.wait_stream(side)
+        plan.run()
     torch.cuda.synchronize()
+    pre, dec, chi_plan = plan.prefill, plan.decode, plan.chi
 
     ao, bo, co_ = O.coeffs_from_factor(wl.coeff["eps"], wl.coeff["L"])
     ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, ao, bo, co_)
@@ -52,4 +44,40 @@ def test_two_stream_step_matches_oracle():
     chi_err = np.abs(to_np(chi_plan.chi) / chi_ref - 1).max()
     log(f"[step] two-stream schedule: max rel err {err:.3e}, chi {chi_err:.3e}")
     assert err <= TOL["bf16"]
+    assert chi_err <= 1e-4
+
+
+def test_two_stream_step_full_size_sampled():
+    """The same schedule at the timed workload's shape (B=4, Hq=14, Hkv=2,
+    N=2048 prompt tokens + 1 decoded, d_h=d_v=64, G=4), where chi runs
+    beside a scan long enough for the two to overlap: the decoded token,
+    sampled prefill rows and chi against the oracle after several
+    back-to-back steps."""
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    from helpers import sample_rows
+    wl = S.make(2, seq_len=2048 + 1)
+    N = wl.seq_len - 1
+    qa, ka, va = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+    q, k, v = (t[:, :, :N].contiguous() for t in (qa, ka, va))
+    qn, kn, vn = (t[:, :, N].contiguous() for t in (qa, ka, va))
+    a, b, c = oal.coeffs_from_factor(wl.coeff["eps"], wl.coeff["L"])
+    co = oal.Coeffs(wl.group_of_dim, a, b, c)
+    plan = oal.StepPlan(q, k, v, qn, kn, vn, co)
+    for _ in range(4):
+        plan.run()
+    torch.cuda.synchronize()
+
+    rows = np.append(sample_rows(N, 64, 24, seed=11), N)
+    ao, bo, co_ = O.coeffs_from_factor(wl.coeff["eps"], wl.coeff["L"])
+    ref = O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, ao, bo, co_, rows=rows)
+    got = np.concatenate([to_np(plan.prefill.y)[:, :, rows[:-1]], to_np(plan.decode.y)[:, :, None]], axis=2)
+    err = rel_err(got, ref)
+    dec_err = rel_err(got[:, :, -1:], ref[:, :, -1:])
+    _, chi_ref = O.chi_separable(wl.q[:, :, :N], wl.k[:, :, :N])
+    chi_err = np.abs(to_np(plan.chi.chi) / chi_ref - 1).max()
+    log(f"[step] full-size two-stream schedule: rows {err:.3e}, decoded {dec_err:.3e}, chi {chi_err:.3e}")
+    assert err <= TOL["bf16"]
+    assert dec_err <= TOL["bf16"]
     assert chi_err <= 1e-4
