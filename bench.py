@@ -258,7 +258,9 @@ def run_pmc_target(args):
     pass); ``states``: the chunk scan of the main workload; ``based16``: the
     one-pass prefill of the d_h = 16 Based Taylor workload (B=8, H=16,
     N=8192); ``rebased``: the one-pass prefill of the ReBased workload in the
-    dimension-wise form (B=16, H=8, N=2048); ``copy``: a plain device copy of
+    dimension-wise form (B=16, H=8, N=2048); ``long``: the prefill of the
+    long-context multi-head workload (B=1, H=16, N=32768, d_h=64, eight
+    groups from its contribution scores); ``copy``: a plain device copy of
     1 GiB (fp32), whose FETCH_SIZE and WRITE_SIZE readings calibrate the
     counters against a known byte count."""
     import torch
@@ -275,6 +277,18 @@ def run_pmc_target(args):
         torch.cuda.synchronize()
         print(json.dumps({"pmc_target": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
                           "launches": args.steps}), flush=True)
+        return
+    if args.pmc_target == "long":
+        wl = S.make(5)
+        q, k, v = device_inputs(wl)
+        chi = oal.contrib(q, k).cpu().numpy()
+        groups = oal.groups_from_contribution(chi, wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"])
+        pre = oal.PrefillPlan(q, k, v, coeffs_for(wl, groups))
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            pre.run()
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": args.pmc_target, "launches": args.steps}), flush=True)
         return
     if args.pmc_target in ("based16", "rebased"):
         wl = S.make(3 if args.pmc_target == "based16" else 4)
@@ -348,7 +362,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run chi, prefill and decode back to back on one stream")
-    ap.add_argument("--pmc-target", choices=("readout", "states", "based16", "rebased", "copy"), default=None,
+    ap.add_argument("--pmc-target", choices=("readout", "states", "based16", "rebased", "long", "copy"), default=None,
                     help="only launch this kernel --steps times (for rocprofv3 counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
