@@ -74,7 +74,16 @@ __device__ __forceinline__ void feature_pair(int f, int& r, int& t) {
 // Rows per slice (a multiple of 16) and slice count for `states` states.
 void decode_slicing(int d_h, long states, int& rows, int& nslice, bool diagonal) {
   const int D = diagonal ? 1 + 2 * d_h : (int)packed_features(d_h);
-  long want = (2048 + states - 1) / states;           // aim for >= 2048 CTAs
+  // about 512 CTAs (two per compute unit): with 32-128 states, more and
+  // smaller slices only add per-CTA set-up; from 256 states on, up to eight
+  // slices while that keeps >= 2048 CTAs (three slices of 720 rows stream
+  // worse than eight of 272 there)
+  long want = (512 + states - 1) / states;
+  if (states >= 256) {
+    const long a2048 = (2048 + states - 1) / states;
+    const long floor8 = a2048 < 8 ? a2048 : 8;
+    if (want < floor8) want = floor8;
+  }
   want = want < 1 ? 1 : want;
   const long min_slices = (D + 1023) / 1024;           // at most 1024 rows per CTA
   if (want < min_slices) want = min_slices;
