@@ -869,11 +869,12 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
   const int c = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int R = Hq / Hkv;
-  // Builds with eight head slots run short of registers: there the wave
+  // Builds with eight head slots, and the eight-group build with one slot
+  // (held to two waves per SIMD), run short of registers: there the wave
   // index is made scalar and the lanes' LDS offsets are recomputed per stage
   // (values hidden from loop-invariant hoisting), which keeps every spill
-  // out of the stage loop.  Smaller builds keep the offsets live.
-  constexpr bool kTight = RMAX >= 8;
+  // out of the stage loop.  Other builds keep the offsets live.
+  constexpr bool kTight = RMAX >= 8 || (RMAX == 1 && NG == 8 && IsBf16<T>::value);
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = kTight ? __builtin_amdgcn_readfirstlane(tid / kWave) : tid / kWave;
   const int lg = lane / 16, l16 = lane % 16;
