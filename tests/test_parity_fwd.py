@@ -222,6 +222,19 @@ def test_c5_eight_groups_small():
     _run_case(wl, groups=groups)
 
 
+@pytest.mark.parametrize("hq,hkv,dtype", [(14, 2, "bf16"), (6, 2, "bf16"), (4, 2, "bf16"), (4, 2, "f32"),
+                                          (14, 2, "f32")])
+def test_eight_groups_grouped_query_heads(hq, hkv, dtype):
+    """Eight contribution-derived groups with several query heads per KV head:
+    the readout builds with eight, four and two head slots (seven query heads
+    leave one slot dead), the ones that run shortest of registers."""
+    require_gpu()
+    wl = S.make(5, batch=2, n_q_heads=hq, n_kv_heads=hkv, seq_len=200, dtype=dtype)
+    groups = _groups_from_gpu_chi(wl, to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype))
+    assert groups.max() == 7
+    _run_case(wl, groups=groups)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_many_kv_heads_eight_wave_scan(dtype):
     # 16 (sequence, KV head) pairs at d_h = 64: the scan grid with four
