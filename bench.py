@@ -189,12 +189,26 @@ def run_main(args):
 
 
 def run_secondary(args):
+    import numpy as np
     import torch
     import grouped_quadratic_softmax_amd as oal
     import synthetic as S
 
     out = {}
     steps, warm = max(3, args.steps // 5), 2
+    # the same GQA layer (B=4, N=2048, Hq=14, Hkv=2) with eight groups of
+    # eight dimensions: the readout alone (its eight-group build)
+    wl = S.make(2, seq_len=2048)
+    q, k, v = device_inputs(wl)
+    rng = np.random.default_rng(2048)
+    a8, b8, c8 = oal.coeffs_from_factor(1e-3, rng.standard_normal((wl.n_q_heads, 9, 9)))
+    g8 = np.repeat(np.arange(8, dtype=np.int32), 8)[None, :].repeat(wl.n_q_heads, 0)
+    pre = oal.PrefillPlan(q, k, v, oal.Coeffs(g8, a8, b8, c8))
+    pre.states()
+    ms = time_events(pre.outputs, steps, warm)
+    flops = wl.batch * wl.seq_len * wl.n_q_heads * 2 * feature_count(64) * (DV + 1)
+    out["c2_gqa_g8_readout"] = {"ms": ms, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    del pre, q, k, v
     # d_h = 16 Based Taylor prefill, B=8, H=16, N=8192 (HBM-bound)
     wl = S.make(3)
     q, k, v = device_inputs(wl)
