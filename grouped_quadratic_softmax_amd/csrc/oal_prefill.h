@@ -1188,6 +1188,11 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
 #pragma unroll
       for (int n = 0; n < 5; ++n) cur[n] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int jt0 = 0; jt0 <= rt; jt0 += 2) {
+        // With eight groups the 45 distinct polynomial coefficients, hoisted
+        // out of this loop, would sit in registers for the whole block and
+        // push the build into spills; there they are re-read from LDS per
+        // key tile (the row pointer is hidden from loop-invariant hoisting).
+        const float* pck = NG >= 8 ? pc[opaque<true>(hh)] : pcr;
         float p[8];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -1217,12 +1222,12 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
             float sv[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) sv[g] = sg[g][e] * sfac;
-            float kap = pcr[0];
+            float kap = pck[0];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-              float inner = pcr[1 + g] + pcr[1 + NG + g * NG + g] * sv[g];
+              float inner = pck[1 + g] + pck[1 + NG + g * NG + g] * sv[g];
 #pragma unroll
-              for (int g2 = g + 1; g2 < NG; ++g2) inner += 2.f * pcr[1 + NG + g * NG + g2] * sv[g2];
+              for (int g2 = g + 1; g2 < NG; ++g2) inner += 2.f * pck[1 + NG + g * NG + g2] * sv[g2];
               kap += sv[g] * inner;
             }
             const int key = 16 * jt + 4 * lg + e;
