@@ -878,12 +878,16 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
   const int c = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int R = Hq / Hkv;
-  // Builds with eight head slots, and the eight-group build with one slot
-  // (held to two waves per SIMD), run short of registers: there the wave
+  // Builds with eight head slots, and the eight-group builds with one slot
+  // (held to two waves per SIMD) or four, run short of registers (measured
+  // gains: one slot 899 -> 830 us on the 32k-token prefill, four slots
+  // 96 -> 76 us; the two-slot eight-group build is faster without, 49 us
+  // against 54, although it spills 124 bytes per lane): there the wave
   // index is made scalar and the lanes' LDS offsets are recomputed per stage
-  // (values hidden from loop-invariant hoisting), which keeps every spill
-  // out of the stage loop.  Other builds keep the offsets live.
-  constexpr bool kTight = RMAX >= 8 || (RMAX == 1 && NG == 8 && IsBf16<T>::value);
+  // (values hidden from loop-invariant hoisting), which keeps the spills out
+  // of the stage loop (one reload is left in the eight-slot eight-group
+  // build).  Other builds keep the offsets live.
+  constexpr bool kTight = RMAX >= 8 || (NG == 8 && IsBf16<T>::value && (RMAX == 1 || RMAX == 4));
   // The eight-slot eight-group build still spilled the lane index out of the
   // stage loop; there it is re-derived from the hardware at each use
   // (measured: 116-117 -> 111-112 us; the four-group build lost 2 us with it).
