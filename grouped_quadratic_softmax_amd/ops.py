@@ -323,8 +323,10 @@ class StepPlan:
     The scan, the readout and the decode step run in that order on the stream
     current at construction.  Chi reads only q and k, so a second stream of
     default priority runs it from the start of the step, on the compute units
-    that the scan's few workgroups leave idle.  ``run()`` ends with the first
-    stream waiting for the second.  (The decode step stays behind the readout:
+    that the scan's few workgroups leave idle.  ``run()`` starts with the
+    second stream waiting for the first (so chi sees inputs produced earlier
+    on it, and the previous step's consumers of the chi buffer are done) and
+    ends with the first stream waiting for the second.  (The decode step stays behind the readout:
     when the readout has one workgroup per compute unit, a decode launched
     beside it holds compute units that the readout then waits for.)
     """
@@ -339,6 +341,7 @@ class StepPlan:
             self.chi = ContribPlan(q, k)
 
     def run(self):
+        self.side.wait_stream(self.main)
         self.prefill.states()
         self.chi.run()
         self.prefill.outputs()

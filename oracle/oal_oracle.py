@@ -72,6 +72,7 @@ __all__ = [
     "matrix_from_abi_state",
     "group_dims_bootstrap",
     "group_dims_budget",
+    "groups_sorted_split",
 ]
 
 
@@ -537,3 +538,35 @@ def group_dims_budget(chi, n_groups, eps=1e-12):
     order = sorted(range(1, d), key=lambda k: -rho[k])  # stable
     cuts = order[:n_groups - 1]
     return _groups_from_cuts(pi, cuts), rho
+
+
+def groups_sorted_split(chi, bulk_sizes, n_tail):
+    """Contribution-sorted split with a fixed group budget, one head at a time.
+
+    The grouping of the long-context workload: [OAL] sec. 4.2 and App. B sort
+    the dimensions of a head by ascending chi_r (Eq. (2)) with a stable sort
+    (equal scores keep index order) and place the boundaries in that order.
+    Here the budget is fixed: the last ``n_tail`` sorted positions become
+    singleton groups and the rest, still in sorted order, are cut into
+    contiguous runs of ``bulk_sizes``.  Group ids: 0, 1, ... for the bulk runs
+    (lowest contribution first), then the tail singletons in ascending chi.
+
+    chi: [H][d] scores -> [H][d] group ids (pure Python loops).
+    """
+    out = []
+    for row in chi:
+        d = len(row)
+        if sum(bulk_sizes) + n_tail != d:
+            raise ValueError("bulk sizes plus tail must cover the head dimensions")
+        pi = _sorted_order([float(x) for x in row])
+        gid = [0] * d
+        pos = 0
+        for g, size in enumerate(bulk_sizes):
+            for _ in range(size):
+                gid[pi[pos]] = g
+                pos += 1
+        for i in range(n_tail):
+            gid[pi[pos]] = len(bulk_sizes) + i
+            pos += 1
+        out.append(gid)
+    return np.array(out, dtype=np.int64)

@@ -48,6 +48,85 @@ def test_fp32_path_is_bit_exact_on_dyadic_inputs():
         assert np.array_equal(got, want)
 
 
+def _sparse_dyadic_case(seed, d, dtype, diagonal, B=2, Hq=4, Hkv=2, N=160, G=4):
+    """Inputs on which every operand of every path is exact in bf16 (8
+    significant bits), so the kernels' (num, den) are exact whatever the
+    operand format (fp32, fp16 or bf16) and the accumulation order.
+
+    Every token of q and k has exactly two nonzero dimensions, each +-1, and
+    v is in {-1, 0, 1}: a state entry is an integer of magnitude <= N, every
+    group score s_g is in {0, +-1, +-2} / sqrt(d_h), and with a = 2, b in
+    {+-1/2} and c from {0, 1, 2} every kernel value is a multiple of 1/64
+    below 4 (at most 8 significant bits) and >= 1 (positive denominators).  At d_h = 32, sqrt(d_h) is irrational, so b = 0 there (the
+    quadratic term carries 1/d_h, which is dyadic).  The dimension-wise form
+    (singleton groups, diagonal c) uses c_rr in {1, 2}.
+    """
+    rng = np.random.default_rng(seed)
+
+    def two_hot(shape):
+        x = np.zeros(shape + (d,), np.float32)
+        for idx in np.ndindex(*shape):
+            dims = rng.choice(d, size=2, replace=False)
+            x[idx + (dims,)] = rng.choice([-1.0, 1.0], size=2)
+        return x
+
+    q, k = two_hot((B, Hq, N)), two_hot((B, Hkv, N))
+    v = rng.integers(-1, 2, size=(B, Hkv, N, 64)).astype(np.float32)
+    if diagonal:
+        G = d
+        groups = np.stack([rng.permutation(d) for _ in range(Hq)]).astype(np.int32)
+        c = np.stack([np.diag(rng.integers(1, 3, size=d).astype(np.float64)) for _ in range(Hq)])
+    else:
+        groups = np.stack([rng.permutation(np.arange(d) % G) for _ in range(Hq)]).astype(np.int32)
+        w = (rng.random((Hq, G)) < 0.5).astype(np.float64)
+        c = np.eye(G)[None] + w[:, :, None] * w[:, None, :]  # I + w w^T: PSD, entries in {0, 1, 2}
+    b = rng.choice([-0.5, 0.5], size=(Hq, G))
+    if d == 32:
+        b[:] = 0.0
+    a = np.full(Hq, 2.0)
+    return q, k, v, groups, a, b, c
+
+
+def _ulp(x, dtype):
+    """Spacing of the output format at |x| (float32 or bfloat16)."""
+    x = np.abs(np.asarray(x, np.float32))
+    e = np.floor(np.log2(np.maximum(x, np.float32(2.0 ** -126))))
+    return np.ldexp(1.0, (e - (23 if dtype == "f32" else 7)).astype(np.int32))
+
+
+@pytest.mark.parametrize("d,dtype,diagonal", [(16, "bf16", False), (16, "f32", False), (32, "bf16", False),
+                                              (32, "f32", False), (64, "bf16", False), (16, "bf16", True),
+                                              (64, "bf16", True), (32, "f32", True)])
+def test_exact_on_sparse_dyadic_inputs(d, dtype, diagonal):
+    """Every build (fp32, the bf16-input chunk kernels, the one-pass kernels
+    and the dimension-wise form) on inputs where all operands are exact: the
+    output equals the oracle's y rounded once to the output format; the only
+    freedom left is the rounding of the final division (one unit in the last
+    place).  A wrong group id, head map or mask changes y by far more."""
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    q, k, v, groups, a, b, c = _sparse_dyadic_case(100 + d, d, dtype, diagonal)
+    y_ref, num, den = O.attention_direct(q, k, v, groups, a, b, c, return_parts=True)
+    # premises: numerator and denominator are exact in float32, den >= 1
+    assert np.array_equal(num.astype(np.float32).astype(np.float64), num)
+    assert np.array_equal(den.astype(np.float32).astype(np.float64), den)
+    assert den.min() >= 1.0
+    co = oal.Coeffs(groups, a.astype(np.float32), b.astype(np.float32), c.astype(np.float32))
+    assert co.diagonal == diagonal
+    y = oal.fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), co)
+    got = to_np(y)
+    want = y_ref.astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        want = S.bf16_round(want.astype(np.float32)).astype(np.float64)
+    diff = np.abs(got - want)
+    exact = int((diff == 0).sum())
+    log(f"[exact] d={d} {dtype} diagonal={diagonal}: exact {exact} of {got.size}, max diff in ulps "
+        f"{float((diff / _ulp(want, dtype)).max()):.2f}")
+    assert (diff <= _ulp(want, dtype)).all()
+    # rows whose output is exactly representable (e.g. y_1 = v_1) must be exact
+    assert np.array_equal(got[:, :, 0], want[:, :, 0])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_causal_mask_with_one_hot_values(dtype):
     require_gpu()

@@ -30,6 +30,15 @@ def test_ties_keep_index_order():
     assert groups_from_contribution(chi, [2], 2).tolist() == [[0, 0, 1, 2]]
 
 
+def test_sorted_split_matches_oracle_with_ties():
+    """The library's contribution-sorted split and the oracle's (written from
+    the pages separately) give identical maps, also with many exact ties."""
+    rng = np.random.default_rng(21)
+    bulk, tail = [11, 11, 10, 10, 10, 10], 2
+    for chi in (rng.random((5, 64)), np.round(rng.random((5, 64)) * 4) / 4):
+        assert np.array_equal(groups_from_contribution(chi, bulk, tail), O.groups_sorted_split(chi, bulk, tail))
+
+
 def test_bad_budget():
     with pytest.raises(ValueError):
         groups_from_contribution(np.zeros((1, 4)), [2], 1)

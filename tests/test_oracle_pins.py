@@ -37,9 +37,36 @@ def test_state_entry_count_matches_pages(golden):
 
 
 def test_factor_parameter_count(golden):
+    """The factor map (eps, L) -> (a, b, c) of the positive group-aware kernel
+    has the printed number of free parameters: at a generic lower-triangular
+    L with positive diagonal, the Jacobian of the independent outputs (a, b
+    and the upper triangle of the symmetric c) with respect to the
+    lower-triangular entries of L is square, of size (G+1)(G+2)/2, and of full
+    rank (M = L L^T is a local bijection there).  A map that dropped an entry
+    of L, or wrote an asymmetric c, fails the rank or the symmetry check."""
+    rng = np.random.default_rng(39)
     for G, n in golden("state_counts.json")["params"]:
-        L = np.tril(np.ones((G + 1, G + 1)))
-        assert int(L.sum()) == n
+        tri = [(i, j) for i in range(G + 1) for j in range(i + 1)]
+        assert len(tri) == n
+        L0 = np.zeros((G + 1, G + 1))
+        for (i, j) in tri:
+            L0[i, j] = rng.uniform(0.5, 1.5) if i == j else rng.uniform(-0.5, 0.5)
+
+        def outputs(Lm):
+            a, b, c = O.coeffs_from_factor(0.0, Lm)
+            assert np.array_equal(c, c.T)
+            iu = np.triu_indices(G)
+            return np.concatenate([[a], b, c[iu]])
+
+        assert outputs(L0).size == n
+        h = 1e-6
+        J = np.zeros((n, n))
+        for col, (i, j) in enumerate(tri):
+            Lp, Lm = L0.copy(), L0.copy()
+            Lp[i, j] += h
+            Lm[i, j] -= h
+            J[:, col] = (outputs(Lp) - outputs(Lm)) / (2 * h)
+        assert np.linalg.matrix_rank(J, tol=1e-6) == n
 
 
 # ---------------------------------------------------------------- closed forms
@@ -321,6 +348,21 @@ def test_abi_state_layout_roundtrip():
 
 # ---------------------------------------------------------------- ReBased readings
 
+def test_premap_affine_golden(golden):
+    """gamma and beta of the ReBased pre-map, against hand-worked values:
+    gamma scales the normalised value, beta is added after the scaling, and
+    the LayerNorm epsilon is added to the biased variance inside the root."""
+    g = golden("premap_affine.json")
+    for case in g["cases"]:
+        got = O.premap(np.array(case["x"], float), np.array(case["gamma"], float), np.array(case["beta"], float),
+                       case["eps"])
+        assert np.allclose(got, case["want"], rtol=1e-15, atol=1e-15), (case, got)
+    # over a batch of rows the map acts row by row
+    rows = np.array([g["cases"][0]["x"], g["cases"][0]["x"]], float)
+    got = O.premap(rows, np.array(g["cases"][0]["gamma"]), np.array(g["cases"][0]["beta"]), 2.0)
+    assert np.array_equal(got, np.array([g["cases"][0]["want"]] * 2))
+
+
 def test_rebased_premap_and_feature_readings():
     rng = np.random.default_rng(14)
     d = 16
@@ -449,3 +491,35 @@ def test_grouping_budget_rule():
     assert O.group_dims_budget([1, 2, 3, 30, 4], 5)[0] == [0, 1, 2, 4, 3]
     # equal scores keep index order: sorted dims 1, 3, 0, 2; one gap of 5
     assert O.group_dims_budget([5, 1, 5, 1], 2)[0] == [1, 0, 1, 0]
+
+
+# ---------------------------------------------------------------- contribution-sorted split
+
+def test_groups_sorted_split_golden(golden):
+    g = golden("sorted_split.json")
+    got = O.groups_sorted_split([g["chi"]], g["bulk_sizes"], g["n_tail"])
+    assert got.tolist() == [g["want"]]
+
+
+def test_groups_sorted_split_properties():
+    """Every dimension gets exactly one group; bulk groups have the requested
+    sizes; every dimension of a higher group has a score >= every dimension
+    of a lower group (contiguous runs of the ascending order); the top n_tail
+    scores are singletons; and a permutation of the scores permutes the map
+    (no dependence on position except through ties)."""
+    rng = np.random.default_rng(77)
+    bulk, tail = [11, 11, 10, 10, 10, 10], 2
+    chi = rng.random((3, 64))
+    gid = O.groups_sorted_split(chi, bulk, tail)
+    for h in range(3):
+        sizes = np.bincount(gid[h], minlength=8)
+        assert sizes.tolist() == bulk + [1, 1]
+        for g in range(7):
+            assert chi[h][gid[h] == g].max() <= chi[h][gid[h] == g + 1].min()
+        top = np.argsort(chi[h])[-2:]
+        assert gid[h][top].tolist() == [6, 7]
+        perm = rng.permutation(64)
+        gp = O.groups_sorted_split(chi[h:h + 1, perm], bulk, tail)[0]
+        assert np.array_equal(gp, gid[h][perm])
+    with pytest.raises(ValueError):
+        O.groups_sorted_split(chi, [10], 2)

@@ -208,29 +208,62 @@ def test_d32(dtype):
     _run_case(_d32_workload(dtype))
 
 
-def _groups_from_gpu_chi(wl, q, k):
+# Relative accuracy of the library's fp32 chi (non-negative terms, blocked
+# fp32 sums) against the oracle's fp64 value.
+CHI_RTOL = 2e-5
+
+
+def _c5_groups(wl, q, k):
+    """Group map of the contribution-sorted workload, taken from the oracle:
+    chi by the oracle's separable form of Eq. (2), split by the oracle's
+    stable sort.  The HIP path's chi, split by the library's host helper,
+    must give the same map bit for bit; where two dimensions' scores sit
+    closer than the fp32 accuracy of chi across a group boundary, either
+    order is a correct split, and the library's map must then be a valid
+    split of the oracle's scores within that accuracy (same group sizes,
+    every higher group's scores >= every lower group's, up to CHI_RTOL)."""
     import grouped_quadratic_softmax_amd as oal
-    chi = oal.contrib(q, k).cpu().numpy()
-    return oal.groups_from_contribution(chi, wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"])
+    bulk, tail = wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"]
+    _, chi_o = O.chi_separable(wl.q, wl.k)
+    g_o = O.groups_sorted_split(chi_o, bulk, tail).astype(np.int32)
+    chi_g = oal.contrib(q, k).cpu().numpy().astype(np.float64)
+    chi_err = float(np.abs(chi_g / chi_o - 1.0).max())
+    assert chi_err <= CHI_RTOL, chi_err
+    g_g = oal.groups_from_contribution(chi_g, bulk, tail)
+    cuts = np.cumsum(list(bulk) + [1] * tail)[:-1]
+    srt = np.sort(chi_o, axis=1)
+    gap = float(((srt[:, cuts] - srt[:, cuts - 1]) / srt[:, cuts]).min())
+    log(f"[fwd]   chi max rel err {chi_err:.2e}; smallest relative gap at a group boundary {gap:.2e}")
+    if gap > 2 * CHI_RTOL:
+        assert np.array_equal(g_g, g_o)
+    else:
+        G = len(bulk) + tail
+        for h in range(chi_o.shape[0]):
+            assert np.array_equal(np.bincount(g_g[h], minlength=G), np.bincount(g_o[h], minlength=G))
+            for g in range(G - 1):
+                lo, hi = chi_o[h][g_g[h] == g].max(), chi_o[h][g_g[h] == g + 1].min()
+                assert lo <= hi * (1 + 2 * CHI_RTOL), (h, g)
+    return g_o
 
 
 def test_c5_eight_groups_small():
     require_gpu()
     wl = S.make(5, n_q_heads=4, n_kv_heads=4, seq_len=260)
-    groups = _groups_from_gpu_chi(wl, to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype))
+    groups = _c5_groups(wl, to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype))
     assert groups.max() == 7
     _run_case(wl, groups=groups)
 
 
-@pytest.mark.parametrize("hq,hkv,dtype", [(14, 2, "bf16"), (6, 2, "bf16"), (4, 2, "bf16"), (4, 2, "f32"),
-                                          (14, 2, "f32")])
+@pytest.mark.parametrize("hq,hkv,dtype", [(14, 2, "bf16"), (12, 2, "bf16"), (10, 2, "bf16"), (8, 2, "bf16"),
+                                          (6, 2, "bf16"), (4, 2, "bf16"), (4, 2, "f32"), (14, 2, "f32")])
 def test_eight_groups_grouped_query_heads(hq, hkv, dtype):
     """Eight contribution-derived groups with several query heads per KV head:
-    the readout builds with eight, four and two head slots (seven query heads
-    leave one slot dead), the ones that run shortest of registers."""
+    the readout builds with eight, four and two head slots, the ones that run
+    shortest of registers, with every slot live (8, 4 and 2 query heads per
+    KV head) and with dead slots (7, 6, 5 and 3)."""
     require_gpu()
     wl = S.make(5, batch=2, n_q_heads=hq, n_kv_heads=hkv, seq_len=200, dtype=dtype)
-    groups = _groups_from_gpu_chi(wl, to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype))
+    groups = _c5_groups(wl, to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype))
     assert groups.max() == 7
     _run_case(wl, groups=groups)
 
@@ -372,8 +405,25 @@ def test_c2_full_size_sampled():
 
 
 def test_c3_full_size_sampled():
+    """Based workload at full size: a seeded sample of rows over every
+    (sequence, head), plus the first and last row of every 64-token chunk of
+    one (sequence, head)."""
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
     wl = S.make(3)
-    _run_case(wl, rows=sample_rows(wl.seq_len, 512, 48, seed=3))
+    q, k, v = to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype), to_dev(wl.v, wl.dtype)
+    y = to_np(oal.fwd(q, k, v, gpu_coeffs(wl, wl.group_of_dim)))
+    a, b, c = oracle_coeffs(wl)
+    rows = sample_rows(wl.seq_len, 512, 48, seed=3)
+    err = rel_err(y[:, :, rows], O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c, rows=rows))
+    bi, h = 5, 11
+    edge = sample_rows(wl.seq_len, 64, 0, seed=0)
+    sl = lambda x: x[bi:bi + 1, h:h + 1]
+    err_e = rel_err(y[bi, h, edge], O.attention_direct(sl(wl.q), sl(wl.k), sl(wl.v), wl.group_of_dim[h:h + 1],
+                                                       a[h:h + 1], b[h:h + 1], c[h:h + 1], rows=edge)[0, 0])
+    log(f"[fwd] c3 full size: sampled rows {err:.3e}, every chunk edge of (b={bi}, h={h}) {err_e:.3e}")
+    assert np.isfinite(y).all()
+    assert max(err, err_e) <= TOL["bf16"]
 
 
 def test_c4_full_size_sampled():
@@ -384,12 +434,27 @@ def test_c4_full_size_sampled():
 
 
 def test_c5_full_size_sampled():
+    """Long-context workload at full size with the oracle's group map: random
+    rows over every head, plus the first and last row of every 64-token chunk
+    of one head."""
     require_gpu()
+    import grouped_quadratic_softmax_amd as oal
     wl = S.make(5)
-    groups = _groups_from_gpu_chi(wl, to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype))
+    q, k, v = to_dev(wl.q, wl.dtype), to_dev(wl.k, wl.dtype), to_dev(wl.v, wl.dtype)
+    groups = _c5_groups(wl, q, k)
+    y = to_np(oal.fwd(q, k, v, gpu_coeffs(wl, groups)))
+    a, b, c = oracle_coeffs(wl)
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([rng.integers(0, wl.seq_len, 40), [0, 63, 64, 4095, 4096, wl.seq_len - 1]]))
-    _run_case(wl, groups=groups, rows=rows)
+    err = rel_err(y[:, :, rows], O.attention_direct(wl.q, wl.k, wl.v, groups, a, b, c, rows=rows))
+    h = 9
+    edge = sample_rows(wl.seq_len, 64, 0, seed=0)
+    sl = lambda x: x[:, h:h + 1]
+    err_e = rel_err(y[0, h, edge], O.attention_direct(sl(wl.q), sl(wl.k), sl(wl.v), groups[h:h + 1], a[h:h + 1],
+                                                      b[h:h + 1], c[h:h + 1], rows=edge)[0, 0])
+    log(f"[fwd] c5 full size: sampled rows {err:.3e}, every chunk edge of head {h} {err_e:.3e}")
+    assert np.isfinite(y).all()
+    assert max(err, err_e) <= TOL["bf16"]
 
 
 def test_stages_compose_to_fwd_bitwise():
