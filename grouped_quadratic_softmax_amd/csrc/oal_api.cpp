@@ -128,6 +128,9 @@ size_t oal_fwd_workspace_bytes(const oal_dims* dims) {
 size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs) {
   if (coeffs == nullptr || check_dims(dims, true) != OAL_OK) return 0;
   const bool diagonal = coeffs->diagonal != 0;
+  if (oal::onepass16_supported(dims->d_h, dims->dtype, diagonal, dims->n_groups, dims->n_q_heads,
+                               dims->n_kv_heads))
+    return oal::onepass16_workspace_bytes(dims->batch, dims->n_kv_heads, dims->seq_len);
   if (!oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads))
     return diagonal ? 0 : oal_fwd_workspace_bytes(dims);
   return oal::small_workspace_bytes(dims->batch, dims->n_kv_heads, dims->seq_len, dims->d_h, diagonal,
@@ -144,13 +147,16 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   const bool want_states = stages & 1, want_out = stages & 2;
   int st = check_dims(dims, true);
   if (st != OAL_OK) return st;
-  bool diagonal = false, small = false;
+  bool diagonal = false, small = false, onepass = false;
   if (want_out) {
     if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
     if ((st = check_coeff_ptrs(coeffs)) != OAL_OK) return st;
     diagonal = coeffs->diagonal != 0;
     // one-call prefill of a small feature space (the dimension-wise form)
     small = want_states && oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads);
+    // one-call prefill at d_h = 16 with the state on chip
+    onepass = want_states && oal::onepass16_supported(dims->d_h, dims->dtype, diagonal, dims->n_groups,
+                                                      dims->n_q_heads, dims->n_kv_heads);
     if (diagonal && !small) return OAL_ERR_UNSUPPORTED;  // no separate stages for this form
     if (!small && dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
   }
@@ -169,7 +175,7 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   if (want_out && (q == nullptr || y == nullptr)) return OAL_ERR_INVALID_ARG;
   if (want_states && state_out != nullptr && state_out == state_in) return OAL_ERR_INVALID_ARG;
   if (!all_aligned16({q, k, v, y, state_in, state_out, workspace})) return OAL_ERR_INVALID_ARG;
-  if (!small) {  // the small path takes any workspace
+  if (!small && !onepass) {  // the one-pass paths take any workspace
     const size_t need = oal_fwd_workspace_bytes(dims);
     if (workspace == nullptr || workspace_bytes < need) return OAL_ERR_WORKSPACE;
   }
@@ -188,6 +194,10 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   }
   a.state_in = state_in; a.state_out = state_out; a.y = y; a.workspace = workspace;
   a.diagonal = diagonal;
+  if (onepass)
+    return oal::launch_onepass16(a, workspace ? workspace_bytes : 0, (hipStream_t)stream) == hipSuccess
+               ? OAL_OK
+               : OAL_ERR_HIP;
   if (small)
     return oal::launch_fwd_small(a, workspace ? workspace_bytes : 0, (hipStream_t)stream) == hipSuccess
                ? OAL_OK

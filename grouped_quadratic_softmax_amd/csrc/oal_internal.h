@@ -59,6 +59,12 @@ size_t small_segment_bytes(int d_h, bool diagonal);
 // workspace that lets the small path use its full number of segments
 size_t small_workspace_bytes(int B, int Hkv, int N, int d_h, bool diagonal, int dtype);
 hipError_t launch_fwd_small(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
+// One-pass prefill at d_h = 16 with bf16 activations: the state stays in MFMA
+// accumulators; sequences are cut into segments whose starting states come
+// from block sums in the workspace (one segment without a workspace).
+bool onepass16_supported(int d_h, int dtype, bool diagonal, int G, int Hq, int Hkv);
+size_t onepass16_workspace_bytes(int B, int Hkv, int N);
+hipError_t launch_onepass16(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStream_t stream);
 void decode_slicing(int d_h, long states, int& rows, int& nslice, bool diagonal);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h);

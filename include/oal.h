@@ -162,7 +162,14 @@ size_t oal_fwd_workspace_bytes(const oal_dims* dims);
  * per-segment sums (an F x 65 fp32 block per segment and batch x KV head).
  * There oal_fwd accepts any workspace, including none: a smaller one only
  * means fewer segments (the results are the same up to fp32 rounding
- * order).  For every other case the figure is oal_fwd_workspace_bytes(dims). */
+ * order).
+ *
+ * The grouped form at d_h = 16 with bf16 activations (G <= 8, Hq / Hkv <= 8)
+ * is prefilled the same way, with the whole state (153 packed features x
+ * (d_v + 1), App. D) held in MFMA accumulators; its workspace holds the
+ * per-block sums (a 160 x 65 fp32 block per block of chunks and batch x KV
+ * head) and again may be of any size, including none.  For every other case
+ * the figure is oal_fwd_workspace_bytes(dims). */
 size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs);
 
 /* Causal prefill (paper, Eqs. (5)-(6), evaluated chunk by chunk).
@@ -173,8 +180,9 @@ size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeff
  *   state_out:  NULL or [B, Hkv, oal_state_floats]; receives the states after
  *               the last token (may not alias state_in).
  *   workspace:  device scratch of at least oal_fwd_workspace_bytes(dims)
- *               (for the dimension-wise form, any size: see
- *               oal_fwd_workspace_bytes_for); undefined after the call.
+ *               (for the dimension-wise form and the grouped form at
+ *               d_h = 16 in bf16, any size: see oal_fwd_workspace_bytes_for);
+ *               undefined after the call.
  * Calls that share a workspace must be ordered on one stream. */
 int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v,
             const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, float* state_out,
