@@ -1,20 +1,22 @@
 #!/usr/bin/env python3
 """Causal OAL attention throughput on one MI355X.
 
-Workload (default): the Qwen2.5-0.5B-shaped attention layer -- B = 4 sequences
-of N = 2048 tokens, 14 query heads over 2 KV heads (GQA), d_h = d_v = 64,
-bf16, 4 dimension groups (two planted outlier singletons + two bulk groups),
-seeded synthetic inputs.  One step is one pass of the whole hot path over that
-batch: contribution scores chi (Eq. (2)), the chunked causal prefill (chunk
-states, then readout + within-chunk pairs + normalisation) keeping the final
-states, and one recurrent decode step per sequence on those states.
+Workload (default): the Based Taylor kernel (one group, a = 1, b = 1,
+c = 1/2) on a d_h = 16 projected feature space -- B = 8 sequences of N = 8192
+tokens, 16 heads, d_v = 64, bf16, seeded synthetic inputs.  One step is one
+pass of the whole hot path over that batch: contribution scores chi
+(Eq. (2)), the causal prefill keeping the final states (Eqs. (5)-(6)), and one
+recurrent decode step per sequence on those states.
 
 Prints ONE JSON line.  `value` is tokens/s over the whole step (prefill tokens
-plus decoded tokens); `roofline` is the dominant kernel (the chunk readout)
-timed with HIP events on its own stream; `cpu_baseline` is the fp64 oracle on
-the host.  Secondary lines (under "secondary") time the other workloads' hot
-kernels: the d_h = 16 Based prefill (HBM-bound), the 32k-token prefill and the
-batched decode step with 256 x 16 fp32 states (HBM-bound).
+plus decoded tokens).  `roofline` is the prefill (its HBM fraction binds;
+its bf16 MFMA fraction is given beside it), timed with HIP events on its
+own stream; `roofline_decode` is the batched decode step of 256 sequences x
+16 heads with fp32 states (HBM-bound); `ceilings` are the in-place stream and
+MFMA-chain probes measured in the same run; `cpu_baseline` is the fp64
+oracle on the host.  Secondary lines (under "secondary") time the other
+workloads' hot kernels: the Qwen-shaped GQA layer, the ReBased prefill and the
+32k-token prefill.
 """
 
 from __future__ import annotations
@@ -31,8 +33,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 COPY_BYTES = 1 << 30        # calibration copy for the HBM byte counters
+STREAM_BYTES = 2 << 30      # in-place stream probe (read and written once each)
 METRIC = "causal OAL attention tokens/s at 1 GPU; % bf16 MFMA peak (prefill), % HBM BW (decode)"
 DV = 64
+DECODE_SEQS, DECODE_HEADS = 256, 16
 
 
 def feature_count(d):
@@ -48,7 +52,7 @@ def load_traffic(key):
     except (OSError, ValueError):
         return None
     from grouped_quadratic_softmax_amd.profiling import source_hash
-    if not rec or rec.get("source_sha256") != source_hash():
+    if not rec or rec.get("source_sha256") != source_hash(rec.get("sources")):
         return None
     return rec.get("bytes_per_launch")
 
@@ -70,6 +74,8 @@ def coeffs_for(wl, groups=None):
 
 
 def time_events(fn, steps, warmup):
+    """Mean duration (ms) of fn() over `steps` calls, HIP events recorded on
+    the current stream (the stream the plans below launch on)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -84,12 +90,36 @@ def time_events(fn, steps, warmup):
     return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps  # ms
 
 
+def measure_ceilings():
+    """The in-place read+write stream probe over 2 GiB and the bf16 MFMA
+    chain probe (include/oal_ceilings.h), each timed with HIP events."""
+    import ctypes
+    import torch
+    from grouped_quadratic_softmax_amd import _lib as L
+    lib = L.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    buf = torch.zeros(STREAM_BYTES // 4, device="cuda", dtype=torch.float32)
+    ms = time_events(lambda: L.check(lib.oal_ceiling_stream_rw(ctypes.c_void_p(buf.data_ptr()),
+                                                                ctypes.c_size_t(buf.numel()), stream),
+                                     "oal_ceiling_stream_rw"), 10, 3)
+    stream_gbs = 2 * STREAM_BYTES / (ms * 1e-3) / 1e9
+    del buf
+    wgs, iters = 4096, 512
+    out = torch.empty(wgs * 256, device="cuda", dtype=torch.float32)
+    ms_m = time_events(lambda: L.check(lib.oal_ceiling_mfma(ctypes.c_void_p(out.data_ptr()), wgs, iters, stream),
+                                       "oal_ceiling_mfma"), 10, 3)
+    tflops = lib.oal_ceiling_mfma_flops(wgs, iters) / (ms_m * 1e-3) / 1e12
+    return {"stream_rw_GBs": stream_gbs, "stream_rw_bytes": 2 * STREAM_BYTES, "stream_rw_ms": ms,
+            "mfma_bf16_TFLOPs": tflops, "mfma_probe": f"{wgs} workgroups x 4 waves x {iters} x 8 "
+                                                       "v_mfma_f32_16x16x32_bf16", "mfma_ms": ms_m}
+
+
 def run_main(args):
     import torch
     import grouped_quadratic_softmax_amd as oal
     import synthetic as S
 
-    wl = S.make(2, seq_len=2048 + 1)  # token N is the decoded one
+    wl = S.make(3, seq_len=8192 + 1)  # token N is the decoded one
     B, Hq, Hkv, N1, d = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.seq_len, wl.d_h
     N = N1 - 1
     q_all, k_all, v_all = device_inputs(wl)
@@ -97,35 +127,18 @@ def run_main(args):
     qn, kn, vn = (t[:, :, N].contiguous() for t in (q_all, k_all, v_all))
     co = coeffs_for(wl)
 
-    chi_plan = oal.ContribPlan(q, k)
-    pre = oal.PrefillPlan(q, k, v, co)
-    dec = oal.DecodePlan(qn, kn, vn, co, pre.state_out)
     # The timed step (oal.StepPlan) runs chi on a second stream of default
-    # priority beside the scan; the readout and the decode step follow the
-    # scan on the main stream, which waits for chi at the end of every step.
-    overlapped = oal.StepPlan(q, k, v, qn, kn, vn, co)
-    step_overlapped = overlapped.run
+    # priority beside the prefill; the decode step follows the prefill on the
+    # main stream, which waits for chi at the end of every step.
+    plan = oal.StepPlan(q, k, v, qn, kn, vn, co)
+    chi_main = oal.ContribPlan(q, k)  # the same reduction on the main stream, for the per-stage timing
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    stage_ms = [0.0, 0.0, 0.0, 0.0]
-
-    def step(record):
-        if record:
-            ev[0].record()
-        chi_plan.run()
-        if record:
-            ev[1].record()
-        pre.states()
-        if record:
-            ev[2].record()
-        pre.outputs()
-        if record:
-            ev[3].record()
-        dec.run()
-        if record:
-            ev[4].record()
-
-    run_step = (lambda: step(False)) if args.no_overlap else step_overlapped
+    run_step = plan.run
+    if args.no_overlap:
+        def run_step():
+            chi_main.run()
+            plan.prefill.run()
+            plan.decode.run()
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -133,24 +146,21 @@ def run_main(args):
     for _ in range(args.steps):
         run_step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
+    elapsed = time.perf_counter() - t0
 
-    # per-stage durations with HIP events on the same stream (separate pass)
-    for _ in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()
-        for i in range(4):
-            stage_ms[i] += ev[i].elapsed_time(ev[i + 1]) / args.steps
-    out_ms = stage_ms[2]
+    # per-stage durations with HIP events on the main stream (separate pass)
+    stage_ms = {"contrib": time_events(chi_main.run, args.steps, 2),
+                "prefill": time_events(plan.prefill.run, args.steps, 2),
+                "decode": time_events(plan.decode.run, args.steps, 2)}
+    pre_ms = stage_ms["prefill"]
 
     D = feature_count(d)
     tokens_per_step = B * N + B
     ms_per_step = elapsed / args.steps * 1e3
-    readout_flops = B * N * Hq * 2 * D * (DV + 1)         # one launch of the readout kernel
-    update_flops = B * N * Hkv * 2 * D * (DV + 1)
-    achieved = readout_flops / (out_ms * 1e-3) / 1e12
-    traffic = load_traffic("readout_kernel_qwen_layer")
+    io_bytes = B * N * Hq * d * 2 + B * N * Hkv * (d * 2 + DV * 2) + B * N * Hq * DV * 2  # q, k, v, y
+    flops = B * N * Hq * 2 * D * (DV + 1) + B * N * Hkv * 2 * D * (DV + 1)  # readout + state update
+    gbs = io_bytes / (pre_ms * 1e-3) / 1e9
+    tfl = flops / (pre_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC,
         "value": tokens_per_step / (ms_per_step * 1e-3),
@@ -163,29 +173,57 @@ def run_main(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded Gaussian Q/K/V with planted outlier dims; no pretrained weights)",
-        "config": {"workload": "qwen2.5-0.5b-shaped OAL layer: B=4, N=2048, Hq=14, Hkv=2, d_h=d_v=64, G=4, "
+        "mfma_format": "v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulation)",
+        "data": "synthetic (seeded Gaussian Q, K ~ N(0, 1/16), V ~ N(0, 1); no pretrained weights)",
+        "config": {"workload": "Based Taylor kernel (G=1, a=1, b=1, c=1/2): B=8, H=16, N=8192, d_h=16, d_v=64, "
                                "bf16; step = chi + prefill(+final state) + 1 decode token/seq",
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {
-            "kernel": "readout_kernel (oal_fwd_outputs: coefficient tables, chunk readout, intra-chunk block, normalise)",
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": traffic,
-            "algorithmic_flops_per_launch": readout_flops,
-            "avg_launch_ms": out_ms,
+            "kernel": "oal_fwd prefill at d_h=16: onepass16 block sums + onepass16 outputs (two launches)",
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS,
+            "traffic": load_traffic("onepass16_based_prefill"),
+            "algorithmic_bytes_per_launch": io_bytes,
+            "avg_launch_ms": pre_ms,
+            "mfma_achieved_TFLOPs": tfl,
+            "mfma_frac": tfl / PEAK_BF16_TFLOPS,
+            "algorithmic_flops_per_launch": flops,
         },
         "schedule": ("one stream" if args.no_overlap else
-                     "chi on a second stream beside the chunk scan; streams joined every step"),
-        "stages_ms": {"contrib": stage_ms[0], "prefill_states": stage_ms[1], "prefill_outputs": stage_ms[2],
-                      "decode": stage_ms[3]},
-        "prefill_mfma_frac": (readout_flops + update_flops) / ((stage_ms[1] + stage_ms[2]) * 1e-3) / 1e12
-                             / PEAK_BF16_TFLOPS,
+                     "chi on a second stream beside the prefill; the second stream waits for the first at the "
+                     "start of every step and the first for the second at its end"),
+        "stages_ms": stage_ms,
     }
+    del plan, chi_main, q, k, v, q_all, k_all, v_all
     return result, wl
+
+
+def run_decode(args):
+    """The batched decode step: 256 sequences x 16 heads, d_h = d_v = 64,
+    eight groups, fp32 states of (1 + 64 + 2080) x 65 each, updated in place."""
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    import synthetic as S
+
+    S_, H = DECODE_SEQS, DECODE_HEADS
+    D = feature_count(64)
+    g = torch.Generator(device="cuda").manual_seed(1205)
+    state = torch.rand((S_, H, D * (DV + 1)), generator=g, device="cuda", dtype=torch.float32)
+    mk = lambda *shape: torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    qd, kd, vd = mk(S_, H, 64), mk(S_, H, 64), mk(S_, H, 64)
+    groups = ((torch.arange(64) * 8) // 64).repeat(H, 1).numpy()
+    wl5 = S.make(5, seq_len=8, batch=1)
+    dec = oal.DecodePlan(qd, kd, vd, coeffs_for(wl5, groups), state)
+    ms = time_events(dec.run, max(10, args.steps), 3)
+    nbytes = 2 * S_ * H * D * (DV + 1) * 4 + (3 * S_ * H * 64 + S_ * H * 64) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "decode_kernel (oal_decode_step, 256 sequences x 16 heads, G=8, fp32 states)",
+            "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": load_traffic("decode_256x16"), "algorithmic_bytes_per_launch": nbytes,
+            "avg_launch_ms": ms, "tokens_per_s": S_ / (ms * 1e-3)}
 
 
 def run_secondary(args):
@@ -196,32 +234,38 @@ def run_secondary(args):
 
     out = {}
     steps, warm = max(3, args.steps // 5), 2
-    # the same GQA layer (B=4, N=2048, Hq=14, Hkv=2) with eight groups of
-    # eight dimensions: the readout alone (its eight-group build)
-    wl = S.make(2, seq_len=2048)
-    q, k, v = device_inputs(wl)
+    # the Qwen2.5-0.5B-shaped GQA layer (B=4, N=2048, Hq=14, Hkv=2, d_h=64,
+    # G=4): the whole step, and its chunk readout (the MFMA-bound kernel)
+    wl = S.make(2, seq_len=2048 + 1)
+    N = wl.seq_len - 1
+    q_all, k_all, v_all = device_inputs(wl)
+    q, k, v = (t[:, :, :N].contiguous() for t in (q_all, k_all, v_all))
+    qn, kn, vn = (t[:, :, N].contiguous() for t in (q_all, k_all, v_all))
+    plan = oal.StepPlan(q, k, v, qn, kn, vn, coeffs_for(wl))
+    step_ms = time_events(plan.run, steps, warm)
+    pre = oal.PrefillPlan(q, k, v, coeffs_for(wl))
+    st_ms = time_events(pre.states, steps, warm)
+    out_ms = time_events(pre.outputs, steps, warm)
+    D = feature_count(64)
+    rd_flops = wl.batch * N * wl.n_q_heads * 2 * D * (DV + 1)
+    up_flops = wl.batch * N * wl.n_kv_heads * 2 * D * (DV + 1)
+    out["c2_qwen_layer"] = {"step_ms": step_ms, "tokens_per_s": wl.batch * (N + 1) / (step_ms * 1e-3),
+                            "states_ms": st_ms, "readout_ms": out_ms,
+                            "readout_mfma_frac": rd_flops / (out_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                            "readout_traffic": load_traffic("readout_kernel_qwen_layer"),
+                            "prefill_mfma_frac": (rd_flops + up_flops) / ((st_ms + out_ms) * 1e-3) / 1e12
+                                                 / PEAK_BF16_TFLOPS}
+    del plan, pre
+    # the same layer with eight groups of eight dimensions: the readout alone
+    # (its eight-group build)
     rng = np.random.default_rng(2048)
     a8, b8, c8 = oal.coeffs_from_factor(1e-3, rng.standard_normal((wl.n_q_heads, 9, 9)))
     g8 = np.repeat(np.arange(8, dtype=np.int32), 8)[None, :].repeat(wl.n_q_heads, 0)
     pre = oal.PrefillPlan(q, k, v, oal.Coeffs(g8, a8, b8, c8))
     pre.states()
     ms = time_events(pre.outputs, steps, warm)
-    flops = wl.batch * wl.seq_len * wl.n_q_heads * 2 * feature_count(64) * (DV + 1)
-    out["c2_gqa_g8_readout"] = {"ms": ms, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    del pre, q, k, v
-    # d_h = 16 Based Taylor prefill, B=8, H=16, N=8192 (HBM-bound)
-    wl = S.make(3)
-    q, k, v = device_inputs(wl)
-    pre = oal.PrefillPlan(q, k, v, coeffs_for(wl))
-    ms = time_events(pre.run, steps, warm)
-    tok = wl.batch * wl.seq_len
-    D = feature_count(16)
-    flops = tok * 2 * wl.n_q_heads * 2 * D * (DV + 1)
-    io = tok * wl.n_q_heads * (16 * 2 * 2 + DV * 2 * 2)
-    out["c3_based_prefill"] = {"ms": ms, "tokens_per_s": tok / (ms * 1e-3),
-                               "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                               "hbm_frac": io / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    del pre, q, k, v
+    out["c2_gqa_g8_readout"] = {"ms": ms, "mfma_frac": rd_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    del pre, q, k, v, q_all, k_all, v_all
     # ReBased elementwise-square prefill, B=16, H=8, N=2048 (dimension-wise
     # form: features [1, k, k^2], HBM-bound)
     wl = S.make(4)
@@ -243,116 +287,118 @@ def run_secondary(args):
     pre = oal.PrefillPlan(q, k, v, coeffs_for(wl, groups))
     ms = time_events(pre.run, steps, warm)
     tok = wl.batch * wl.seq_len
-    D = feature_count(64)
     flops = tok * 2 * wl.n_q_heads * 2 * D * (DV + 1)
     out["c5_long_prefill"] = {"ms": ms, "tokens_per_s": tok / (ms * 1e-3),
                               "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     del pre, q, k, v
-    # batched decode: 256 sequences x 16 heads, fp32 states (2145 x 65 each)
-    S_, H = 256, 16
-    g = torch.Generator(device="cuda").manual_seed(1205)
-    state = torch.rand((S_, H, D * (DV + 1)), generator=g, device="cuda", dtype=torch.float32)
-    mk = lambda *shape: torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
-    qd, kd, vd = mk(S_, H, 64), mk(S_, H, 64), mk(S_, H, 64)
-    groups = ((torch.arange(64) * 8) // 64).repeat(H, 1).numpy()
-    wl5 = S.make(5, seq_len=8, batch=1)
-    dec = oal.DecodePlan(qd, kd, vd, coeffs_for(wl5, groups), state)
-    ms = time_events(dec.run, max(10, args.steps), 3)
-    nbytes = 2 * S_ * H * D * (DV + 1) * 4 + (3 * S_ * H * 64 + S_ * H * 64) * 2
-    out["c5_decode_256x16"] = {"ms": ms, "tokens_per_s": S_ / (ms * 1e-3),
-                               "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
-                               "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     return out
 
 
 def run_pmc_target(args):
     """Launch only one kernel repeatedly, for rocprofv3 counter passes.
 
-    ``readout``: the chunk readout of the main workload (after one states
-    pass); ``states``: the chunk scan of the main workload; ``based16``: the
-    one-pass prefill of the d_h = 16 Based Taylor workload (B=8, H=16,
-    N=8192); ``rebased``: the one-pass prefill of the ReBased workload in the
+    ``based16``: the prefill of the timed workload (B=8, H=16, N=8192,
+    d_h=16: the one-pass block-sum and output kernels); ``decode``: the
+    batched decode step (256 sequences x 16 heads, fp32 states);
+    ``readout`` / ``states``: the chunk readout / chunk scan of the
+    Qwen-shaped GQA layer (B=4, N=2048, Hq=14, Hkv=2, d_h=64);
+    ``rebased``: the one-pass prefill of the ReBased workload in the
     dimension-wise form (B=16, H=8, N=2048); ``long``: the prefill of the
     long-context multi-head workload (B=1, H=16, N=32768, d_h=64, eight
     groups from its contribution scores); ``copy``: a plain device copy of
     1 GiB (fp32), whose FETCH_SIZE and WRITE_SIZE readings calibrate the
-    counters against a known byte count."""
+    counters against a known byte count; ``mfma``: the bf16 MFMA chain probe,
+    whose MFMA counters calibrate the busy fraction of the prefill kernels;
+    ``stream``: the in-place stream probe over 2 GiB."""
+    import ctypes
     import torch
     import grouped_quadratic_softmax_amd as oal
     import synthetic as S
 
-    if args.pmc_target == "copy":
+    def repeat(fn):
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": args.pmc_target, "launches": args.steps}), flush=True)
+
+    t = args.pmc_target
+    if t == "copy":
         n = COPY_BYTES // 4
         src = torch.ones(n, device="cuda", dtype=torch.float32)
         dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"pmc_target": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
-                          "launches": args.steps}), flush=True)
+        repeat(lambda: dst.copy_(src))
         return
-    if args.pmc_target == "long":
+    if t in ("mfma", "stream"):
+        from grouped_quadratic_softmax_amd import _lib as L
+        lib = L.lib()
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if t == "mfma":
+            out = torch.empty(4096 * 256, device="cuda", dtype=torch.float32)
+            repeat(lambda: L.check(lib.oal_ceiling_mfma(ctypes.c_void_p(out.data_ptr()), 4096, 512, st), t))
+        else:
+            buf = torch.zeros(STREAM_BYTES // 4, device="cuda", dtype=torch.float32)
+            repeat(lambda: L.check(lib.oal_ceiling_stream_rw(ctypes.c_void_p(buf.data_ptr()),
+                                                             ctypes.c_size_t(buf.numel()), st), t))
+        return
+    if t == "decode":
+        S_, H = DECODE_SEQS, DECODE_HEADS
+        D = feature_count(64)
+        g = torch.Generator(device="cuda").manual_seed(1205)
+        state = torch.rand((S_, H, D * (DV + 1)), generator=g, device="cuda", dtype=torch.float32)
+        mk = lambda *shape: torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+        groups = ((torch.arange(64) * 8) // 64).repeat(H, 1).numpy()
+        dec = oal.DecodePlan(mk(S_, H, 64), mk(S_, H, 64), mk(S_, H, 64),
+                             coeffs_for(S.make(5, seq_len=8, batch=1), groups), state)
+        repeat(dec.run)
+        return
+    if t == "long":
         wl = S.make(5)
         q, k, v = device_inputs(wl)
         chi = oal.contrib(q, k).cpu().numpy()
         groups = oal.groups_from_contribution(chi, wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"])
-        pre = oal.PrefillPlan(q, k, v, coeffs_for(wl, groups))
-        torch.cuda.synchronize()
-        for _ in range(args.steps):
-            pre.run()
-        torch.cuda.synchronize()
-        print(json.dumps({"pmc_target": args.pmc_target, "launches": args.steps}), flush=True)
+        pre = oal.PrefillPlan(q, k, v, coeffs_for(wl, groups), staged=False)
+        repeat(pre.run)
         return
-    if args.pmc_target in ("based16", "rebased"):
-        wl = S.make(3 if args.pmc_target == "based16" else 4)
+    if t in ("based16", "rebased"):
+        wl = S.make(3 if t == "based16" else 4)
         q, k, v = device_inputs(wl)
         p = wl.premap
         prep = (oal.Prep(p["gamma_q"], p["beta_q"], p["gamma_k"], p["beta_k"], p["ln_eps"])
                 if p is not None else None)
-        pre = oal.PrefillPlan(q, k, v, coeffs_for(wl), prep)
-        torch.cuda.synchronize()
-        for _ in range(args.steps):
-            pre.run()
-        torch.cuda.synchronize()
-        print(json.dumps({"pmc_target": args.pmc_target, "launches": args.steps}), flush=True)
+        pre = oal.PrefillPlan(q, k, v, coeffs_for(wl), prep, staged=False)
+        repeat(pre.run)
         return
     wl = S.make(2, seq_len=2048 + 1)
     N = wl.seq_len - 1
-    q, k, v = (t[:, :, :N].contiguous() for t in device_inputs(wl))
+    q, k, v = (t_[:, :, :N].contiguous() for t_ in device_inputs(wl))
     pre = oal.PrefillPlan(q, k, v, coeffs_for(wl))
     pre.states()
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        if args.pmc_target == "readout":
-            pre.outputs()
-        else:
-            pre.states()
-    torch.cuda.synchronize()
-    print(json.dumps({"pmc_target": args.pmc_target, "launches": args.steps}), flush=True)
+    repeat(pre.outputs if t == "readout" else pre.states)
 
 
 def cpu_baseline(wl, min_seconds=10.0):
-    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
-    whole sequences of it (every query head, every token), repeated until at
-    least ``min_seconds`` of host time have passed."""
+    """The fp64 oracle (as it stands) on a bounded sample of the same
+    workload: whole sequences of it (every head, every token), each through
+    chi (separable form), the prefix-recurrence attention (the oracle's
+    linear-time form), the final states and one decode step, repeated until
+    at least ``min_seconds`` of host time have passed."""
     import numpy as np
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas_threads = None
     N = wl.seq_len - 1
-    a, b, c = O.coeffs_from_factor(wl.coeff["eps"], wl.coeff["L"])
+    a, b, c = wl.coeff["a"], wl.coeff["b"], wl.coeff["c"]
     done = 0
     t0 = time.perf_counter()
     while True:
         bi = done % wl.batch
         qs, ks, vs = (x[bi:bi + 1, :, :N] for x in (wl.q, wl.k, wl.v))
         O.chi_separable(qs, ks)
-        O.attention_direct(qs, ks, vs, wl.group_of_dim, a, b, c)
-        st = np.stack([np.stack([O.state_from_prefix(ks[0, kh], vs[0, kh]) for kh in range(wl.n_kv_heads)])])
+        _, st = O.attention_recurrent_packed(qs, ks, vs, wl.group_of_dim, a, b, c, return_state=True)
         O.decode_step(st, wl.q[bi:bi + 1, :, N], wl.k[bi:bi + 1, :, N], wl.v[bi:bi + 1, :, N], wl.group_of_dim,
                       a, b, c, wl.n_q_heads)
         done += 1
@@ -360,11 +406,11 @@ def cpu_baseline(wl, min_seconds=10.0):
             break
     dt = time.perf_counter() - t0
     tokens = done * (N + 1)
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "blas_threads": blas_threads, "seconds": dt,
             "sample": f"{done} sequence(s) of the workload ({N} prefill tokens + 1 decoded token each, all "
-                      f"{wl.n_q_heads} query heads): chi (separable form), direct O(N^2) fp64 attention, prefix "
-                      "states, one decode step; repeated until >= 10 s of host time"}
+                      f"{wl.n_q_heads} heads): chi (separable form), fp64 prefix-recurrence attention with the "
+                      f"final states, one decode step; repeated until >= {min_seconds:g} s of host time"}
 
 
 def main():
@@ -376,7 +422,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run chi, prefill and decode back to back on one stream")
-    ap.add_argument("--pmc-target", choices=("readout", "states", "based16", "rebased", "long", "copy"), default=None,
+    ap.add_argument("--pmc-target", default=None,
+                    choices=("based16", "decode", "readout", "states", "rebased", "long", "copy", "mfma", "stream"),
                     help="only launch this kernel --steps times (for rocprofv3 counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -394,6 +441,13 @@ def main():
         return
     result, wl = run_main(args)
     print(f"[bench] main done: {result['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+    result["roofline_decode"] = run_decode(args)
+    result["ceilings"] = measure_ceilings()
+    ce = result["ceilings"]
+    result["roofline"]["frac_of_stream_ceiling"] = result["roofline"]["achieved"] / ce["stream_rw_GBs"]
+    result["roofline"]["mfma_frac_of_probe"] = result["roofline"]["mfma_achieved_TFLOPs"] / ce["mfma_bf16_TFLOPs"]
+    result["roofline_decode"]["frac_of_stream_ceiling"] = result["roofline_decode"]["achieved"] / ce["stream_rw_GBs"]
+    print("[bench] decode and ceilings done", file=sys.stderr, flush=True)
     if not args.no_secondary:
         result["secondary"] = run_secondary(args)
         print("[bench] secondary done", file=sys.stderr, flush=True)

@@ -1,4 +1,4 @@
-"""ctypes view of the C ABI declared in include/oal.h.
+"""ctypes view of the C ABI declared in include/oal.h and include/oal_ceilings.h.
 
 Loads the in-tree ``liboal.so``.  There is no fallback: if the library is
 missing or fails to load, every entry point raises.
@@ -67,6 +67,10 @@ _SIGS = {
     "oal_contrib": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_group_dims": ([ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
     "oal_group_dims_budget": ([ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_double, _P], ctypes.c_int),
+    # include/oal_ceilings.h
+    "oal_ceiling_stream_rw": ([_P, ctypes.c_size_t, _P], ctypes.c_int),
+    "oal_ceiling_mfma": ([_P, ctypes.c_int, ctypes.c_int, _P], ctypes.c_int),
+    "oal_ceiling_mfma_flops": ([ctypes.c_int, ctypes.c_int], ctypes.c_double),
 }
 
 

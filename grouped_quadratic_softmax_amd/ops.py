@@ -224,10 +224,12 @@ class PrefillPlan:
     ``run()`` enqueues one oal_fwd call on the stream that is current at
     construction time; ``states()`` and ``outputs()`` enqueue its two stages
     separately (not available for coefficients in the dimension-wise form).
+    With ``staged=False`` the workspace is sized for ``run()`` alone, which
+    for the one-pass paths is far smaller than the two stages need.
     """
 
     def __init__(self, q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None,
-                 with_state=True):
+                 with_state=True, staged=True):
         import torch
         B, Hq, N, d = q.shape
         Hkv, dv = k.shape[1], v.shape[3]
@@ -240,7 +242,7 @@ class PrefillPlan:
         self._cs = coeffs.struct()
         lib = L.lib()
         nbytes = int(lib.oal_fwd_workspace_bytes_for(ctypes.byref(self.dims), ctypes.byref(self._cs)))
-        if not coeffs.diagonal:  # the two stages need the full workspace
+        if staged and not coeffs.diagonal:  # the two stages need the full workspace
             nbytes = max(nbytes, int(lib.oal_fwd_workspace_bytes(ctypes.byref(self.dims))))
         self.workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
         self._ps = prep.struct() if prep is not None else None
@@ -254,11 +256,14 @@ class PrefillPlan:
         self._fwd_args = (ctypes.byref(self.dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(self._cs), pp,
                           _ptr(state_in), _ptr(self.state_out), _ptr(self.y), *ws, st)
         self._lib = L.lib()
+        self._staged = staged
 
     def states(self):
+        _need(self._staged, "PrefillPlan(staged=False) has no separate stages")
         L.check(self._lib.oal_fwd_states(*self._states_args), "oal_fwd_states")
 
     def outputs(self):
+        _need(self._staged, "PrefillPlan(staged=False) has no separate stages")
         L.check(self._lib.oal_fwd_outputs(*self._out_args), "oal_fwd_outputs")
 
     def run(self):
@@ -315,35 +320,34 @@ class ContribPlan:
 class StepPlan:
     """One pass of the hot path on fixed buffers, spread over two streams.
 
-    A batch of prompts ``q, k, v [B, H, N, d]`` is prefilled (chunk scan,
-    then the chunk readout), each sequence then decodes one token
+    A batch of prompts ``q, k, v [B, H, N, d]`` is prefilled (one oal_fwd
+    call keeping the final states), each sequence then decodes one token
     ``qn, kn, vn [B, H, d]`` on the prefill's final state, and chi (the
     per-dimension contribution of the prompts' q and k) is reduced.
 
-    The scan, the readout and the decode step run in that order on the stream
-    current at construction.  Chi reads only q and k, so a second stream of
-    default priority runs it from the start of the step, on the compute units
-    that the scan's few workgroups leave idle.  ``run()`` starts with the
+    The prefill and the decode step run in that order on the stream current
+    at construction.  Chi reads only q and k, so a second stream of default
+    priority runs it from the start of the step, on the compute units that
+    the prefill's first launch leaves idle.  ``run()`` starts with the
     second stream waiting for the first (so chi sees inputs produced earlier
     on it, and the previous step's consumers of the chi buffer are done) and
-    ends with the first stream waiting for the second.  (The decode step stays behind the readout:
-    when the readout has one workgroup per compute unit, a decode launched
-    beside it holds compute units that the readout then waits for.)
+    ends with the first stream waiting for the second.  (The decode step stays behind the prefill:
+    when the prefill has one workgroup per compute unit, a decode launched
+    beside it holds compute units that the prefill then waits for.)
     """
 
     def __init__(self, q, k, v, qn, kn, vn, coeffs: Coeffs, prep: Optional[Prep] = None):
         import torch
         self.main = torch.cuda.current_stream()
         self.side = torch.cuda.Stream()
-        self.prefill = PrefillPlan(q, k, v, coeffs, prep)
+        self.prefill = PrefillPlan(q, k, v, coeffs, prep, staged=False)
         self.decode = DecodePlan(qn, kn, vn, coeffs, self.prefill.state_out, prep)
         with torch.cuda.stream(self.side):
             self.chi = ContribPlan(q, k)
 
     def run(self):
         self.side.wait_stream(self.main)
-        self.prefill.states()
+        self.prefill.run()
         self.chi.run()
-        self.prefill.outputs()
         self.decode.run()
         self.main.wait_stream(self.side)

@@ -4,6 +4,7 @@ Two uses:
 
 * ``stats DIR``: a markdown table of the per-kernel launch statistics that
   ``rocprofv3 --kernel-trace --stats --output-format csv -d DIR`` wrote.
+* ``counters DIR...``: a markdown table of per-dispatch counter medians.
 * ``traffic``: HBM bytes per launch of one kernel from two counter passes
   (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, each reported in KiB per
   dispatch), each scaled by the factor that maps the same counter onto the
@@ -32,7 +33,8 @@ CSRC = os.path.join(PKG, "csrc")
 PREFILL_SOURCES = ("oal_prefill.h", "oal_prefill_d64.hip", "oal_device.h", "oal_layout.h", "oal_internal.h")
 
 
-def source_hash(files=PREFILL_SOURCES) -> str:
+def source_hash(files=None) -> str:
+    files = PREFILL_SOURCES if files is None else files
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -71,7 +73,16 @@ def counter_values(d: str, counter: str, name_has: str) -> list[float]:
 
 
 def short_name(n: str, width: int = 110) -> str:
-    n = n.split("(")[0] if "(" in n and not n.startswith("(") else n
+    """The kernel name without its trailing parameter list (names may hold
+    parentheses of their own, e.g. ``(anonymous namespace)``)."""
+    n = n.replace("(anonymous namespace)::", "")
+    if n.endswith(")"):
+        depth = 0
+        for i in range(len(n) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(n[i], 0)
+            if depth == 0:
+                n = n[:i] if i > 0 else n
+                break
     return n if len(n) <= width else n[: width - 3] + "..."
 
 
@@ -84,16 +95,59 @@ def stats_markdown(d: str, title: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel, copy_bytes, commands):
+def counter_by_kernel(d: str, counter: str, name_has: str) -> dict:
+    """Median per-dispatch value of one counter for every distinct kernel
+    whose name contains ``name_has``."""
+    per = {}
+    for f in _find(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and name_has in r["Kernel_Name"]:
+                per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    if not per:
+        raise ValueError(f"no {counter} values for kernels matching {name_has!r} under {d}")
+    return {k: statistics.median(v) for k, v in per.items()}
+
+
+def traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel, copy_bytes, commands,
+                   sources=None):
+    """HBM bytes of one call: the medians per dispatch of every kernel whose
+    name contains ``kernel`` (a call may launch several), summed, each
+    counter scaled by the copy calibration."""
     kib = 1024.0
-    fetch = statistics.median(counter_values(fetch_dir, "FETCH_SIZE", kernel)) * kib
-    write = statistics.median(counter_values(write_dir, "WRITE_SIZE", kernel)) * kib
+    fetch = sum(counter_by_kernel(fetch_dir, "FETCH_SIZE", kernel).values()) * kib
+    write = sum(counter_by_kernel(write_dir, "WRITE_SIZE", kernel).values()) * kib
     cfetch = statistics.median(counter_values(copy_fetch_dir, "FETCH_SIZE", "copy")) * kib
     cwrite = statistics.median(counter_values(copy_write_dir, "WRITE_SIZE", "copy")) * kib
     ff, fw = copy_bytes / cfetch, copy_bytes / cwrite
-    return {"bytes_per_launch": fetch * ff + write * fw, "fetch_bytes": fetch * ff, "write_bytes": write * fw,
-            "fetch_counter_bytes": fetch, "write_counter_bytes": write, "fetch_factor": ff, "write_factor": fw,
-            "copy_bytes": copy_bytes, "kernel_match": kernel, "source_sha256": source_hash(), "commands": commands}
+    rec = {"bytes_per_launch": fetch * ff + write * fw, "fetch_bytes": fetch * ff, "write_bytes": write * fw,
+           "fetch_counter_bytes": fetch, "write_counter_bytes": write, "fetch_factor": ff, "write_factor": fw,
+           "copy_bytes": copy_bytes, "kernel_match": kernel, "source_sha256": source_hash(sources),
+           "commands": commands}
+    if sources is not None:
+        rec["sources"] = list(sources)
+    return rec
+
+
+def counters_markdown(dirs, kernels, title, commands) -> str:
+    """Per-dispatch medians of every counter found under ``dirs`` for the
+    kernels whose names contain one of ``kernels``."""
+    rows = {}
+    for d in dirs:
+        for f in _find(d, "counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                name = r["Kernel_Name"]
+                if any(k in name for k in kernels):
+                    rows.setdefault(short_name(name, 90), {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+    counters = sorted({c for v in rows.values() for c in v})
+    lines = [f"# {title}", "", "Commands (repository root, one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "",
+             "```", *commands, "```", "", "Median per dispatch.", "",
+             "| kernel | dispatches | " + " | ".join(counters) + " |", "|---|---|" + "---|" * len(counters)]
+    for k, v in sorted(rows.items()):
+        n = max(len(x) for x in v.values())
+        cells = [f"{statistics.median(v[c]):.4g}" if c in v else "" for c in counters]
+        lines.append(f"| `{k}` | {n} | " + " | ".join(cells) + " |")
+    return "\n".join(lines) + "\n"
 
 
 def main(argv=None):
@@ -108,12 +162,22 @@ def main(argv=None):
         s2.add_argument("--" + a, required=True)
     s2.add_argument("--copy-bytes", type=int, default=1 << 30)
     s2.add_argument("--commands", nargs="*", default=[])
+    s2.add_argument("--sources", nargs="*", default=None,
+                    help="csrc files whose change makes the record stale (default: the chunk prefill's)")
+    s3 = sub.add_parser("counters")
+    s3.add_argument("dirs", nargs="+")
+    s3.add_argument("--kernels", nargs="+", required=True)
+    s3.add_argument("--title", required=True)
+    s3.add_argument("--commands", nargs="*", default=[])
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         sys.stdout.write(stats_markdown(args.dir, args.title, args.command))
         return
+    if args.cmd == "counters":
+        sys.stdout.write(counters_markdown(args.dirs, args.kernels, args.title, args.commands))
+        return
     rec = traffic_record(args.fetch, args.write, args.copy_fetch, args.copy_write, args.kernel, args.copy_bytes,
-                         args.commands)
+                         args.commands, args.sources)
     table = {}
     if os.path.exists(args.out):
         with open(args.out) as f:
