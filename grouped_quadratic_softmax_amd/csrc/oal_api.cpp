@@ -130,7 +130,7 @@ size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeff
   const bool diagonal = coeffs->diagonal != 0;
   if (oal::onepass16_supported(dims->d_h, dims->dtype, diagonal, dims->n_groups, dims->n_q_heads,
                                dims->n_kv_heads))
-    return oal::onepass16_workspace_bytes(dims->batch, dims->n_kv_heads, dims->seq_len);
+    return oal::onepass16_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->seq_len);
   if (!oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads))
     return diagonal ? 0 : oal_fwd_workspace_bytes(dims);
   return oal::small_workspace_bytes(dims->batch, dims->n_kv_heads, dims->seq_len, dims->d_h, diagonal,

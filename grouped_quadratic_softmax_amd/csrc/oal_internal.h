@@ -63,8 +63,12 @@ hipError_t launch_fwd_small(const FwdLaunch& a, size_t workspace_bytes, hipStrea
 // accumulators; sequences are cut into segments whose starting states come
 // from block sums in the workspace (one segment without a workspace).
 bool onepass16_supported(int d_h, int dtype, bool diagonal, int G, int Hq, int Hkv);
-size_t onepass16_workspace_bytes(int B, int Hkv, int N);
+size_t onepass16_workspace_bytes(int B, int Hq, int Hkv, int N);
 hipError_t launch_onepass16(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
+// one wave per (sequence x head, segment): heads with their own keys, no pre-map
+bool onepass16w_supported(int Hq, int Hkv, bool premap);
+size_t onepass16w_workspace_bytes(int B, int Hkv, int N);
+hipError_t launch_onepass16w(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStream_t stream);
 void decode_slicing(int d_h, long states, int& rows, int& nslice, bool diagonal);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h);

@@ -48,7 +48,7 @@ def test_fp32_path_is_bit_exact_on_dyadic_inputs():
         assert np.array_equal(got, want)
 
 
-def _sparse_dyadic_case(seed, d, dtype, diagonal, B=2, Hq=4, Hkv=2, N=160, G=4):
+def _sparse_dyadic_case(seed, d, dtype, diagonal, B=2, Hq=4, Hkv=2, N=160, G=4, heads=None):
     """Inputs on which every operand of every path is exact in bf16 (8
     significant bits), so the kernels' (num, den) are exact whatever the
     operand format (fp32, fp16 or bf16) and the accumulation order.
@@ -62,6 +62,8 @@ def _sparse_dyadic_case(seed, d, dtype, diagonal, B=2, Hq=4, Hkv=2, N=160, G=4):
     (singleton groups, diagonal c) uses c_rr in {1, 2}.
     """
     rng = np.random.default_rng(seed)
+    if heads is not None:
+        Hq, Hkv = heads
 
     def two_hot(shape):
         x = np.zeros(shape + (d,), np.float32)
@@ -94,10 +96,12 @@ def _ulp(x, dtype):
     return np.ldexp(1.0, (e - (23 if dtype == "f32" else 7)).astype(np.int32))
 
 
-@pytest.mark.parametrize("d,dtype,diagonal", [(16, "bf16", False), (16, "f32", False), (32, "bf16", False),
-                                              (32, "f32", False), (64, "bf16", False), (16, "bf16", True),
-                                              (64, "bf16", True), (32, "f32", True)])
-def test_exact_on_sparse_dyadic_inputs(d, dtype, diagonal):
+@pytest.mark.parametrize("d,dtype,diagonal,heads", [(16, "bf16", False, None), (16, "bf16", False, (3, 3)),
+                                                    (16, "f32", False, None), (32, "bf16", False, None),
+                                                    (32, "f32", False, None), (64, "bf16", False, None),
+                                                    (16, "bf16", True, None), (64, "bf16", True, None),
+                                                    (32, "f32", True, None)])
+def test_exact_on_sparse_dyadic_inputs(d, dtype, diagonal, heads):
     """Every build (fp32, the bf16-input chunk kernels, the one-pass kernels
     and the dimension-wise form) on inputs where all operands are exact: the
     output equals the oracle's y rounded once to the output format; the only
@@ -105,7 +109,7 @@ def test_exact_on_sparse_dyadic_inputs(d, dtype, diagonal):
     place).  A wrong group id, head map or mask changes y by far more."""
     require_gpu()
     import grouped_quadratic_softmax_amd as oal
-    q, k, v, groups, a, b, c = _sparse_dyadic_case(100 + d, d, dtype, diagonal)
+    q, k, v, groups, a, b, c = _sparse_dyadic_case(100 + d, d, dtype, diagonal, heads=heads)
     y_ref, num, den = O.attention_direct(q, k, v, groups, a, b, c, return_parts=True)
     # premises: numerator and denominator are exact in float32, den >= 1
     assert np.array_equal(num.astype(np.float32).astype(np.float64), num)
@@ -120,7 +124,7 @@ def test_exact_on_sparse_dyadic_inputs(d, dtype, diagonal):
         want = S.bf16_round(want.astype(np.float32)).astype(np.float64)
     diff = np.abs(got - want)
     exact = int((diff == 0).sum())
-    log(f"[exact] d={d} {dtype} diagonal={diagonal}: exact {exact} of {got.size}, max diff in ulps "
+    log(f"[exact] d={d} {dtype} diagonal={diagonal} heads={heads}: exact {exact} of {got.size}, max diff in ulps "
         f"{float((diff / _ulp(want, dtype)).max()):.2f}")
     assert (diff <= _ulp(want, dtype)).all()
     # rows whose output is exactly representable (e.g. y_1 = v_1) must be exact

@@ -334,16 +334,19 @@ def test_state_out_and_continuation(dtype):
     assert to_np(s_full).shape[-1] == D * 65
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_d16_workspace_sizes_stages_and_state(dtype):
+@pytest.mark.parametrize("dtype,heads", [("bf16", (4, 2)), ("f32", (4, 2)), ("bf16", (4, 4)), ("f32", (4, 4))])
+def test_d16_workspace_sizes_stages_and_state(dtype, heads):
     """d_h = 16 full space: oal_fwd with its default workspace and with a
     minimal one (refused by the chunk path, fewer segments on a one-pass
     path) and the two-stage calls all match the oracle; the final state
-    matches Eq. (5) and carries a continuation across a ragged split."""
+    matches Eq. (5) and carries a continuation across a ragged split.  With
+    four query heads on two KV heads the bf16 prefill is the one-pass CTA
+    build; with a KV head per query head it is the one-wave-per-segment
+    build, here over eight segments of three chunks."""
     require_gpu()
     import torch
     import grouped_quadratic_softmax_amd as oal
-    wl = S.make(3, batch=2, n_q_heads=4, n_kv_heads=2, seq_len=1500, dtype=dtype)
+    wl = S.make(3, batch=2, n_q_heads=heads[0], n_kv_heads=heads[1], seq_len=1500, dtype=dtype)
     co = gpu_coeffs(wl, wl.group_of_dim)
     q, k, v = to_dev(wl.q, dtype), to_dev(wl.k, dtype), to_dev(wl.v, dtype)
     a, b, c = oracle_coeffs(wl)
@@ -380,6 +383,33 @@ def test_d16_workspace_sizes_stages_and_state(dtype):
             bound = (2 * u + N * 2.0 ** -24) * absum + 2.0 ** -24 * absum.max()
             for got in (s_seg, s_one, s2, plan.state_out):
                 assert (np.abs(to_np(got)[bi, kh] - ref_s) <= bound).all(), (bi, kh)
+
+
+@pytest.mark.parametrize("G,N", [(2, 777), (3, 130), (5, 64), (8, 1000)])
+def test_d16_heads_with_own_keys_grouped(G, N):
+    """The one-wave-per-segment build at d_h = 16 (as many query heads as KV
+    heads) with several groups of uneven size: every row against the
+    oracle, and the final state against Eq. (5)."""
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    rng = np.random.default_rng(160 + G)
+    wl = S.make(3, batch=2, n_q_heads=3, n_kv_heads=3, seq_len=N)
+    groups = np.stack([rng.permutation(np.arange(16) % G) for _ in range(3)]).astype(np.int32)
+    a, b, c = O.coeffs_from_factor(1e-3, rng.standard_normal((3, G + 1, G + 1)) * 0.5)
+    co = oal.Coeffs(groups, a.astype(np.float32), b.astype(np.float32), c.astype(np.float32))
+    q, k, v = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+    y, st = oal.fwd(q, k, v, co, return_state=True)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, groups, a, b, c)
+    err = rel_err(to_np(y), ref)
+    log(f"[fwd]   d16 own-keys G={G} N={N}: max rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    u = 2.0 ** -9
+    for bi in range(wl.batch):
+        for kh in range(wl.n_kv_heads):
+            ref_s = O.abi_state_from_matrix(O.state_from_prefix(wl.k[bi, kh], wl.v[bi, kh]))
+            absum = O.abi_state_from_matrix(O.state_from_prefix(np.abs(wl.k[bi, kh]), np.abs(wl.v[bi, kh])))
+            bound = (2 * u + N * 2.0 ** -24) * absum + 2.0 ** -24 * absum.max()
+            assert (np.abs(to_np(st)[bi, kh] - ref_s) <= bound).all(), (bi, kh)
 
 
 def test_zero_length_passes_state_through():
