@@ -256,12 +256,108 @@ __global__ __launch_bounds__(64, 1) void onepass16w_kernel(const Args16 p) {
     return u4_frag(lo.x, lo.y, hi.x, hi.y);
   };
 
+  // ---- the state before a chunk as bf16 operands, each feature row times
+  // its query-side coefficient (so that the query features stay plain
+  // monomials).  K-block kb is rounded as soon as its two tiles hold the
+  // state (during the update of the chunk before), so the rounding overlaps
+  // the update's MFMAs. ----
+  bf16x8 As[NKB][4], Az[NKB];
+  auto convert = [&](auto KC) __attribute__((always_inline)) {
+    constexpr int kb = decltype(KC)::value;
+    const float4 c0 = lds_f4(&sh.coefq[32 * kb + 4 * lg]), c1 = lds_f4(&sh.coefq[32 * kb + 16 + 4 * lg]);
+    auto frag = [&](const f32x4& x0, const f32x4& x1) __attribute__((always_inline)) {
+      return u4_frag(pack_bf16(x0[0] * c0.x, x0[1] * c0.y), pack_bf16(x0[2] * c0.z, x0[3] * c0.w),
+                     pack_bf16(x1[0] * c1.x, x1[1] * c1.y), pack_bf16(x1[2] * c1.z, x1[3] * c1.w));
+    };
+#pragma unroll
+    for (int n = 0; n < 4; ++n) As[kb][n] = frag(S[2 * kb][n], S[2 * kb + 1][n]);
+    Az[kb] = frag(Z[2 * kb], Z[2 * kb + 1]);
+  };
+  if (OUT) {
+    convert(std::integral_constant<int, 0>{});
+    convert(std::integral_constant<int, 1>{});
+    convert(std::integral_constant<int, 2>{});
+    convert(std::integral_constant<int, 3>{});
+    convert(std::integral_constant<int, 4>{});
+  }
   const bf16x8 ones = kOnes;  // B operand that sums the rows of A (z, denominators)
+  auto update_chunk = [&]() __attribute__((always_inline)) {
+      // ---- state update with the chunk: both key steps of a tile back to
+      // back, so that each accumulator is updated in place ----
+      {
+        float kv[2][8];
+  #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          float x[4];
+          unpack4(k_rows4_at(sh.k + 32 * ks * DH, ko), x);
+          kv[ks][0] = x[0]; kv[ks][1] = x[1]; kv[ks][2] = x[2]; kv[ks][3] = x[3];
+          unpack4(k_rows4_at(sh.k + (32 * ks + 16) * DH, ko), x);
+          kv[ks][4] = x[0]; kv[ks][5] = x[1]; kv[ks][6] = x[2]; kv[ks][7] = x[3];
+        }
+        bf16x8 Vf[2][4];
+  #pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+  #pragma unroll
+          for (int n = 0; n < 4; ++n) Vf[ks][n] = vfrag(ks, n);
+        auto mtile = [&](auto MC) __attribute__((always_inline)) {
+          constexpr int M = decltype(MC)::value;
+          float f0[8], f1[8];
+          key_features<M>(kv[0], l, 0, CK, f0);  // the constant is 1 for every token (fixed up below)
+          key_features<M>(kv[1], l, 0, CK, f1);
+          const bf16x8 A0 = frag8(f0), A1 = frag8(f1);
+  #pragma unroll
+          for (int n = 0; n < 4; ++n) S[M][n] = mma32(A1, Vf[1][n], mma32(A0, Vf[0][n], S[M][n]));
+          Z[M] = mma32(A1, ones, mma32(A0, ones, Z[M]));
+        };
+        // the next chunk's operands of K-block kb are rounded one tile after
+        // tiles 2 kb and 2 kb + 1 were updated
+        mtile(std::integral_constant<int, 0>{});
+        mtile(std::integral_constant<int, 1>{});
+        mtile(std::integral_constant<int, 2>{});
+        if (OUT) convert(std::integral_constant<int, 0>{});
+        mtile(std::integral_constant<int, 3>{});
+        mtile(std::integral_constant<int, 4>{});
+        if (OUT) convert(std::integral_constant<int, 1>{});
+        mtile(std::integral_constant<int, 5>{});
+        mtile(std::integral_constant<int, 6>{});
+        if (OUT) convert(std::integral_constant<int, 2>{});
+        mtile(std::integral_constant<int, 7>{});
+        mtile(std::integral_constant<int, 8>{});
+        if (OUT) convert(std::integral_constant<int, 3>{});
+        mtile(std::integral_constant<int, 9>{});
+        if (OUT) convert(std::integral_constant<int, 4>{});
+      }
+  };
+
+  if (!OUT) {
+    // block sums: the chunk rows two chunks ahead are in flight (the update
+    // alone is too short to cover one chunk's load latency)
+    PreW pa, pb;
+    fetch(c_begin, pa);
+    if (c_begin + 1 < c_end) fetch(c_begin + 1, pb);
+    for (int c = c_begin; c < c_end; c += 2) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) asm volatile("" : "+a"(S[m][n]));
+        asm volatile("" : "+a"(Z[m]));
+      }
+      commit(pa);
+      if (c + 2 < c_end) fetch(c + 2, pa);
+      update_chunk();
+      if (c + 1 < c_end) {
+        commit(pb);
+        if (c + 3 < c_end) fetch(c + 3, pb);
+        update_chunk();
+      }
+    }
+  }
+
   PreW pre;
-  fetch(c_begin, pre);
+  if (OUT) fetch(c_begin, pre);
   if (OUT) __syncthreads();  // tables
 
-  for (int c = c_begin; c < c_end; ++c) {
+  for (int c = c_begin; OUT && c < c_end; ++c) {
     // keep the state in accumulation registers across the loop (an empty
     // statement that only constrains register allocation; without it the
     // loop-carried tiles are allocated to ordinary VGPRs and copied around
@@ -273,28 +369,11 @@ __global__ __launch_bounds__(64, 1) void onepass16w_kernel(const Args16 p) {
       asm volatile("" : "+a"(Z[m]));
     }
     commit(pre);
-    // The next chunk's loads are issued part-way through the chunk (the
-    // outputs kernel: after half of the readout), so that their registers
-    // are not live while the bf16 state is.  Every wait on the memory
-    // counter also waits for them: nothing in the chunk may spill.
-    if (!OUT && c + 1 < c_end) fetch(c + 1, pre);
-
-    if (OUT) {
-      // ---- the state before the chunk as bf16 operands, each feature row
-      // times its query-side coefficient (so that the query features stay
-      // plain monomials) ----
-      bf16x8 As[NKB][4], Az[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float4 c0 = lds_f4(&sh.coefq[32 * kb + 4 * lg]), c1 = lds_f4(&sh.coefq[32 * kb + 16 + 4 * lg]);
-        auto frag = [&](const f32x4& x0, const f32x4& x1) __attribute__((always_inline)) {
-          return u4_frag(pack_bf16(x0[0] * c0.x, x0[1] * c0.y), pack_bf16(x0[2] * c0.z, x0[3] * c0.w),
-                         pack_bf16(x1[0] * c1.x, x1[1] * c1.y), pack_bf16(x1[2] * c1.z, x1[3] * c1.w));
-        };
-#pragma unroll
-        for (int n = 0; n < 4; ++n) As[kb][n] = frag(S[2 * kb][n], S[2 * kb + 1][n]);
-        Az[kb] = frag(Z[2 * kb], Z[2 * kb + 1]);
-      }
+    // The next chunk's loads are issued part-way through the readout, so
+    // that their registers are not live while the whole bf16 state is.
+    // Every wait on the memory counter also waits for them: nothing in the
+    // chunk may spill.
+    {
       const int nvalid = min(CK, N - c * CK);
       const bool badh = sh.bad != 0;
       auto tile = [&](auto TC) __attribute__((always_inline)) {
@@ -385,13 +464,14 @@ __global__ __launch_bounds__(64, 1) void onepass16w_kernel(const Args16 p) {
         // denominator in every element.  Rows past the end of the sequence
         // fall outside the descriptor and are not written.
         {
-          const float rinv = __builtin_amdgcn_rcpf(Dn[0]);
+          // a bad group id makes the head's outputs NaN (NaN times anything)
+          const float rinv = badh ? __builtin_nanf("") : __builtin_amdgcn_rcpf(Dn[0]);
           const auto ry = buf_rsrc(p.y + (rowbase + (long)c * CK + 16 * T) * DV, (nvalid - 16 * T) * DV * 2);
 #pragma unroll
           for (int n = 0; n < 4; ++n) {
             float y[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = badh ? __builtin_nanf("") : Y[n][e] * rinv;
+            for (int e = 0; e < 4; ++e) y[e] = Y[n][e] * rinv;
             buf_store8(ry, l * DV * 2 + 8 * lg + 32 * n, make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])));
           }
         }
@@ -403,44 +483,7 @@ __global__ __launch_bounds__(64, 1) void onepass16w_kernel(const Args16 p) {
       tile(std::integral_constant<int, 3>{});
     }
 
-    // ---- state update with the chunk: both key steps of a tile back to
-    // back, so that each accumulator is updated in place ----
-    {
-      float kv[2][8];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float x[4];
-        unpack4(k_rows4_at(sh.k + 32 * ks * DH, ko), x);
-        kv[ks][0] = x[0]; kv[ks][1] = x[1]; kv[ks][2] = x[2]; kv[ks][3] = x[3];
-        unpack4(k_rows4_at(sh.k + (32 * ks + 16) * DH, ko), x);
-        kv[ks][4] = x[0]; kv[ks][5] = x[1]; kv[ks][6] = x[2]; kv[ks][7] = x[3];
-      }
-      bf16x8 Vf[2][4];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) Vf[ks][n] = vfrag(ks, n);
-      auto mtile = [&](auto MC) __attribute__((always_inline)) {
-        constexpr int M = decltype(MC)::value;
-        float f0[8], f1[8];
-        key_features<M>(kv[0], l, 0, CK, f0);  // the constant is 1 for every token (fixed up below)
-        key_features<M>(kv[1], l, 0, CK, f1);
-        const bf16x8 A0 = frag8(f0), A1 = frag8(f1);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) S[M][n] = mma32(A1, Vf[1][n], mma32(A0, Vf[0][n], S[M][n]));
-        Z[M] = mma32(A1, ones, mma32(A0, ones, Z[M]));
-      };
-      mtile(std::integral_constant<int, 0>{});
-      mtile(std::integral_constant<int, 1>{});
-      mtile(std::integral_constant<int, 2>{});
-      mtile(std::integral_constant<int, 3>{});
-      mtile(std::integral_constant<int, 4>{});
-      mtile(std::integral_constant<int, 5>{});
-      mtile(std::integral_constant<int, 6>{});
-      mtile(std::integral_constant<int, 7>{});
-      mtile(std::integral_constant<int, 8>{});
-      mtile(std::integral_constant<int, 9>{});
-    }
+    update_chunk();
   }
   // The constant feature (tile 9, row 8: lane row 2, element 0) counted 1 for
   // every row of the last chunk, also past the end of the sequence; the key
