@@ -63,6 +63,7 @@ _SIGS = {
     "oal_fwd_outputs": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_decode_workspace_bytes": ([_P], ctypes.c_size_t),
     "oal_decode_step": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "oal_decode_step_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "oal_contrib_workspace_bytes": ([_P], ctypes.c_size_t),
     "oal_contrib": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_group_dims": ([ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),

@@ -263,6 +263,17 @@ int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const vo
   return oal::launch_decode(a, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
 }
 
+int oal_decode_step_noalloc(const oal_dims* dims, const void* q, const void* k, const void* v,
+                            const oal_coeffs* coeffs, const oal_prep* prep, float* state, void* y, void* stream) {
+  const size_t need = oal_decode_workspace_bytes(dims);
+  void* ws = nullptr;
+  if (need > 0) {
+    if (need > oal::kDecodeScratchBytes) return OAL_ERR_WORKSPACE;
+    if (oal::decode_scratch(&ws) != hipSuccess) return OAL_ERR_HIP;
+  }
+  return oal_decode_step(dims, q, k, v, coeffs, prep, state, y, ws, need, stream);
+}
+
 size_t oal_contrib_workspace_bytes(const oal_dims* dims) {
   if (check_dims(dims, true) != OAL_OK) return 0;
   if (dims->n_q_heads / dims->n_kv_heads > 16) return 0;

@@ -19,6 +19,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "oal_device.h"
 #include "oal_internal.h"
 
@@ -346,6 +348,32 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream) {
     case 32: return launch_decode_d<float, 32>(a, stream);
     default: return launch_decode_d<float, 64>(a, stream);
   }
+}
+
+// ---- scratch for the decode step of callers that cannot allocate ----
+// One array per device that loads the library, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not the device array:
+// the device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 }  // namespace oal

@@ -73,6 +73,9 @@ hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStr
 void decode_slicing(int d_h, long states, int& rows, int& nslice, bool diagonal);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+// the decode step's scratch array of the current device (see oal_decode_step_noalloc)
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
 size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h);
 hipError_t launch_contrib(const ContribLaunch& a, hipStream_t stream);
 

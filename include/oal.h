@@ -227,6 +227,19 @@ int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const vo
                     const oal_coeffs* coeffs, const oal_prep* prep, float* state, void* y,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* oal_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as oal_decode_step, without the
+ * workspace: its scratch is a 32 MiB device array of the library (one per
+ * device that loads it, held until the process ends; its address is looked
+ * up once per device, on the first call with that device current).  Nothing
+ * is allocated.  Returns OAL_ERR_WORKSPACE when oal_decode_workspace_bytes(dims)
+ * exceeds 32 MiB.  Every call on a device uses that device's array, so calls
+ * that may overlap on one device (on different streams without ordering,
+ * or from several threads) race and must not be made. */
+int oal_decode_step_noalloc(const oal_dims* dims, const void* q, const void* k, const void* v,
+                            const oal_coeffs* coeffs, const oal_prep* prep, float* state, void* y, void* stream);
+
 /* Bytes of device workspace oal_contrib needs for `dims` (0 if invalid). */
 size_t oal_contrib_workspace_bytes(const oal_dims* dims);
 
