@@ -63,14 +63,22 @@ struct Octet<float> {
 }  // namespace
 
 // Tokens per partial block: a power of two of at least 128 (measured best on
-// gfx950 for 2k-token prompts: fewer block triples to fold), enough to give
-// every token slot of a CTA (256 threads over d_h / 8 dimension octets) one
-// token, and large enough to keep the blocks per prompt at or below 64.
-static int contrib_block_tokens(int N, int d_h) {
+// gfx950 for 2k-token prompts: fewer block triples to fold).  Each token slot
+// of a CTA (256 threads over d_h / 8 dimension octets) should scan a run of
+// at least eight tokens, so that its loads and sums outweigh the ordered
+// combine, as long as the grid keeps about 1024 CTAs (`ctas_per_block` CTAs
+// per token block); and the blocks per prompt stay at or below 64.
+static int contrib_block_tokens(int N, int d_h, long ctas_per_block) {
+  const int slots = 256 / (d_h / 8);
   int tb = 128;
-  while (tb < 256 / (d_h / 8)) tb *= 2;
+  while (tb < 8 * slots) tb *= 2;
+  while (tb > 128 && (long)((N + tb - 1) / tb) * ctas_per_block < 1024) tb /= 2;
   while ((long)tb * 64 < (long)N) tb *= 2;
   return tb;
+}
+static long contrib_ctas_per_block(int P, int Hq, int Hkv) {
+  const int R = Hq / Hkv, rmax = R <= 1 ? 1 : 2;  // query heads per CTA (launch_contrib_d)
+  return (long)P * Hkv * ((R + rmax - 1) / rmax);
 }
 
 template <typename T, int DH, int RMAX>
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(4 * DH) void contrib_combine_kernel(const float* __
 }
 
 size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h) {
-  const int TB = contrib_block_tokens(N, d_h);
+  const int TB = contrib_block_tokens(N, d_h, contrib_ctas_per_block(P, Hq, Hkv));
   const long nblk = (N + TB - 1) / TB;
   const int R = Hq / Hkv;
   return (size_t)P * Hkv * nblk * (2 * R + 1) * d_h * sizeof(float);
@@ -265,7 +273,7 @@ size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h) {
 
 template <typename T, int DH, int RMAX>
 static hipError_t launch_contrib_r(const ContribLaunch& a, hipStream_t stream) {
-  const int TB = contrib_block_tokens(a.N, a.d_h);
+  const int TB = contrib_block_tokens(a.N, a.d_h, contrib_ctas_per_block(a.P, a.Hq, a.Hkv));
   const int nblk = (a.N + TB - 1) / TB;
   float* part = reinterpret_cast<float*>(a.workspace);
   const int nhg = (a.Hq / a.Hkv + RMAX - 1) / RMAX;
