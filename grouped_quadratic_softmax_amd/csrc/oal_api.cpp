@@ -133,7 +133,8 @@ size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeff
     return oal::onepass16_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->seq_len);
   if (!oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads))
     return diagonal ? 0 : oal_fwd_workspace_bytes(dims);
-  return oal::small_workspace_bytes(dims->batch, dims->n_kv_heads, dims->seq_len, dims->d_h, diagonal,
+  return oal::small_workspace_bytes_for(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->seq_len, dims->d_h,
+                                       diagonal,
                                     dims->dtype);
 }
 

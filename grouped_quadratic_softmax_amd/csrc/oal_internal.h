@@ -58,6 +58,7 @@ bool small_path_supported(int d_h, bool diagonal, int Hq, int Hkv);
 size_t small_segment_bytes(int d_h, bool diagonal);
 // workspace that lets the small path use its full number of segments
 size_t small_workspace_bytes(int B, int Hkv, int N, int d_h, bool diagonal, int dtype);
+size_t small_workspace_bytes_for(int B, int Hq, int Hkv, int N, int d_h, bool diagonal, int dtype);
 hipError_t launch_fwd_small(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 // One-pass prefill at d_h = 16 with bf16 activations: the state stays in MFMA
 // accumulators; sequences are cut into segments whose starting states come
@@ -65,6 +66,11 @@ hipError_t launch_fwd_small(const FwdLaunch& a, size_t workspace_bytes, hipStrea
 bool onepass16_supported(int d_h, int dtype, bool diagonal, int G, int Hq, int Hkv);
 size_t onepass16_workspace_bytes(int B, int Hq, int Hkv, int N);
 hipError_t launch_onepass16(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
+// dimension-wise form at d_h = 64, bf16, heads with their own keys: one wave
+// per (sequence x head, segment)
+bool dimw_supported(int d_h, int dtype, bool diagonal, int Hq, int Hkv);
+size_t dimw_workspace_bytes(int B, int Hkv, int N);
+hipError_t launch_dimw(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 // one wave per (sequence x head, segment): heads with their own keys, no pre-map
 bool onepass16w_supported(int Hq, int Hkv, bool premap);
 size_t onepass16w_workspace_bytes(int B, int Hkv, int N);

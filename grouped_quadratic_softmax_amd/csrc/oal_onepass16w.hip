@@ -66,36 +66,6 @@ struct PreW {
   uint4 q[2], k[2], v[8];
 };
 
-// Raw buffer descriptor (gfx9 family) over `bytes` bytes from `base`: loads
-// past the end read zero, stores past the end are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, max(bytes, 0), 0x00020000);
-}
-typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int voff, uint2 x) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, x), r, voff, 0, 0);
-}
-
-__device__ __forceinline__ uint2 k_rows4_at(const uint16_t* ktile, int off) {
-  const v4s16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16*)(ktile + off));
-  return __builtin_bit_cast(uint2, x);
-}
-
-// Piece permutation of the value rows in LDS, periodic in 16 rows: row r
-// keeps its 16-byte piece p at p ^ vswz16(r).  Over any 16 consecutive rows
-// the eight even (odd) rows send their 32-byte column pairs to each bank
-// quarter exactly twice, so the transposing reads below (16 rows x 32
-// bytes) take the minimal two passes; being periodic, the offsets of rows
-// 16 and 32 further on differ by constants.
-__device__ __forceinline__ int vswz16(int r) { return (((r & 15) >> 1) ^ ((r & 15) >> 3)) & 7; }
-__device__ __forceinline__ bf16x8 u4_frag(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
-}
-
 template <bool OUT, int NG>
 __global__ __launch_bounds__(64, 1) void onepass16w_kernel(const Args16 p) {
   __shared__ LdsW sh;
@@ -515,19 +485,6 @@ __global__ __launch_bounds__(64, 1) void onepass16w_kernel(const Args16 p) {
   }
 }
 
-// Segment sums -> inclusive prefix sums over segments, in place: slot s
-// becomes the sum of the segment sums 0 .. s (float4 per thread).
-__global__ __launch_bounds__(256) void onepass16w_scan_kernel(float4* __restrict__ bs, int nblk, long per_slot) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= per_slot) return;
-  float4 acc = bs[i];
-  for (int s = 1; s < nblk; ++s) {
-    const float4 x = bs[s * per_slot + i];
-    acc = make_float4(acc.x + x.x, acc.y + x.y, acc.z + x.z, acc.w + x.w);
-    bs[s * per_slot + i] = acc;
-  }
-}
-
 struct PlanW {
   int nseg, seg_chunks;
 };
@@ -582,7 +539,7 @@ hipError_t launch_onepass16w(const FwdLaunch& a, size_t workspace_bytes, hipStre
     if (pl.nseg > 1)                                                                                   \
       hipLaunchKernelGGL((onepass16w_kernel<false, 1>), dim3(pl.nseg - 1, BH), dim3(kWave), 0, stream, p); \
     if (pl.nseg > 2)                                                                                   \
-      hipLaunchKernelGGL(onepass16w_scan_kernel, dim3((unsigned)((per_slot + 255) / 256)), dim3(256), 0, stream, \
+      hipLaunchKernelGGL(segment_prefix_scan_kernel, dim3((unsigned)((per_slot + 255) / 256)), dim3(256), 0, stream, \
                          reinterpret_cast<float4*>(a.workspace), pl.nseg - 1, per_slot);             \
     hipLaunchKernelGGL((onepass16w_kernel<true, G_>), dim3(pl.nseg, BH), dim3(kWave), 0, stream, p);   \
   } while (0)

@@ -33,6 +33,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "oal_device.h"
 #include "oal_internal.h"
 
@@ -674,6 +676,11 @@ size_t small_workspace_bytes(int B, int Hkv, int N, int d_h, bool diagonal, int 
   return nseg > 1 ? (size_t)nseg * BH * small_segment_bytes(d_h, diagonal) : 0;
 }
 
+size_t small_workspace_bytes_for(int B, int Hq, int Hkv, int N, int d_h, bool diagonal, int dtype) {
+  const size_t cta = small_workspace_bytes(B, Hkv, N, d_h, diagonal, dtype);
+  return dimw_supported(d_h, dtype, diagonal, Hq, Hkv) ? std::max(cta, dimw_workspace_bytes(B, Hkv, N)) : cta;
+}
+
 bool small_path_supported(int d_h, bool diagonal, int Hq, int Hkv) {
   (void)d_h;
   return Hq / Hkv <= 8 && diagonal;
@@ -681,6 +688,7 @@ bool small_path_supported(int d_h, bool diagonal, int Hq, int Hkv) {
 
 hipError_t launch_fwd_small(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream) {
   if (!a.diagonal) return hipErrorInvalidValue;  // only the dimension-wise form is dispatched here
+  if (dimw_supported(a.d_h, a.dtype, a.diagonal, a.Hq, a.Hkv)) return launch_dimw(a, workspace_bytes, stream);
   if (a.dtype == 1) {
     switch (a.d_h) {
       case 16: return launch_small_t<uint16_t, 16, true>(a, workspace_bytes, stream);

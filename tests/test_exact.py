@@ -100,6 +100,7 @@ def _ulp(x, dtype):
                                                     (16, "f32", False, None), (32, "bf16", False, None),
                                                     (32, "f32", False, None), (64, "bf16", False, None),
                                                     (16, "bf16", True, None), (64, "bf16", True, None),
+                                                    (64, "bf16", True, (3, 3)),
                                                     (32, "f32", True, None)])
 def test_exact_on_sparse_dyadic_inputs(d, dtype, diagonal, heads):
     """Every build (fp32, the bf16-input chunk kernels, the one-pass kernels

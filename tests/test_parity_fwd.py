@@ -94,6 +94,18 @@ def test_dimensionwise_form(d, dtype):
     _run_case(_diag_workload(d, dtype, seed=d))
 
 
+@pytest.mark.parametrize("N", [31, 32, 33, 200, 1000])
+def test_dimensionwise_form_own_keys(N):
+    """d_h = 64, bf16, a KV head per query head: the one-wave build (32-token
+    chunks; N = 1000 runs eight segments with a ragged last chunk)."""
+    _run_case(_diag_workload(64, "bf16", seed=640 + N, Hq=3, Hkv=3, N=N))
+
+
+def test_dimensionwise_own_keys_premap_segments():
+    """The ReBased pre-map on the one-wave build over several segments."""
+    _run_case(S.make(4, batch=2, n_q_heads=3, n_kv_heads=3, seq_len=777))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_dimensionwise_one_segment_matches(dtype):
     """Without room for segment sums the one-pass path walks each sequence in
@@ -119,12 +131,12 @@ def test_dimensionwise_one_segment_matches(dtype):
         assert np.abs(to_np(s_)[..., touched] - ref_s[..., touched]).max() <= 1e-2 * scale
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_dimensionwise_state_and_continuation(dtype):
+@pytest.mark.parametrize("dtype,heads", [("bf16", (4, 2)), ("f32", (4, 2)), ("bf16", (3, 3))])
+def test_dimensionwise_state_and_continuation(dtype, heads):
     require_gpu()
     import torch
     import grouped_quadratic_softmax_amd as oal
-    wl = _diag_workload(64, dtype, seed=7, N=170)
+    wl = _diag_workload(64, dtype, seed=7, N=170, Hq=heads[0], Hkv=heads[1])
     co = gpu_coeffs(wl, wl.group_of_dim)
     assert co.diagonal
     q, k, v = to_dev(wl.q, dtype), to_dev(wl.k, dtype), to_dev(wl.v, dtype)
