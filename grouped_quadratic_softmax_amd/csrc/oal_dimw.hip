@@ -51,7 +51,7 @@ constexpr int D = 64;          // d_h
 constexpr int C = 32;          // tokens per chunk
 constexpr int NT = 9;          // accumulator tiles
 constexpr int NKBW = 5;         // K-blocks of 32 feature rows (the last: tile 8 and a zero tile)
-constexpr int NQ = 5 * NT;     // accumulator quads per lane (tile, column tile 0..3 of H / 4: z)
+constexpr int NBS = 34;        // float4 rows of 64 lanes per segment sum (below)
 constexpr int kSegTarget = 1024;
 constexpr int kSegMax = 8;
 constexpr long PF = packed_features(D);  // rows of the library's packed state
@@ -59,6 +59,7 @@ constexpr long PF = packed_features(D);  // rows of the library's packed state
 struct __align__(16) Lds {
   uint16_t q[C * D];   // mapped query rows [32][64] bf16, 16-byte pieces permuted (vswz16)
   uint16_t k[C * D];   // mapped key rows, same layout; rows past the end zero
+  uint16_t k2[C * D];  // their elementwise squares (rounded once from fp32), same layout
   uint16_t v[C * DV];  // value rows, same layout
   float coef[4][32];   // query-side coefficient of K-block kb's row p (kb 0, 1: linear; 2, 3: squares)
   float gq[D], bq[D], gk[D], bk[D];  // pre-map affine of the head
@@ -100,6 +101,24 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
   const long rowbase = (long)bh * N;
   const int h = bh % p.Hq;  // query head = KV head
   constexpr long SF = PF * (DV + 1);
+
+  // ---- prefix of the earlier segments (segment sums in the compact layout:
+  // rows 4 m + n: S[m][n] of tiles 0..7; row 32, lane (lg, m): z of tile m,
+  // rows 4 lg ..; row 33, lane (0, l): row 0 of tile 8 at columns 16 n + l).
+  // Issued first so that the loads overlap the table set-up. ----
+  f32x4 P[8][4], PZ[NT], P8;
+  if (OUT && seg > 0) {
+    const auto rb = buf_rsrc(reinterpret_cast<const float4*>(p.blocksum) + ((long)(seg - 1) * BH + bh) * NBS * kWave,
+                             NBS * kWave * 16);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        P[m][n] = __builtin_bit_cast(f32x4, buf_load16(rb, 16 * lane + (4 * m + n) * kWave * 16));
+#pragma unroll
+    for (int m = 0; m < NT; ++m) PZ[m] = __builtin_bit_cast(f32x4, buf_load16(rb, (32 * kWave + 16 * lg + m) * 16));
+    P8 = __builtin_bit_cast(f32x4, buf_load16(rb, (33 * kWave + l) * 16));
+  }
 
   // ---- per-head tables ----
   {
@@ -153,16 +172,15 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
       }
   }
   if (OUT && seg > 0) {
-    const auto rb = buf_rsrc(reinterpret_cast<const float4*>(p.blocksum) + ((long)(seg - 1) * BH + bh) * NQ * kWave,
-                             NQ * kWave * 16);
 #pragma unroll
-    for (int m = 0; m < NT; ++m)
+    for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int n = 0; n < 5; ++n) {
-        const f32x4 x = __builtin_bit_cast(f32x4, buf_load16(rb, 16 * lane + (5 * m + n) * kWave * 16));
-        f32x4& acc = n < 4 ? S[m][n] : Z[m];
-        acc = acc + x;
-      }
+      for (int n = 0; n < 4; ++n) S[m][n] = S[m][n] + P[m][n];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) Z[m] = Z[m] + PZ[m];
+    if (lg == 0)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) S[8][n][0] += P8[n];
   }
 
   // ---- chunk rows ----
@@ -183,9 +201,8 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
     for (int u = 0; u < 4; ++u) r.v[u] = buf_load16(rv, off16 + 1024 * u);
   };
   // LayerNorm + affine of one 16-byte piece (dims 8 (lane % 8) ..) of a row
-  // whose other pieces sit in the seven neighbouring lanes
-  auto premap_piece = [&](uint4 w, const float* gm, const float* bt) __attribute__((always_inline)) {
-    float x[8];
+  // whose other pieces sit in the seven neighbouring lanes, in fp32
+  auto premap_vals = [&](uint4 w, const float* gm, const float* bt, float (&x)[8]) __attribute__((always_inline)) {
     unpack4(make_uint2(w.x, w.y), *reinterpret_cast<float(*)[4]>(&x[0]));
     unpack4(make_uint2(w.z, w.w), *reinterpret_cast<float(*)[4]>(&x[4]));
     float s1 = 0.f;
@@ -206,6 +223,8 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
     const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = fmaf(x[i] * rstd, gg[i], bb[i]);
+  };
+  auto pack8 = [](const float (&x)[8]) __attribute__((always_inline)) {
     return make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7]));
   };
   auto commit = [&](int c, const Pre& r) __attribute__((always_inline)) {
@@ -214,13 +233,32 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
     for (int u = 0; u < 4; ++u) {
       const int idx = lane + 64 * u, row = idx / 8;
       const int off = row * D + 8 * ((idx & 7) ^ vswz16(row));
-      uint4 kw = r.k[u];
+      float x[8];
       if (PREMAP) {
-        kw = premap_piece(kw, sh.gk, sh.bk);
-        if (row >= nvalid) kw = make_uint4(0, 0, 0, 0);  // the mapped zero row is beta, not zero
+        premap_vals(r.k[u], sh.gk, sh.bk, x);
+      } else {
+        unpack4(make_uint2(r.k[u].x, r.k[u].y), *reinterpret_cast<float(*)[4]>(&x[0]));
+        unpack4(make_uint2(r.k[u].z, r.k[u].w), *reinterpret_cast<float(*)[4]>(&x[4]));
+      }
+      float x2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x2[i] = x[i] * x[i];
+      uint4 kw = PREMAP ? pack8(x) : r.k[u], kw2 = pack8(x2);
+      if (PREMAP && row >= nvalid) {  // the mapped zero row is beta, not zero
+        kw = make_uint4(0, 0, 0, 0);
+        kw2 = kw;
       }
       *reinterpret_cast<uint4*>(&sh.k[off]) = kw;
-      if (OUT) *reinterpret_cast<uint4*>(&sh.q[off]) = PREMAP ? premap_piece(r.q[u], sh.gq, sh.bq) : r.q[u];
+      *reinterpret_cast<uint4*>(&sh.k2[off]) = kw2;
+      if (OUT) {
+        uint4 qw = r.q[u];
+        if (PREMAP) {
+          float xq[8];
+          premap_vals(qw, sh.gq, sh.bq, xq);
+          qw = pack8(xq);
+        }
+        *reinterpret_cast<uint4*>(&sh.q[off]) = qw;
+      }
       *reinterpret_cast<uint4*>(&sh.v[off]) = r.v[u];
     }
   };
@@ -297,9 +335,7 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // linear tile m (dims 16 m + l) and its squares (tile m + 4)
-      const bf16x8 A = tr8(sh.k, m);
-      const uint4 w = __builtin_bit_cast(uint4, A);
-      const bf16x8 A2 = sq_frag(w, nullptr);
+      const bf16x8 A = tr8(sh.k, m), A2 = tr8(sh.k2, m);
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         S[m][n] = mma32(A, Vf[n], S[m][n]);
@@ -313,20 +349,26 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
     Z[8] = mma32(cst_rows, ones, Z[8]);
   };
 
+  // the state stays in the accumulator registers across chunks (without
+  // this the compiler parks part of it in VGPRs and copies it every chunk)
+  auto pin_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) asm volatile("" : "+a"(S[m][n]));
+      asm volatile("" : "+a"(Z[m]));
+    }
+  };
   if (!OUT) {
     Pre pa, pb;
     fetch(c_begin, pa);
     if (c_begin + 1 < c_end) fetch(c_begin + 1, pb);
     for (int c = c_begin; c < c_end; c += 2) {
-#pragma unroll
-      for (int m = 0; m < NT; ++m) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) asm volatile("" : "+a"(S[m][n]));
-        asm volatile("" : "+a"(Z[m]));
-      }
+      pin_state();
       commit(c, pa);
       if (c + 2 < c_end) fetch(c + 2, pa);
       update_chunk();
+      pin_state();
       if (c + 1 < c_end) {
         commit(c + 1, pb);
         if (c + 3 < c_end) fetch(c + 3, pb);
@@ -343,24 +385,20 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
   const float a_cf = sh.a;
   const bool badh = sh.bad != 0;
   for (int c = c_begin; OUT && c < c_end; ++c) {
-#pragma unroll
-    for (int m = 0; m < NT; ++m) {
-#pragma unroll
-      for (int n = 0; n < 4; ++n) asm volatile("" : "+a"(S[m][n]));
-      asm volatile("" : "+a"(Z[m]));
-    }
+    pin_state();
     commit(c, pre);
     if (c + 1 < c_end) fetch(c + 1, pre);
     const int nvalid = min(C, N - c * C);
-    // key features of both key tiles (token layout: row = key l), per K-block
-    auto key_feats = [&](int kt, bf16x8 (&Kf)[NKBW]) __attribute__((always_inline)) {
-      const uint4 w0 = row_lin(sh.k, 16 * kt + l, 0), w1 = row_lin(sh.k, 16 * kt + l, 1);
-      Kf[0] = __builtin_bit_cast(bf16x8, w0);
-      Kf[1] = __builtin_bit_cast(bf16x8, w1);
-      Kf[2] = sq_frag(w0, nullptr);
-      Kf[3] = sq_frag(w1, nullptr);
-      Kf[4] = cst_tok;
+    // key features of a key tile (token layout: row = key l), K-blocks 0..3
+    // (K-block 4 is the constant, cst_tok); key tile 0 serves both query tiles
+    auto key_feats = [&](int kt, bf16x8 (&Kf)[4]) __attribute__((always_inline)) {
+      Kf[0] = __builtin_bit_cast(bf16x8, row_lin(sh.k, 16 * kt + l, 0));
+      Kf[1] = __builtin_bit_cast(bf16x8, row_lin(sh.k, 16 * kt + l, 1));
+      Kf[2] = __builtin_bit_cast(bf16x8, row_lin(sh.k2, 16 * kt + l, 0));
+      Kf[3] = __builtin_bit_cast(bf16x8, row_lin(sh.k2, 16 * kt + l, 1));
     };
+    bf16x8 Kf0[4];
+    key_feats(0, Kf0);
     auto tile = [&](auto TC) __attribute__((always_inline)) {
       constexpr int T = decltype(TC)::value;
       if (16 * T >= nvalid) return;
@@ -402,11 +440,12 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
           for (int e = 0; e < 4; ++e) pk[kt][e] = 0.f;
           continue;
         }
-        bf16x8 Kf[NKBW];
-        key_feats(kt, Kf);
-        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 Kf1[4];
+        if (kt == 1) key_feats(1, Kf1);
+        const bf16x8(&Kf)[4] = kt == 0 ? Kf0 : Kf1;
+        f32x4 sc = mma32(cst_tok, Bq[4], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int kb = 0; kb < NKBW; ++kb) sc = mma32(Kf[kb], Bq[kb], sc);
+        for (int kb = 0; kb < 4; ++kb) sc = mma32(Kf[kb], Bq[kb], sc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk[kt][e] = (kt < T || 4 * lg + e <= l) ? sc[e] : 0.f;
       }
@@ -437,14 +476,18 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
   if (c_end == nchunks && lg == 0) Z[8][0] -= (float)(nchunks * C - N);
 
   if (!OUT) {
-    float4* bs = reinterpret_cast<float4*>(p.blocksum) + ((long)seg * BH + bh) * NQ * kWave + lane;
+    float4* bs = reinterpret_cast<float4*>(p.blocksum) + ((long)seg * BH + bh) * NBS * kWave + lane;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) bs[(4 * m + n) * kWave] = make_float4(S[m][n][0], S[m][n][1], S[m][n][2], S[m][n][3]);
+    // z is the same in every column: lane (lg, m) keeps tile m's
+    f32x4 zsel = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < NT; ++m)
-#pragma unroll
-      for (int n = 0; n < 5; ++n) {
-        const f32x4& x = n < 4 ? S[m][n] : Z[m];
-        bs[(5 * m + n) * kWave] = make_float4(x[0], x[1], x[2], x[3]);
-      }
+      if (l == m) zsel = Z[m];
+    bs[32 * kWave] = make_float4(zsel[0], zsel[1], zsel[2], zsel[3]);
+    bs[33 * kWave] = lg == 0 ? make_float4(S[8][0][0], S[8][1][0], S[8][2][0], S[8][3][0]) : make_float4(0.f, 0.f, 0.f, 0.f);
   } else if (c_end == nchunks && p.state_out != nullptr) {
     float* so = p.state_out + (long)bh * SF;
 #pragma unroll
@@ -464,7 +507,7 @@ struct PlanD {
   int nseg, seg_chunks;
 };
 
-size_t segsum_bytes_d(int BH, int nseg) { return (size_t)(nseg - 1) * BH * dw::NQ * kWave * sizeof(float4); }
+size_t segsum_bytes_d(int BH, int nseg) { return (size_t)(nseg - 1) * BH * dw::NBS * kWave * sizeof(float4); }
 
 PlanD pland(int BH, int nchunks, size_t workspace_bytes) {
   if (nchunks <= 1) return PlanD{1, 1};
@@ -507,7 +550,7 @@ hipError_t launch_dimw(const FwdLaunch& a, size_t workspace_bytes, hipStream_t s
   p.y = reinterpret_cast<uint16_t*>(a.y);
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;
   p.seg_chunks = pl.seg_chunks; p.blk_chunks = pl.seg_chunks; p.nblk = pl.nseg - 1;
-  const long per_slot = (long)BH * dw::NQ * kWave;
+  const long per_slot = (long)BH * dw::NBS * kWave;
 #define OAL_DIMW(PM)                                                                                          \
   do {                                                                                                        \
     if (pl.nseg > 1)                                                                                          \
