@@ -20,6 +20,7 @@ from .ops import (  # noqa: F401
     feature_count,
     fwd,
     fwd_workspace_bytes,
+    fwd_workspace_bytes_for,
     state_floats,
 )
 

@@ -26,15 +26,24 @@
 //     registers and V^T P^T on MFMA (the value fragments of the update);
 //  3. the state update S += phi_K^T [V | 1].
 //
-// Segments as in the d_h = 16 one-wave kernel: a first kernel sums
-// phi_K^T [V | 1] over each segment but the last, a scan turns the sums into
-// prefix sums over segments, and the outputs kernel starts segment s from
-// the initial state plus the prefix of segments 0 .. s - 1.
+// Segments.  The outputs of segment s start from the initial state plus the
+// sums phi_K^T [V | 1] over segments 0 .. s - 1.  With four or more segments
+// per sequence one launch does it all: a workgroup of four waves takes four
+// consecutive segments; each wave first sums its segment (the last segment
+// of the sequence needs no sum), the waves hand their sums to the later
+// waves of the group through LDS, and with two groups per sequence wave 3 of
+// the first group publishes the group's total for the second group (device-
+// scope stores and a flag, polled with a bound); then every wave produces
+// its segment's outputs.  With two or three segments a first kernel writes
+// the segment sums, a scan turns them into prefix sums and the outputs
+// kernel reads them.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cstddef>
 #include <type_traits>
 
@@ -56,15 +65,39 @@ constexpr int kSegTarget = 1024;
 constexpr int kSegMax = 8;
 constexpr long PF = packed_features(D);  // rows of the library's packed state
 
-struct __align__(16) Lds {
+constexpr int NQF = 5 * NT;    // accumulator quads per lane (S[m][0..3], then z[m])
+
+// kernel modes
+constexpr int kSums = 0;     // sums of phi_K^T [V | 1] over a segment
+constexpr int kOutputs = 1;  // outputs of a segment from the scanned sums
+constexpr int kChained = 2;  // both, four segments per workgroup, prefixes formed in the launch
+
+struct __align__(16) Tiles {  // one wave's chunk
   uint16_t q[C * D];   // mapped query rows [32][64] bf16, 16-byte pieces permuted (vswz16)
   uint16_t k[C * D];   // mapped key rows, same layout; rows past the end zero
   uint16_t k2[C * D];  // their elementwise squares (rounded once from fp32), same layout
   uint16_t v[C * DV];  // value rows, same layout
+};
+struct __align__(16) Tables {  // per head
   float coef[4][32];   // query-side coefficient of K-block kb's row p (kb 0, 1: linear; 2, 3: squares)
   float gq[D], bq[D], gk[D], bk[D];  // pre-map affine of the head
   float a;             // constant coefficient
-  int bad;             // a group id outside [0, G)
+  int bad;             // a group id outside [0, G), or a chained prefix that never arrived
+};
+struct __align__(16) LdsOne {
+  Tiles t[1];
+  Tables tb;
+};
+// The four waves' chunk tiles, and between the two loops (when no tile is in
+// use) the segment sums of waves 0..2 handed to the later waves, in register
+// order (quad 5 m + n: S[m][n], 5 m + 4: z[m]).
+constexpr int kXchBytes = 3 * NQF * kWave * 16;
+struct __align__(16) LdsChained {
+  union {
+    Tiles t[4];
+    unsigned char xch[kXchBytes];
+  };
+  Tables tb;
 };
 
 // 16-byte pieces of the next chunk's rows held by one lane: piece lane + 64 u
@@ -89,15 +122,71 @@ __device__ __forceinline__ float sum8(float x) {
 
 }  // namespace dw
 
-template <bool OUT, bool PREMAP>
-__global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
+// Hand-over of a group total between workgroups on any XCD.  The data and
+// the flag go through device-scope accesses (cache policy SC1: they bypass
+// the non-coherent L2 of each XCD), and the writer waits for its data stores
+// to complete before it sets the flag.  This avoids the whole-L2 write-back
+// and invalidation that release and acquire fences cost.
+constexpr int kDeviceScope = 16;  // SC1 in the buffer instructions' cache-policy operand
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int voff, const f32x4& x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, x), r, voff, 0, kDeviceScope);
+}
+__device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kDeviceScope));
+}
+// The flag holds a 64-bit tag unique to the launch (a process-wide counter
+// from a random start), so whatever the workspace held before cannot pass
+// for it and the flags need no clearing between launches.
+__device__ __forceinline__ void publish_flag(uint64_t* flag, uint64_t tag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the data stores are complete
+  __hip_atomic_store(flag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until another workgroup has published a group total.  Bounded: false
+// after about 2^20 polls.
+__device__ __forceinline__ bool wait_published(const uint64_t* flag, uint64_t tag) {
+  for (int i = 0; i < (1 << 20); ++i) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) {
+      asm volatile("" ::: "memory");
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+template <int MODE, bool PREMAP>
+__global__ __launch_bounds__(MODE == dw::kChained ? 4 * kWave : kWave, 1) void dimw_kernel(const Args16 p) {
   using namespace dw;
-  __shared__ Lds sh;
-  const int seg = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
-  const int lane = threadIdx.x, lg = lane / 16, l = lane % 16;
+  constexpr bool OUT = MODE != kSums;
+  constexpr bool SUMS = MODE != kOutputs;
+  typedef std::conditional_t<MODE == kChained, LdsChained, LdsOne> L;
+  __shared__ L sh;
+  const int lane = threadIdx.x % kWave, lg = lane / 16, l = lane % 16;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  Tiles& tl = sh.t[MODE == kChained ? wv : 0];
+  Tables& tb = sh.tb;
+  // (sequence x head, segment).  Chained launches run at most two groups of
+  // four segments per sequence, group-major: the first groups never wait,
+  // and the second groups that wait (one workgroup per compute unit) are
+  // fewer than the compute units (the planner checks), so some first group
+  // always finds a compute unit whatever the dispatch order.
+  int seg, bh, grp = 0;
+  if constexpr (MODE == kChained) {
+    bh = blockIdx.x % p.BH;
+    grp = blockIdx.x / p.BH;
+    seg = 4 * grp + wv;
+  } else {
+    seg = blockIdx.x;
+    bh = blockIdx.y;
+  }
+  const int BH = MODE == kChained ? p.BH : gridDim.y;
   const int N = p.N;
   const int nchunks = (N + C - 1) / C;
   const int c_begin = seg * p.seg_chunks, c_end = min(c_begin + p.seg_chunks, nchunks);
+  const bool live = c_begin < c_end;          // empty segments past the end
+  const bool last = live && c_end == nchunks;  // the segment that ends the sequence
   const long rowbase = (long)bh * N;
   const int h = bh % p.Hq;  // query head = KV head
   constexpr long SF = PF * (DV + 1);
@@ -107,7 +196,7 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
   // rows 4 lg ..; row 33, lane (0, l): row 0 of tile 8 at columns 16 n + l).
   // Issued first so that the loads overlap the table set-up. ----
   f32x4 P[8][4], PZ[NT], P8;
-  if (OUT && seg > 0) {
+  if (MODE == kOutputs && seg > 0) {
     const auto rb = buf_rsrc(reinterpret_cast<const float4*>(p.blocksum) + ((long)(seg - 1) * BH + bh) * NBS * kWave,
                              NBS * kWave * 16);
 #pragma unroll
@@ -121,25 +210,25 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
   }
 
   // ---- per-head tables ----
-  {
+  if (wv == 0) {
     const float rs = 0.125f, rd = 1.f / 64.f;  // 1/sqrt(d), 1/d at d = 64
     for (int i = lane; i < 128; i += kWave) {
       const int kb = i / 32, pr = i % 32;
       const int r = (kb & 1) * 32 + pr;
       const int g = min(max(p.group_of_dim[h * D + r], 0), p.G - 1);
-      sh.coef[kb][pr] = kb < 2 ? p.cb[h * p.G + g] * rs : p.cc[(h * p.G + g) * p.G + g] * rd;
+      tb.coef[kb][pr] = kb < 2 ? p.cb[h * p.G + g] * rs : p.cc[(h * p.G + g) * p.G + g] * rd;
     }
     if (PREMAP) {
-      sh.gq[lane] = p.gamma_q[h * D + lane];
-      sh.bq[lane] = p.beta_q[h * D + lane];
-      sh.gk[lane] = p.gamma_k[h * D + lane];
-      sh.bk[lane] = p.beta_k[h * D + lane];
+      tb.gq[lane] = p.gamma_q[h * D + lane];
+      tb.bq[lane] = p.beta_q[h * D + lane];
+      tb.gk[lane] = p.gamma_k[h * D + lane];
+      tb.bk[lane] = p.beta_k[h * D + lane];
     }
     const int g = p.group_of_dim[h * D + lane];
     const bool anyb = __ballot(g < 0 || g >= p.G) != 0;
     if (lane == 0) {
-      sh.a = p.ca[h];
-      sh.bad = anyb ? 1 : 0;
+      tb.a = p.ca[h];
+      tb.bad = anyb ? 1 : 0;
     }
   }
   __syncthreads();
@@ -158,7 +247,7 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
     if (m < 8) return abi_index(D, 16 * (m - 4) + row, 16 * (m - 4) + row);
     return row == 0 ? 0 : -1;
   };
-  if (OUT && p.state_in != nullptr) {
+  auto load_state_in = [&]() __attribute__((always_inline)) {
     const float* si = p.state_in + (long)bh * SF;
 #pragma unroll
     for (int m = 0; m < NT; ++m)
@@ -170,8 +259,11 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
         for (int n = 0; n < 4; ++n) S[m][n][e] = si[af * DV + 16 * n + l];
         Z[m][e] = si[PF * DV + af];
       }
-  }
-  if (OUT && seg > 0) {
+  };
+  // the sums of the chained launch start segment 0 from the initial state, so
+  // that every later prefix includes it
+  if (p.state_in != nullptr && (MODE == kOutputs || (MODE == kChained && seg == 0))) load_state_in();
+  if (MODE == kOutputs && seg > 0) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -185,12 +277,12 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
 
   // ---- chunk rows ----
   const int off16 = 16 * lane;
-  auto fetch = [&](int c, Pre& r) __attribute__((always_inline)) {
+  auto fetch = [&](int c, Pre& r, bool wq) __attribute__((always_inline)) {
     const long r0 = rowbase + (long)c * C;
     const int left = N - c * C;
     const auto rk = buf_rsrc(p.k + r0 * D, left * D * 2);
     const auto rv = buf_rsrc(p.v + r0 * DV, left * DV * 2);
-    if (OUT) {
+    if (wq) {
       const auto rq = buf_rsrc(p.q + r0 * D, left * D * 2);
 #pragma unroll
       for (int u = 0; u < 4; ++u) r.q[u] = buf_load16(rq, off16 + 1024 * u);
@@ -227,7 +319,7 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
   auto pack8 = [](const float (&x)[8]) __attribute__((always_inline)) {
     return make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7]));
   };
-  auto commit = [&](int c, const Pre& r) __attribute__((always_inline)) {
+  auto commit = [&](int c, const Pre& r, bool wq) __attribute__((always_inline)) {
     const int nvalid = min(C, N - c * C);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -235,7 +327,7 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
       const int off = row * D + 8 * ((idx & 7) ^ vswz16(row));
       float x[8];
       if (PREMAP) {
-        premap_vals(r.k[u], sh.gk, sh.bk, x);
+        premap_vals(r.k[u], tb.gk, tb.bk, x);
       } else {
         unpack4(make_uint2(r.k[u].x, r.k[u].y), *reinterpret_cast<float(*)[4]>(&x[0]));
         unpack4(make_uint2(r.k[u].z, r.k[u].w), *reinterpret_cast<float(*)[4]>(&x[4]));
@@ -248,18 +340,18 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
         kw = make_uint4(0, 0, 0, 0);
         kw2 = kw;
       }
-      *reinterpret_cast<uint4*>(&sh.k[off]) = kw;
-      *reinterpret_cast<uint4*>(&sh.k2[off]) = kw2;
-      if (OUT) {
+      *reinterpret_cast<uint4*>(&tl.k[off]) = kw;
+      *reinterpret_cast<uint4*>(&tl.k2[off]) = kw2;
+      if (wq) {
         uint4 qw = r.q[u];
         if (PREMAP) {
           float xq[8];
-          premap_vals(qw, sh.gq, sh.bq, xq);
+          premap_vals(qw, tb.gq, tb.bq, xq);
           qw = pack8(xq);
         }
-        *reinterpret_cast<uint4*>(&sh.q[off]) = qw;
+        *reinterpret_cast<uint4*>(&tl.q[off]) = qw;
       }
-      *reinterpret_cast<uint4*>(&sh.v[off]) = r.v[u];
+      *reinterpret_cast<uint4*>(&tl.v[off]) = r.v[u];
     }
   };
 
@@ -331,11 +423,11 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
   auto update_chunk = [&]() __attribute__((always_inline)) {
     bf16x8 Vf[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) Vf[n] = tr8(sh.v, n);
+    for (int n = 0; n < 4; ++n) Vf[n] = tr8(tl.v, n);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // linear tile m (dims 16 m + l) and its squares (tile m + 4)
-      const bf16x8 A = tr8(sh.k, m), A2 = tr8(sh.k2, m);
+      const bf16x8 A = tr8(tl.k, m), A2 = tr8(tl.k2, m);
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         S[m][n] = mma32(A, Vf[n], S[m][n]);
@@ -359,43 +451,109 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
       asm volatile("" : "+a"(Z[m]));
     }
   };
-  if (!OUT) {
+  // ---- segment sum (the segment that ends the sequence needs none) ----
+  if (SUMS && live && !last) {
     Pre pa, pb;
-    fetch(c_begin, pa);
-    if (c_begin + 1 < c_end) fetch(c_begin + 1, pb);
+    fetch(c_begin, pa, false);
+    if (c_begin + 1 < c_end) fetch(c_begin + 1, pb, false);
     for (int c = c_begin; c < c_end; c += 2) {
       pin_state();
-      commit(c, pa);
-      if (c + 2 < c_end) fetch(c + 2, pa);
+      commit(c, pa, false);
+      if (c + 2 < c_end) fetch(c + 2, pa, false);
       update_chunk();
       pin_state();
       if (c + 1 < c_end) {
-        commit(c + 1, pb);
-        if (c + 3 < c_end) fetch(c + 3, pb);
+        commit(c + 1, pb, false);
+        if (c + 3 < c_end) fetch(c + 3, pb, false);
         update_chunk();
       }
     }
   }
 
   Pre pre;
-  if (OUT) {
-    fetch(c_begin, pre);
-    convert_all();
+  if (OUT && live) fetch(c_begin, pre, true);
+  bool lost = false;  // a chained prefix that never arrived
+  if constexpr (MODE == kChained) {
+    // ---- exclusive prefix of the segment: the sums of the earlier waves of
+    // the group through LDS, plus the published total of the earlier group of
+    // the sequence.  Wave 3 of a group that has a successor publishes the
+    // group's inclusive total. ----
+    float4* xch = reinterpret_cast<float4*>(sh.xch);
+    auto quad = [&](int q) __attribute__((always_inline)) -> f32x4& { return q % 5 < 4 ? S[q / 5][q % 5] : Z[q / 5]; };
+    auto slot = [&](int j, int q) __attribute__((always_inline)) {
+      return __builtin_bit_cast(f32x4, xch[(j * NQF + q) * kWave + lane]);
+    };
+    __syncthreads();  // every wave is done with its tiles
+    if (wv < 3)
+#pragma unroll
+      for (int q = 0; q < NQF; ++q) {
+        const f32x4 x = quad(q);
+        xch[(wv * NQF + q) * kWave + lane] = make_float4(x[0], x[1], x[2], x[3]);
+      }
+    __syncthreads();
+    const auto rpub = buf_rsrc(p.pub + (long)bh * NQF * kWave, NQF * kWave * 16);
+    // wave w: the sums of waves 0 .. w - 1 (wave 3 of a first group with a
+    // successor also publishes them plus its own), one pass over the quads
+    auto prefix_from_slots = [&](auto WC, bool publish) __attribute__((always_inline)) {
+      constexpr int W = decltype(WC)::value, QB = 9;  // quads per batch of LDS reads in flight
+#pragma unroll
+      for (int q0 = 0; q0 < NQF; q0 += QB) {
+        f32x4 x[QB];
+#pragma unroll
+        for (int i = 0; i < QB; ++i) x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+          f32x4 r[QB];
+#pragma unroll
+          for (int i = 0; i < QB; ++i) r[i] = slot(j, q0 + i);
+#pragma unroll
+          for (int i = 0; i < QB; ++i) x[i] = x[i] + r[i];
+        }
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+          if (publish) store_coherent(rpub, 16 * ((q0 + i) * kWave + lane), x[i] + quad(q0 + i));
+          quad(q0 + i) = x[i];
+        }
+      }
+    };
+    switch (wv) {
+      case 0: prefix_from_slots(std::integral_constant<int, 0>{}, false); break;
+      case 1: prefix_from_slots(std::integral_constant<int, 1>{}, false); break;
+      case 2: prefix_from_slots(std::integral_constant<int, 2>{}, false); break;
+      default:
+        if (grp == 0 && p.nwg > 1) {
+          prefix_from_slots(std::integral_constant<int, 3>{}, true);
+          if (lane == 0) publish_flag(p.ctl + bh, p.tag);
+        } else {
+          prefix_from_slots(std::integral_constant<int, 3>{}, false);
+        }
+    }
+    if (grp > 0) {
+      lost = !wait_published(p.ctl + bh, p.tag);
+      f32x4 t[NQF];
+#pragma unroll
+      for (int q = 0; q < NQF; ++q) t[q] = load_coherent(rpub, 16 * (q * kWave + lane));
+#pragma unroll
+      for (int q = 0; q < NQF; ++q) quad(q) = quad(q) + t[q];
+    }
+    if (seg == 0 && p.state_in != nullptr) load_state_in();
+    __syncthreads();  // the hand-over slots are read before the tiles reuse them
   }
-  const float a_cf = sh.a;
-  const bool badh = sh.bad != 0;
+  if (OUT && live) convert_all();
+  const float a_cf = tb.a;
+  const bool badh = tb.bad != 0 || lost;
   for (int c = c_begin; OUT && c < c_end; ++c) {
     pin_state();
-    commit(c, pre);
-    if (c + 1 < c_end) fetch(c + 1, pre);
+    commit(c, pre, true);
+    if (c + 1 < c_end) fetch(c + 1, pre, true);
     const int nvalid = min(C, N - c * C);
     // key features of a key tile (token layout: row = key l), K-blocks 0..3
     // (K-block 4 is the constant, cst_tok); key tile 0 serves both query tiles
     auto key_feats = [&](int kt, bf16x8 (&Kf)[4]) __attribute__((always_inline)) {
-      Kf[0] = __builtin_bit_cast(bf16x8, row_lin(sh.k, 16 * kt + l, 0));
-      Kf[1] = __builtin_bit_cast(bf16x8, row_lin(sh.k, 16 * kt + l, 1));
-      Kf[2] = __builtin_bit_cast(bf16x8, row_lin(sh.k2, 16 * kt + l, 0));
-      Kf[3] = __builtin_bit_cast(bf16x8, row_lin(sh.k2, 16 * kt + l, 1));
+      Kf[0] = __builtin_bit_cast(bf16x8, row_lin(tl.k, 16 * kt + l, 0));
+      Kf[1] = __builtin_bit_cast(bf16x8, row_lin(tl.k, 16 * kt + l, 1));
+      Kf[2] = __builtin_bit_cast(bf16x8, row_lin(tl.k2, 16 * kt + l, 0));
+      Kf[3] = __builtin_bit_cast(bf16x8, row_lin(tl.k2, 16 * kt + l, 1));
     };
     bf16x8 Kf0[4];
     key_feats(0, Kf0);
@@ -406,11 +564,11 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
       // and of the within-chunk scores
       bf16x8 Bq[NKBW];
       {
-        const uint4 w0 = row_lin(sh.q, 16 * T + l, 0), w1 = row_lin(sh.q, 16 * T + l, 1);
+        const uint4 w0 = row_lin(tl.q, 16 * T + l, 0), w1 = row_lin(tl.q, 16 * T + l, 1);
         float cf[4][8];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const float4 c0 = lds_f4(&sh.coef[kb][4 * lg]), c1 = lds_f4(&sh.coef[kb][16 + 4 * lg]);
+          const float4 c0 = lds_f4(&tb.coef[kb][4 * lg]), c1 = lds_f4(&tb.coef[kb][16 + 4 * lg]);
           cf[kb][0] = c0.x; cf[kb][1] = c0.y; cf[kb][2] = c0.z; cf[kb][3] = c0.w;
           cf[kb][4] = c1.x; cf[kb][5] = c1.y; cf[kb][6] = c1.z; cf[kb][7] = c1.w;
         }
@@ -452,7 +610,7 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
       const float x8[8] = {pk[0][0], pk[0][1], pk[0][2], pk[0][3], pk[1][0], pk[1][1], pk[1][2], pk[1][3]};
       const bf16x8 Pf = frag8(x8);
 #pragma unroll
-      for (int n = 0; n < 4; ++n) Y[n] = mma32(tr8(sh.v, n), Pf, Y[n]);
+      for (int n = 0; n < 4; ++n) Y[n] = mma32(tr8(tl.v, n), Pf, Y[n]);
       Dn = mma32(ones, Pf, Dn);
       {
         const float rinv = badh ? __builtin_nanf("") : __builtin_amdgcn_rcpf(Dn[0]);
@@ -473,9 +631,9 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
   }
   // the constant feature counted 1 for every row of the last chunk, also past
   // the end of the sequence (the mapped key rows there are zero)
-  if (c_end == nchunks && lg == 0) Z[8][0] -= (float)(nchunks * C - N);
+  if (OUT && last && lg == 0) Z[8][0] -= (float)(nchunks * C - N);
 
-  if (!OUT) {
+  if (MODE == kSums) {
     float4* bs = reinterpret_cast<float4*>(p.blocksum) + ((long)seg * BH + bh) * NBS * kWave + lane;
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -488,7 +646,7 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
       if (l == m) zsel = Z[m];
     bs[32 * kWave] = make_float4(zsel[0], zsel[1], zsel[2], zsel[3]);
     bs[33 * kWave] = lg == 0 ? make_float4(S[8][0][0], S[8][1][0], S[8][2][0], S[8][3][0]) : make_float4(0.f, 0.f, 0.f, 0.f);
-  } else if (c_end == nchunks && p.state_out != nullptr) {
+  } else if (OUT && last && p.state_out != nullptr) {
     float* so = p.state_out + (long)bh * SF;
 #pragma unroll
     for (int m = 0; m < NT; ++m)
@@ -505,18 +663,60 @@ __global__ __launch_bounds__(64, 1) void dimw_kernel(const Args16 p) {
 
 struct PlanD {
   int nseg, seg_chunks;
+  int nwg;  // chained launch with nwg groups of four segments; 0: three-kernel path
 };
 
 size_t segsum_bytes_d(int BH, int nseg) { return (size_t)(nseg - 1) * BH * dw::NBS * kWave * sizeof(float4); }
+// chained launch: ticket and flags, then the published group totals
+// chained launch with two groups: a flag per sequence, then the first
+// groups' published totals
+size_t ctl_bytes_d(int BH) { return ((size_t)BH * sizeof(uint64_t) + 255) / 256 * 256; }
 
-PlanD pland(int BH, int nchunks, size_t workspace_bytes) {
-  if (nchunks <= 1) return PlanD{1, 1};
-  int nseg = std::min({std::max(1, (dw::kSegTarget + BH - 1) / BH), dw::kSegMax, nchunks});
-  for (;; --nseg) {
+uint64_t launch_tag() {
+  static std::atomic<uint64_t> next{0x9e3779b97f4a7c15ull ^
+                                    (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                                    ((uint64_t)(uintptr_t)&next << 17)};
+  return next.fetch_add(1, std::memory_order_relaxed);
+}
+size_t chained_bytes_d(int BH, int nwg) {
+  return nwg > 1 ? ctl_bytes_d(BH) + (size_t)BH * dw::NQF * kWave * sizeof(float4) : 0;
+}
+
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// About kSegTarget waves: with four or more segments per sequence, groups of
+// four segments chained in one launch (two groups when the workspace holds
+// the published totals and the waiting groups are fewer than the compute
+// units, else one); below that the block sums, the scan and the outputs as
+// three launches.
+PlanD pland(int BH, int nchunks, size_t workspace_bytes, int cus) {
+  if (nchunks <= 1) return PlanD{1, 1, 0};
+  const int target = std::min({std::max(1, (dw::kSegTarget + BH - 1) / BH), dw::kSegMax, nchunks});
+  if (target >= 4) {
+    int nwg = target / 4;  // 1 or 2 (kSegMax = 8)
+    if (chained_bytes_d(BH, nwg) > workspace_bytes || BH >= cus) nwg = 1;
+    PlanD pl{};
+    pl.nwg = nwg;
+    pl.nseg = 4 * nwg;
+    pl.seg_chunks = (nchunks + pl.nseg - 1) / pl.nseg;
+    return pl;
+  }
+  for (int nseg = target;; --nseg) {
     PlanD pl{};
     pl.seg_chunks = (nchunks + nseg - 1) / nseg;
     pl.nseg = std::max(1, (nchunks + pl.seg_chunks - 1) / pl.seg_chunks);
-    if (pl.nseg <= 1) return PlanD{1, nchunks};
+    if (pl.nseg <= 1) return PlanD{1, nchunks, 0};
     if (segsum_bytes_d(BH, pl.nseg) <= workspace_bytes) return pl;
   }
 }
@@ -529,14 +729,15 @@ bool dimw_supported(int d_h, int dtype, bool diagonal, int Hq, int Hkv) {
 
 size_t dimw_workspace_bytes(int B, int Hkv, int N) {
   const int BH = B * Hkv;
-  const PlanD pl = pland(BH, (N + dw::C - 1) / dw::C, (size_t)-1);
+  const PlanD pl = pland(BH, (N + dw::C - 1) / dw::C, (size_t)-1, 1 << 30);
+  if (pl.nwg > 0) return chained_bytes_d(BH, pl.nwg);
   return pl.nseg > 1 ? segsum_bytes_d(BH, pl.nseg) : 0;
 }
 
 hipError_t launch_dimw(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream) {
   const int BH = a.B * a.Hkv;
   const int nchunks = (a.N + dw::C - 1) / dw::C;
-  const PlanD pl = pland(BH, nchunks, a.workspace ? workspace_bytes : 0);
+  const PlanD pl = pland(BH, nchunks, a.workspace ? workspace_bytes : 0, device_cus());
   Args16 p{};
   p.q = reinterpret_cast<const uint16_t*>(a.q);
   p.k = reinterpret_cast<const uint16_t*>(a.k);
@@ -550,15 +751,25 @@ hipError_t launch_dimw(const FwdLaunch& a, size_t workspace_bytes, hipStream_t s
   p.y = reinterpret_cast<uint16_t*>(a.y);
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;
   p.seg_chunks = pl.seg_chunks; p.blk_chunks = pl.seg_chunks; p.nblk = pl.nseg - 1;
+  p.nwg = pl.nwg; p.nseg = pl.nseg; p.BH = BH;
+  if (pl.nwg > 1) {
+    p.ctl = reinterpret_cast<uint64_t*>(a.workspace);
+    p.pub = reinterpret_cast<float4*>(reinterpret_cast<char*>(a.workspace) + ctl_bytes_d(BH));
+    p.tag = launch_tag();
+  }
   const long per_slot = (long)BH * dw::NBS * kWave;
 #define OAL_DIMW(PM)                                                                                          \
   do {                                                                                                        \
+    if (pl.nwg > 0) {                                                                                         \
+      hipLaunchKernelGGL((dimw_kernel<dw::kChained, PM>), dim3(BH * pl.nwg), dim3(4 * kWave), 0, stream, p);  \
+      break;                                                                                                  \
+    }                                                                                                         \
     if (pl.nseg > 1)                                                                                          \
-      hipLaunchKernelGGL((dimw_kernel<false, PM>), dim3(pl.nseg - 1, BH), dim3(kWave), 0, stream, p);         \
+      hipLaunchKernelGGL((dimw_kernel<dw::kSums, PM>), dim3(pl.nseg - 1, BH), dim3(kWave), 0, stream, p);     \
     if (pl.nseg > 2)                                                                                          \
       hipLaunchKernelGGL(segment_prefix_scan_kernel, dim3((unsigned)((per_slot + 255) / 256)), dim3(256), 0,   \
                          stream, reinterpret_cast<float4*>(a.workspace), pl.nseg - 1, per_slot);              \
-    hipLaunchKernelGGL((dimw_kernel<true, PM>), dim3(pl.nseg, BH), dim3(kWave), 0, stream, p);                \
+    hipLaunchKernelGGL((dimw_kernel<dw::kOutputs, PM>), dim3(pl.nseg, BH), dim3(kWave), 0, stream, p);        \
   } while (0)
   if (a.premap) {
     OAL_DIMW(true);

@@ -151,6 +151,11 @@ struct Args16 {
   int seg_chunks;   // chunks per segment (outputs kernel)
   int blk_chunks;   // chunks per summed block (divides seg_chunks)
   int nblk;         // blocks summed by the first kernel per (sequence, KV head)
+  // one-launch segment chaining (workgroups of four segment waves)
+  uint64_t* ctl;    // [BH]: == tag once the first group's total is published
+  float4* pub;      // [BH][quads x 64 lanes]: the first groups' totals
+  uint64_t tag;     // unique to the launch
+  int nwg, nseg, BH;
 };
 
 // Key features of tile M for the eight tokens t0 .. t0 + 7 whose k_l this

@@ -125,6 +125,15 @@ def fwd_workspace_bytes(B, Hq, Hkv, N, d_h, d_v, G, dtype) -> int:
     return int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(dims)))
 
 
+def fwd_workspace_bytes_for(q, k, v, coeffs: Coeffs) -> int:
+    """Workspace oal_fwd uses at full parallelism for these tensors and
+    coefficients (oal_fwd_workspace_bytes_for)."""
+    B, Hq, N, d = q.shape
+    dims = _dims(B, Hq, k.shape[1], N, d, v.shape[3], coeffs.n_groups, q.dtype)
+    cs = coeffs.struct()
+    return int(L.lib().oal_fwd_workspace_bytes_for(ctypes.byref(dims), ctypes.byref(cs)))
+
+
 def fwd(q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None, return_state=False,
         y=None, state_out=None, workspace=None):
     """Causal OAL prefill.  q [B, Hq, N, d], k [B, Hkv, N, d], v [B, Hkv, N, 64].

@@ -94,11 +94,35 @@ def test_dimensionwise_form(d, dtype):
     _run_case(_diag_workload(d, dtype, seed=d))
 
 
-@pytest.mark.parametrize("N", [31, 32, 33, 200, 1000])
+@pytest.mark.parametrize("N", [31, 32, 33, 129, 200, 300, 1000])
 def test_dimensionwise_form_own_keys(N):
     """d_h = 64, bf16, a KV head per query head: the one-wave build (32-token
-    chunks; N = 1000 runs eight segments with a ragged last chunk)."""
+    chunks).  N = 33: two segments in three launches; 129 and 200: one group
+    of four chained segments (129: the fourth empty); 300: two chained groups
+    whose second holds one segment and three empty ones; 1000: two full
+    groups with a ragged last chunk."""
     _run_case(_diag_workload(64, "bf16", seed=640 + N, Hq=3, Hkv=3, N=N))
+
+
+def test_dimensionwise_chained_back_to_back():
+    """Two calls of the same shape with different inputs, the second reusing
+    the first's workspace: the hand-over between the chained groups of
+    segments must carry the second call's totals, not the first's."""
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    ws = None
+    for seed in (21, 22):
+        wl = _diag_workload(64, "bf16", seed=seed, N=1000, Hq=3, Hkv=3)
+        co = gpu_coeffs(wl, wl.group_of_dim)
+        q, k, v = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+        if ws is None:
+            nbytes = oal.fwd_workspace_bytes_for(q, k, v, co)
+            assert nbytes > 0  # two chained groups publish a total
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        y = oal.fwd(q, k, v, co, workspace=ws)
+        a, b, c = oracle_coeffs(wl)
+        assert rel_err(to_np(y), O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)) <= TOL["bf16"]
 
 
 def test_dimensionwise_own_keys_premap_segments():
@@ -131,16 +155,19 @@ def test_dimensionwise_one_segment_matches(dtype):
         assert np.abs(to_np(s_)[..., touched] - ref_s[..., touched]).max() <= 1e-2 * scale
 
 
-@pytest.mark.parametrize("dtype,heads", [("bf16", (4, 2)), ("f32", (4, 2)), ("bf16", (3, 3))])
-def test_dimensionwise_state_and_continuation(dtype, heads):
+@pytest.mark.parametrize("dtype,heads,N,n1", [("bf16", (4, 2), 170, 90), ("f32", (4, 2), 170, 90),
+                                              ("bf16", (3, 3), 170, 90), ("bf16", (3, 3), 1000, 600)])
+def test_dimensionwise_state_and_continuation(dtype, heads, N, n1):
+    """Final state and continuation from it; (3, 3) at N = 1000 runs both
+    halves as two chained groups of segments (the initial state enters the
+    first segment's sum)."""
     require_gpu()
     import torch
     import grouped_quadratic_softmax_amd as oal
-    wl = _diag_workload(64, dtype, seed=7, N=170, Hq=heads[0], Hkv=heads[1])
+    wl = _diag_workload(64, dtype, seed=7, N=N, Hq=heads[0], Hkv=heads[1])
     co = gpu_coeffs(wl, wl.group_of_dim)
     assert co.diagonal
     q, k, v = to_dev(wl.q, dtype), to_dev(wl.k, dtype), to_dev(wl.v, dtype)
-    n1 = 90
     sf = oal.state_floats(64, 64)
     sentinel = 7.0
     s1 = torch.full((wl.batch, wl.n_kv_heads, sf), sentinel, device="cuda")
