@@ -122,39 +122,6 @@ __device__ __forceinline__ float sum8(float x) {
 
 }  // namespace dw
 
-// Hand-over of a group total between workgroups on any XCD.  The data and
-// the flag go through device-scope accesses (cache policy SC1: they bypass
-// the non-coherent L2 of each XCD), and the writer waits for its data stores
-// to complete before it sets the flag.  This avoids the whole-L2 write-back
-// and invalidation that release and acquire fences cost.
-constexpr int kDeviceScope = 16;  // SC1 in the buffer instructions' cache-policy operand
-__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int voff, const f32x4& x) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, x), r, voff, 0, kDeviceScope);
-}
-__device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, int voff) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kDeviceScope));
-}
-// The flag holds a 64-bit tag unique to the launch (a process-wide counter
-// from a random start), so whatever the workspace held before cannot pass
-// for it and the flags need no clearing between launches.
-__device__ __forceinline__ void publish_flag(uint64_t* flag, uint64_t tag) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the data stores are complete
-  __hip_atomic_store(flag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until another workgroup has published a group total.  Bounded: false
-// after about 2^20 polls.
-__device__ __forceinline__ bool wait_published(const uint64_t* flag, uint64_t tag) {
-  for (int i = 0; i < (1 << 20); ++i) {
-    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) {
-      asm volatile("" ::: "memory");
-      return true;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return false;
-}
-
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 template <int MODE, bool PREMAP>
 __global__ __launch_bounds__(MODE == dw::kChained ? 4 * kWave : kWave, 1) void dimw_kernel(const Args16 p) {
@@ -671,28 +638,8 @@ size_t segsum_bytes_d(int BH, int nseg) { return (size_t)(nseg - 1) * BH * dw::N
 // chained launch with two groups: a flag per sequence, then the first
 // groups' published totals
 size_t ctl_bytes_d(int BH) { return ((size_t)BH * sizeof(uint64_t) + 255) / 256 * 256; }
-
-uint64_t launch_tag() {
-  static std::atomic<uint64_t> next{0x9e3779b97f4a7c15ull ^
-                                    (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
-                                    ((uint64_t)(uintptr_t)&next << 17)};
-  return next.fetch_add(1, std::memory_order_relaxed);
-}
 size_t chained_bytes_d(int BH, int nwg) {
   return nwg > 1 ? ctl_bytes_d(BH) + (size_t)BH * dw::NQF * kWave * sizeof(float4) : 0;
-}
-
-// compute units of the current device (cached per device)
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = n;
-  }
-  return cached[dev];
 }
 
 // About kSegTarget waves: with four or more segments per sequence, groups of
@@ -722,6 +669,28 @@ PlanD pland(int BH, int nchunks, size_t workspace_bytes, int cus) {
 }
 
 }  // namespace
+
+// A 64-bit tag unique to each chained launch in the process: a counter from
+// a start that mixes the clock and an address
+uint64_t chained_launch_tag() {
+  static std::atomic<uint64_t> next{0x9e3779b97f4a7c15ull ^
+                                    (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                                    ((uint64_t)(uintptr_t)&next << 17)};
+  return next.fetch_add(1, std::memory_order_relaxed);
+}
+
+// compute units of the current device (cached per device)
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 bool dimw_supported(int d_h, int dtype, bool diagonal, int Hq, int Hkv) {
   return d_h == 64 && dtype == 1 && diagonal && Hq == Hkv;
@@ -755,7 +724,7 @@ hipError_t launch_dimw(const FwdLaunch& a, size_t workspace_bytes, hipStream_t s
   if (pl.nwg > 1) {
     p.ctl = reinterpret_cast<uint64_t*>(a.workspace);
     p.pub = reinterpret_cast<float4*>(reinterpret_cast<char*>(a.workspace) + ctl_bytes_d(BH));
-    p.tag = launch_tag();
+    p.tag = chained_launch_tag();
   }
   const long per_slot = (long)BH * dw::NBS * kWave;
 #define OAL_DIMW(PM)                                                                                          \

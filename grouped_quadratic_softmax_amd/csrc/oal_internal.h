@@ -72,6 +72,11 @@ bool dimw_supported(int d_h, int dtype, bool diagonal, int Hq, int Hkv);
 size_t dimw_workspace_bytes(int B, int Hkv, int N);
 hipError_t launch_dimw(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 // one wave per (sequence x head, segment): heads with their own keys, no pre-map
+// Chained one-launch prefills: a tag unique to the launch for the flags of
+// their hand-over, and the compute units of the current device.
+uint64_t chained_launch_tag();
+int device_cus();
+
 bool onepass16w_supported(int Hq, int Hkv, bool premap);
 size_t onepass16w_workspace_bytes(int B, int Hkv, int N);
 hipError_t launch_onepass16w(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);

@@ -232,6 +232,38 @@ __device__ __forceinline__ bf16x8 u4_frag(uint32_t a, uint32_t b, uint32_t c, ui
   return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
 }
 
+// Hand-over of a group total between workgroups on any XCD.  The data and
+// the flag go through device-scope accesses (cache policy SC1: they bypass
+// the non-coherent L2 of each XCD), and the writer waits for its data stores
+// to complete before it sets the flag.  This avoids the whole-L2 write-back
+// and invalidation that release and acquire fences cost.
+constexpr int kDeviceScope = 16;  // SC1 in the buffer instructions' cache-policy operand
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int voff, const f32x4& x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, x), r, voff, 0, kDeviceScope);
+}
+__device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kDeviceScope));
+}
+// The flag holds a 64-bit tag unique to the launch (a process-wide counter
+// from a random start), so whatever the workspace held before cannot pass
+// for it and the flags need no clearing between launches.
+__device__ __forceinline__ void publish_flag(uint64_t* flag, uint64_t tag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the data stores are complete
+  __hip_atomic_store(flag, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until another workgroup has published a group total.  Bounded: false
+// after about 2^20 polls.
+__device__ __forceinline__ bool wait_published(const uint64_t* flag, uint64_t tag) {
+  for (int i = 0; i < (1 << 20); ++i) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) {
+      asm volatile("" ::: "memory");
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
 // Segment sums -> inclusive prefix sums over segments, in place: slot s
 // becomes the sum of the segment sums 0 .. s (float4 per thread).
 __global__ __launch_bounds__(256) void segment_prefix_scan_kernel(float4* __restrict__ bs, int nblk, long per_slot) {

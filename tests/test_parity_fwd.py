@@ -424,6 +424,27 @@ def test_d16_workspace_sizes_stages_and_state(dtype, heads):
                 assert (np.abs(to_np(got)[bi, kh] - ref_s) <= bound).all(), (bi, kh)
 
 
+def test_d16_chained_back_to_back():
+    """d_h = 16, a KV head per query head, two chained groups of segments:
+    two calls with different inputs on one workspace, each against the
+    oracle (the second must not take the first call's hand-over)."""
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    ws = None
+    for seed in (31, 32):
+        wl = S.make(3, batch=2, n_q_heads=3, n_kv_heads=3, seq_len=1500, seed=seed)
+        co = gpu_coeffs(wl, wl.group_of_dim)
+        q, k, v = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+        if ws is None:
+            nbytes = oal.fwd_workspace_bytes_for(q, k, v, co)
+            assert nbytes > 0
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        y = oal.fwd(q, k, v, co, workspace=ws)
+        a, b, c = oracle_coeffs(wl)
+        assert rel_err(to_np(y), O.attention_direct(wl.q, wl.k, wl.v, wl.group_of_dim, a, b, c)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("G,N", [(2, 777), (3, 130), (5, 64), (8, 1000)])
 def test_d16_heads_with_own_keys_grouped(G, N):
     """The one-wave-per-segment build at d_h = 16 (as many query heads as KV
