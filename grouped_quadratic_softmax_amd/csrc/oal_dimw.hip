@@ -176,26 +176,31 @@ __global__ __launch_bounds__(MODE == dw::kChained ? 4 * kWave : kWave, 1) void d
     P8 = __builtin_bit_cast(f32x4, buf_load16(rb, (33 * kWave + l) * 16));
   }
 
-  // ---- per-head tables ----
-  if (wv == 0) {
+  // ---- per-head tables, spread over the workgroup's threads ----
+  {
     const float rs = 0.125f, rd = 1.f / 64.f;  // 1/sqrt(d), 1/d at d = 64
-    for (int i = lane; i < 128; i += kWave) {
+    const int tid = threadIdx.x, nth = blockDim.x;
+    for (int i = tid; i < 128; i += nth) {
       const int kb = i / 32, pr = i % 32;
       const int r = (kb & 1) * 32 + pr;
       const int g = min(max(p.group_of_dim[h * D + r], 0), p.G - 1);
       tb.coef[kb][pr] = kb < 2 ? p.cb[h * p.G + g] * rs : p.cc[(h * p.G + g) * p.G + g] * rd;
     }
     if (PREMAP) {
-      tb.gq[lane] = p.gamma_q[h * D + lane];
-      tb.bq[lane] = p.beta_q[h * D + lane];
-      tb.gk[lane] = p.gamma_k[h * D + lane];
-      tb.bk[lane] = p.beta_k[h * D + lane];
+      const int nw = nth / kWave;  // four arrays over the waves
+      for (int j = wv; j < 4; j += nw) {
+        const float* src = j == 0 ? p.gamma_q : j == 1 ? p.beta_q : j == 2 ? p.gamma_k : p.beta_k;
+        float* dst = j == 0 ? tb.gq : j == 1 ? tb.bq : j == 2 ? tb.gk : tb.bk;
+        dst[lane] = src[h * D + lane];
+      }
     }
-    const int g = p.group_of_dim[h * D + lane];
-    const bool anyb = __ballot(g < 0 || g >= p.G) != 0;
-    if (lane == 0) {
-      tb.a = p.ca[h];
-      tb.bad = anyb ? 1 : 0;
+    if (wv == 0) {
+      const int g = p.group_of_dim[h * D + lane];
+      const bool anyb = __ballot(g < 0 || g >= p.G) != 0;
+      if (lane == 0) {
+        tb.a = p.ca[h];
+        tb.bad = anyb ? 1 : 0;
+      }
     }
   }
   __syncthreads();

@@ -128,11 +128,12 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
   const long rowbase = (long)bh * N;  // rows of q, k, v and y of this (sequence, head)
   constexpr long SF = D16 * (DV + 1);
 
-  // ---- per-head tables (outputs) ----
-  if (OUT && wv == 0) {
+  // ---- per-head tables (outputs), spread over the workgroup's threads ----
+  if (OUT) {
     const int h = bh % p.Hq;
     const float rs = 0.25f, rd = 1.f / 16.f;  // 1/sqrt(d), 1/d at d = 16
-    for (int f = lane; f < FT; f += kWave) {
+    const int tid = threadIdx.x, nth = blockDim.x;
+    for (int f = tid; f < FT; f += nth) {
       int r = 0, t = 0;
       op_feature(f / 16, f % 16, r, t);
       float cf = 0.f;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
       }
       tb.coefq[f] = cf;
     }
-    for (int j = lane; j < 73; j += kWave) {
+    for (int j = tid; j < 73; j += nth) {
       float x = 0.f;
       if (j == 0) {
         x = p.ca[h];
@@ -165,14 +166,14 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
     }
     int g = 0;
     bool badg = false;
-    if (lane < DH) {
+    if (wv == 0 && lane < DH) {
       g = p.group_of_dim[h * DH + lane];
       badg = g < 0 || g >= p.G;
       g = min(max(g, 0), p.G - 1);
     }
     const bool anyb = __ballot(badg) != 0;
-    if (lane == 0) tb.bad = anyb ? 1 : 0;
-    if (lane < 32) {  // lane = 4 group + lg: masks of dims 4 lg .. 4 lg + 3
+    if (wv == 0 && lane == 0) tb.bad = anyb ? 1 : 0;
+    if (wv == 0 && lane < 32) {  // lane = 4 group + lg: masks of dims 4 lg .. 4 lg + 3
       const int gg = lane / 4, lgg = lane % 4;
       uint32_t m0 = 0, m1 = 0;
       for (int i = 0; i < 4; ++i) {
