@@ -179,7 +179,8 @@ def run_main(args):
                                "bf16; step = chi + prefill(+final state) + 1 decode token/seq",
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {
-            "kernel": "oal_fwd prefill at d_h=16: onepass16 block sums + onepass16 outputs (two launches)",
+            "kernel": "onepass16w_kernel (oal_fwd prefill at d_h=16 in one launch: segment sums and outputs of "
+                      "four segments per workgroup, two chained workgroups per sequence)",
             "bound": "hbm",
             "achieved": gbs,
             "peak": PEAK_HBM_GBS,
@@ -277,7 +278,9 @@ def run_secondary(args):
     tok = wl.batch * wl.seq_len
     io = tok * wl.n_q_heads * (2 * 64 * 2) + tok * wl.n_kv_heads * (2 * 64 * 2)
     out["c4_rebased_prefill"] = {"ms": ms, "tokens_per_s": tok / (ms * 1e-3),
-                                 "hbm_frac": io / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                                 "hbm_frac": io / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                 "kernel": "dimw_kernel (one launch, chained segment groups)",
+                                 "traffic": load_traffic("dimw_rebased_prefill")}
     del pre, q, k, v
     # 32k-token prefill, 16 heads, 8 contribution-sorted groups
     wl = S.make(5)
@@ -298,11 +301,11 @@ def run_pmc_target(args):
     """Launch only one kernel repeatedly, for rocprofv3 counter passes.
 
     ``based16``: the prefill of the timed workload (B=8, H=16, N=8192,
-    d_h=16: the one-pass block-sum and output kernels); ``decode``: the
+    d_h=16: the one-launch chained kernel); ``decode``: the
     batched decode step (256 sequences x 16 heads, fp32 states);
     ``readout`` / ``states``: the chunk readout / chunk scan of the
     Qwen-shaped GQA layer (B=4, N=2048, Hq=14, Hkv=2, d_h=64);
-    ``rebased``: the one-pass prefill of the ReBased workload in the
+    ``rebased``: the one-launch prefill of the ReBased workload in the
     dimension-wise form (B=16, H=8, N=2048); ``long``: the prefill of the
     long-context multi-head workload (B=1, H=16, N=32768, d_h=64, eight
     groups from its contribution scores); ``copy``: a plain device copy of
