@@ -105,17 +105,37 @@ def coeffs_from_factor(eps, L):
 # kernel evaluation
 # --------------------------------------------------------------------------
 
-def premap(x, gamma, beta, ln_eps=1e-5):
-    """ReBased pre-map gamma * norm(x) + beta along the last axis.
+def premap(x, gamma, beta, ln_eps=1e-5, kind="layernorm"):
+    """Pre-map gamma * norm(x) + beta along the last axis.
 
-    [ReBased] section "Let training place the parabola": the feature map is
-    (gamma * norm(x) + beta) squared elementwise; this returns the part inside
-    the square.  norm is LayerNorm (mean and biased variance over d_h).
+    kind "layernorm": [ReBased] section "Let training place the parabola":
+    the feature map is (gamma * norm(x) + beta) squared elementwise; this
+    returns the part inside the square.  norm is LayerNorm (mean and biased
+    variance over d_h, eps added to the variance).
+
+    kind "l2": the TaylorShift-style map of [OAL] App. F.1 (the TaylorShift
+    baseline): queries and keys are scaled to unit l2 norm, norm(x) =
+    x / sqrt(sum_r x_r^2 + eps) (reading: eps inside the root, as for
+    LayerNorm).  With gamma = tau * sqrt(d_h) on the queries, gamma = 1 on
+    the keys and beta = 0, the scaled dot product q~.k~ / sqrt(d_h) is that
+    baseline's s = tau * qhat.khat, and a = 1, b = 1, c = 1/2 give its
+    polynomial 1 + s + s^2 / 2.
     """
     x = np.asarray(x, dtype=np.float64)
-    mu = x.mean(axis=-1, keepdims=True)
-    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
-    return np.asarray(gamma, np.float64) * (x - mu) / np.sqrt(var + ln_eps) + np.asarray(beta, np.float64)
+    if kind == "layernorm":
+        mu = x.mean(axis=-1, keepdims=True)
+        var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+        xn = (x - mu) / np.sqrt(var + ln_eps)
+    elif kind == "l2":
+        xn = x / np.sqrt((x ** 2).sum(axis=-1, keepdims=True) + ln_eps)
+    else:
+        raise ValueError(f"unknown pre-map kind {kind!r}")
+    return np.asarray(gamma, np.float64) * xn + np.asarray(beta, np.float64)
+
+
+def _premap_p(x, p, which, head):
+    """premap with the parameters of dict p for 'q' or 'k' of one head."""
+    return premap(x, p["gamma_" + which][head], p["beta_" + which][head], p["ln_eps"], p.get("kind", "layernorm"))
 
 
 def group_scores(q, k, group_of_dim, n_groups):
@@ -165,7 +185,8 @@ def attention_direct(Q, K, V, group_of_dim, a, b, c, premap_params=None, rows=No
 
     Q: [B, Hq, N, d]; K: [B, Hkv, N, d]; V: [B, Hkv, N, dv]; group_of_dim:
     [Hq, d]; a: [Hq]; b: [Hq, G]; c: [Hq, G, G]; premap_params: None or the
-    ReBased affine {"gamma_q", "beta_q", "gamma_k", "beta_k", "ln_eps"}.
+    pre-map {"gamma_q", "beta_q", "gamma_k", "beta_k", "ln_eps"[, "kind"]}
+    (kind "layernorm", the default, or "l2"; see ``premap``).
     ``rows``: optional sorted array of output positions (0-based) to evaluate;
     each y_i is computed from its own definition, so any subset is exact.
     Returns y [B, Hq, R, dv] (and num [.., dv], den [..] if return_parts).
@@ -189,8 +210,8 @@ def attention_direct(Q, K, V, group_of_dim, a, b, c, premap_params=None, rows=No
             k = K[bi, kh]
             if premap_params is not None:
                 p = premap_params
-                q = premap(q, p["gamma_q"][h], p["beta_q"][h], p["ln_eps"])
-                k = premap(k, p["gamma_k"][kh], p["beta_k"][kh], p["ln_eps"])
+                q = _premap_p(q, p, "q", h)
+                k = _premap_p(k, p, "k", kh)
             G = len(b[h])
             s = group_scores(q, k, group_of_dim[h], G)
             w = kappa_from_scores(s, a[h], b[h], c[h]) * causal
@@ -268,14 +289,13 @@ def attention_recurrent_packed(Q, K, V, group_of_dim, a, b, c, premap_params=Non
             k = K[bi, kh]
             if premap_params is not None:
                 p = premap_params
-                k = premap(k, p["gamma_k"][kh], p["beta_k"][kh], p["ln_eps"])
+                k = _premap_p(k, p, "k", kh)
             fk = phi_k_packed(k)
             fq = {}
             for h in heads:
                 q = Q[bi, h]
                 if premap_params is not None:
-                    q = premap(q, premap_params["gamma_q"][h], premap_params["beta_q"][h],
-                               premap_params["ln_eps"])
+                    q = _premap_p(q, premap_params, "q", h)
                 fq[h] = phi_q_packed(q, group_of_dim[h], a[h], b[h], c[h])
             st = S[bi, kh]
             for i in range(N):
@@ -326,7 +346,7 @@ def attention_recurrent_ordered(Q, K, V, group_of_dim, a, b, c):
     return y
 
 
-def state_from_prefix(K, V, premap_k=None, ln_eps=1e-5):
+def state_from_prefix(K, V, premap_k=None, ln_eps=1e-5, kind="layernorm"):
     """Packed state sum_j phi_k(k_j) [v_j, 1]^T of one (sequence, KV head).
 
     K: [n, d], V: [n, dv]; premap_k: optional (gamma_k, beta_k) for the
@@ -335,7 +355,7 @@ def state_from_prefix(K, V, premap_k=None, ln_eps=1e-5):
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
     if premap_k is not None:
-        K = premap(K, premap_k[0], premap_k[1], ln_eps)
+        K = premap(K, premap_k[0], premap_k[1], ln_eps, kind)
     fk = phi_k_packed(K)
     U = np.concatenate([V, np.ones((V.shape[0], 1))], axis=1)
     return fk.T @ U
@@ -361,14 +381,14 @@ def decode_step(state, q, k, v, group_of_dim, a, b, c, n_q_heads, premap_params=
             kk = k[s, kh]
             if premap_params is not None:
                 p = premap_params
-                kk = premap(kk, p["gamma_k"][kh], p["beta_k"][kh], p["ln_eps"])
+                kk = _premap_p(kk, p, "k", kh)
             st[s, kh] += np.outer(phi_k_packed(kk), np.concatenate([v[s, kh], [1.0]]))
         for h in range(n_q_heads):
             kh = _kv_head(h, n_q_heads, Hkv)
             qq = q[s, h]
             if premap_params is not None:
                 p = premap_params
-                qq = premap(qq, p["gamma_q"][h], p["beta_q"][h], p["ln_eps"])
+                qq = _premap_p(qq, p, "q", h)
             ut = phi_q_packed(qq, group_of_dim[h], a[h], b[h], c[h]) @ st[s, kh]
             y[s, h] = ut[:dv] / ut[dv]
     return y, st

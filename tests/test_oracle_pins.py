@@ -383,6 +383,53 @@ def test_rebased_premap_and_feature_readings():
     assert val == pytest.approx(float(np.dot(qt, kt)) ** 2, rel=1e-12)
 
 
+def test_premap_l2_golden(golden):
+    """The TaylorShift-style pre-map (unit l2 norm, then gamma and beta),
+    against hand-worked values: no centring, the sum (not the mean) of
+    squares, epsilon inside the root."""
+    g = golden("premap_l2.json")
+    for case in g["cases"]:
+        got = O.premap(np.array(case["x"], float), np.array(case["gamma"], float), np.array(case["beta"], float),
+                       case["eps"], kind="l2")
+        assert np.allclose(got, case["want"], rtol=1e-15, atol=1e-15), (case, got)
+
+
+def test_premap_l2_unit_norm_and_scale_invariance():
+    rng = np.random.default_rng(41)
+    d = 16
+    x = _rand(rng, 7, d, std=3)
+    z = O.premap(x, np.ones(d), np.zeros(d), 0.0, kind="l2")
+    assert np.allclose(np.linalg.norm(z, axis=-1), 1.0, rtol=1e-14)
+    assert np.allclose(O.premap(4.5 * x, np.ones(d), np.zeros(d), 0.0, kind="l2"), z, rtol=1e-14)
+    # the direction is kept (z is a positive multiple of x)
+    assert np.allclose(z * np.linalg.norm(x, axis=-1, keepdims=True), x, rtol=1e-13)
+
+
+def test_taylorshift_through_the_grouped_kernel():
+    """[OAL] App. F.1, the TaylorShift baseline: kappa = 1 + s + s^2 / 2 with
+    s = tau * qhat . khat over unit vectors, causal and normalised.  The
+    oracle's path (l2 pre-map with gamma_q = tau sqrt(d), gamma_k = 1, beta =
+    0, then one group with a = 1, b = 1, c = 1/2) must equal that formula
+    written out here with numpy's norm."""
+    rng = np.random.default_rng(42)
+    B, H, N, d, dv = 2, 3, 9, 8, 5
+    Q, K, V = _rand(rng, B, H, N, d), _rand(rng, B, H, N, d), _rand(rng, B, H, N, dv)
+    tau = np.array([0.7, 1.0, 2.3])
+    p = {"gamma_q": np.repeat((tau * math.sqrt(d))[:, None], d, 1), "beta_q": np.zeros((H, d)),
+         "gamma_k": np.ones((H, d)), "beta_k": np.zeros((H, d)), "ln_eps": 0.0, "kind": "l2"}
+    got = O.attention_direct(Q, K, V, np.zeros((H, d), int), np.ones(H), np.ones((H, 1)), np.full((H, 1, 1), 0.5),
+                             premap_params=p)
+    want = np.zeros_like(got)
+    for bi in range(B):
+        for h in range(H):
+            qh = Q[bi, h] / np.linalg.norm(Q[bi, h], axis=-1, keepdims=True)
+            kh = K[bi, h] / np.linalg.norm(K[bi, h], axis=-1, keepdims=True)
+            s = tau[h] * qh @ kh.T
+            w = np.tril(1 + s + 0.5 * s ** 2)
+            want[bi, h] = (w @ V[bi, h]) / w.sum(1, keepdims=True)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- contribution score
 
 def test_chi_bruteforce_equals_separable_varlen_gqa():
