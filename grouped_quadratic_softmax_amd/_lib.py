@@ -32,7 +32,7 @@ class OalCoeffs(ctypes.Structure):
 
 class OalPrep(ctypes.Structure):
     _fields_ = [("gamma_q", ctypes.c_void_p), ("beta_q", ctypes.c_void_p), ("gamma_k", ctypes.c_void_p),
-                ("beta_k", ctypes.c_void_p), ("ln_eps", ctypes.c_float)]
+                ("beta_k", ctypes.c_void_p), ("ln_eps", ctypes.c_float), ("kind", ctypes.c_int32)]
 
 
 class OalGroupParams(ctypes.Structure):

@@ -51,6 +51,7 @@ int check_prep(const oal_prep* p) {
   if (p->gamma_q == nullptr || p->beta_q == nullptr || p->gamma_k == nullptr || p->beta_k == nullptr)
     return OAL_ERR_INVALID_ARG;
   if (!(p->ln_eps >= 0.f) || !isfinite(p->ln_eps)) return OAL_ERR_INVALID_ARG;
+  if (p->kind != OAL_PREMAP_LAYERNORM && p->kind != OAL_PREMAP_L2) return OAL_ERR_INVALID_ARG;
   return OAL_OK;
 }
 
@@ -192,6 +193,7 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   if (prep) {
     a.gamma_q = prep->gamma_q; a.beta_q = prep->beta_q; a.gamma_k = prep->gamma_k; a.beta_k = prep->beta_k;
     a.ln_eps = prep->ln_eps;
+    a.premap_kind = prep->kind;
   }
   a.state_in = state_in; a.state_out = state_out; a.y = y; a.workspace = workspace;
   a.diagonal = diagonal;
@@ -259,6 +261,7 @@ int oal_decode_step(const oal_dims* dims, const void* q, const void* k, const vo
   if (prep) {
     a.gamma_q = prep->gamma_q; a.beta_q = prep->beta_q; a.gamma_k = prep->gamma_k; a.beta_k = prep->beta_k;
     a.ln_eps = prep->ln_eps;
+    a.premap_kind = prep->kind;
   }
   a.state = state; a.y = y; a.workspace = workspace;
   return oal::launch_decode(a, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;

@@ -32,16 +32,16 @@ constexpr int NC = DV + 1;
 
 template <int DH>
 __device__ __forceinline__ void premap_vec(float* x, const float* __restrict__ gamma,
-                                           const float* __restrict__ beta, float eps) {
+                                           const float* __restrict__ beta, float eps, PremapNorm pn) {
   float mu = 0.f;
   for (int c = 0; c < DH; ++c) mu += x[c];
-  mu *= 1.f / DH;
+  mu *= pn.mean_w;
   float var = 0.f;
   for (int c = 0; c < DH; ++c) {
     const float t = x[c] - mu;
     var += t * t;
   }
-  var *= 1.f / DH;
+  var *= pn.var_w;
   const float inv = 1.f / sqrtf(var + eps);
   for (int c = 0; c < DH; ++c) x[c] = gamma[c] * (x[c] - mu) * inv + beta[c];
 }
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     const int32_t* __restrict__ group_of_dim, const float* __restrict__ ca,
     const float* __restrict__ cb, const float* __restrict__ cc, int G,
     const float* __restrict__ gamma_q, const float* __restrict__ beta_q,
-    const float* __restrict__ gamma_k, const float* __restrict__ beta_k, float ln_eps,
+    const float* __restrict__ gamma_k, const float* __restrict__ beta_k, float ln_eps, PremapNorm pn,
     float* __restrict__ state, float* __restrict__ part, T* __restrict__ y, int Hq, int Hkv, int rows,
     int diagonal) {
   constexpr int D = (int)packed_features(DH);
@@ -139,10 +139,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   }
   __syncthreads();
   if (PREMAP) {
-    if (tid == 0) premap_vec<DH>(khat, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
+    if (tid == 0) premap_vec<DH>(khat, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps, pn);
     if (tid >= 64 && tid - 64 < R) {
       const int hh = tid - 64, h = kvh * R + hh;
-      premap_vec<DH>(qhat[hh], gamma_q + h * DH, beta_q + h * DH, ln_eps);
+      premap_vec<DH>(qhat[hh], gamma_q + h * DH, beta_q + h * DH, ln_eps, pn);
     }
   }
   for (int idx = tid; idx < R * DH; idx += blockDim.x) {
@@ -313,11 +313,12 @@ static hipError_t launch_decode_r(const DecodeLaunch& a, hipStream_t stream) {
   if (a.premap)
     hipLaunchKernelGGL((decode_partial_kernel<T, DH, RMAX, true>), grid, dim3(256), shm, stream, qq, kk, vv,
                        a.group_of_dim, a.ca, a.cb, a.cc, a.G, a.gamma_q, a.beta_q, a.gamma_k, a.beta_k,
-                       a.ln_eps, a.state, part, yy, a.Hq, a.Hkv, rows, (int)a.diagonal);
+                       a.ln_eps, premap_norm(a.premap_kind, DH), a.state, part, yy, a.Hq, a.Hkv, rows,
+                       (int)a.diagonal);
   else
     hipLaunchKernelGGL((decode_partial_kernel<T, DH, RMAX, false>), grid, dim3(256), shm, stream, qq, kk, vv,
                        a.group_of_dim, a.ca, a.cb, a.cc, a.G, nullptr, nullptr, nullptr, nullptr, 0.f,
-                       a.state, part, yy, a.Hq, a.Hkv, rows, (int)a.diagonal);
+                       premap_norm(0, DH), a.state, part, yy, a.Hq, a.Hkv, rows, (int)a.diagonal);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nslice == 1) return err;
   const long total = (long)a.B * a.Hq * DV;

@@ -135,6 +135,17 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 // sum / max over aligned groups of 4 lanes, in every lane of the group
+// Normalisation of the pre-map gamma * norm(x) + beta over d_h:
+//   mu = mean_w * sum_r x_r,  norm(x) = (x - mu) / sqrt(var_w * sum_r (x_r - mu)^2 + eps)
+// LayerNorm (kind 0): mean_w = var_w = 1 / d_h; unit l2 norm (kind 1):
+// mean_w = 0, var_w = 1.
+struct PremapNorm {
+  float mean_w, var_w;
+};
+__host__ __device__ inline PremapNorm premap_norm(int kind, int dh) {
+  return kind == 1 ? PremapNorm{0.f, 1.f} : PremapNorm{1.f / (float)dh, 1.f / (float)dh};
+}
+
 __device__ __forceinline__ float quad_sum(float x) {
   x += dpp<kDppXor1>(x, 0.f);
   return x + dpp<kDppXor2>(x, 0.f);

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(MODE == dw::kChained ? 4 * kWave : kWave, 1) void d
 #pragma unroll
     for (int u = 0; u < 4; ++u) r.v[u] = buf_load16(rv, off16 + 1024 * u);
   };
-  // LayerNorm + affine of one 16-byte piece (dims 8 (lane % 8) ..) of a row
+  // Pre-map (LayerNorm or unit l2 norm, then the affine) of one 16-byte piece (dims 8 (lane % 8) ..) of a row
   // whose other pieces sit in the seven neighbouring lanes, in fp32
   auto premap_vals = [&](uint4 w, const float* gm, const float* bt, float (&x)[8]) __attribute__((always_inline)) {
     unpack4(make_uint2(w.x, w.y), *reinterpret_cast<float(*)[4]>(&x[0]));
@@ -272,14 +272,14 @@ __global__ __launch_bounds__(MODE == dw::kChained ? 4 * kWave : kWave, 1) void d
     float s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) s1 += x[i];
-    const float mu = sum8(s1) * (1.f / D);
+    const float mu = sum8(s1) * p.pn.mean_w;
     float s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       x[i] -= mu;
       s2 += x[i] * x[i];
     }
-    const float rstd = __builtin_amdgcn_rsqf(sum8(s2) * (1.f / D) + p.ln_eps);
+    const float rstd = __builtin_amdgcn_rsqf(sum8(s2) * p.pn.var_w + p.ln_eps);
     const int d0 = 8 * (lane & 7);
     const float4 g0 = lds_f4(gm + d0), g1 = lds_f4(gm + d0 + 4);
     const float4 b0 = lds_f4(bt + d0), b1 = lds_f4(bt + d0 + 4);
@@ -720,6 +720,7 @@ hipError_t launch_dimw(const FwdLaunch& a, size_t workspace_bytes, hipStream_t s
   p.ca = a.ca; p.cb = a.cb; p.cc = a.cc; p.G = a.G;
   p.gamma_q = a.gamma_q; p.beta_q = a.beta_q; p.gamma_k = a.gamma_k; p.beta_k = a.beta_k;
   p.ln_eps = a.ln_eps;
+  p.pn = premap_norm(a.premap_kind, dw::D);
   p.state_in = a.state_in; p.state_out = a.state_out;
   p.blocksum = reinterpret_cast<float*>(a.workspace);
   p.y = reinterpret_cast<uint16_t*>(a.y);

@@ -19,6 +19,7 @@ struct FwdLaunch {
   bool premap;
   const float *gamma_q, *beta_q, *gamma_k, *beta_k;
   float ln_eps;
+  int premap_kind = 0;  // OAL_PREMAP_LAYERNORM or OAL_PREMAP_L2
   const float* state_in;
   float* state_out;
   void* y;
@@ -34,6 +35,7 @@ struct DecodeLaunch {
   bool premap;
   const float *gamma_q, *beta_q, *gamma_k, *beta_k;
   float ln_eps;
+  int premap_kind = 0;  // OAL_PREMAP_LAYERNORM or OAL_PREMAP_L2
   float* state;
   void* y;
   void* workspace;

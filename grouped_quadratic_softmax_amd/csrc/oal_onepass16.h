@@ -143,6 +143,7 @@ struct Args16 {
   int G;
   const float *gamma_q, *beta_q, *gamma_k, *beta_k;
   float ln_eps;
+  PremapNorm pn;    // the pre-map's normalisation (LayerNorm or unit l2 norm)
   const float* state_in;
   float* state_out;
   float* blocksum;  // [nblk][BH][FT][DV + 1] fp32: sums of phi_K^T [V | 1] over blocks of chunks

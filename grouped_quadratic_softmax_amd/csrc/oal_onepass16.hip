@@ -75,17 +75,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// ReBased pre-map of four dims of a token row spread over four consecutive
+// Pre-map (LayerNorm or unit l2 norm, then the affine) of four dims of a token row spread over four consecutive
 // lanes, with this lane's gamma and beta values.
-__device__ __forceinline__ void premap4(float (&x)[4], const float (&gamma)[4], const float (&beta)[4], float eps) {
+__device__ __forceinline__ void premap4(float (&x)[4], const float (&gamma)[4], const float (&beta)[4], float eps,
+                                        PremapNorm pn) {
   float s = x[0] + x[1] + x[2] + x[3];
   s = quad_sum(s);
-  const float mu = s * (1.f / DH);
+  const float mu = s * pn.mean_w;
   float v2 = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v2 += (x[i] - mu) * (x[i] - mu);
   v2 = quad_sum(v2);
-  const float inv = 1.f / sqrtf(v2 * (1.f / DH) + eps);
+  const float inv = 1.f / sqrtf(v2 * pn.var_w + eps);
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = gamma[i] * (x[i] - mu) * inv + beta[i];
 }
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(256, OP16_OCC) void onepass16_kernel(const Args16 p
   auto stage_q_vals = [&](float (&x)[4], int c, int hh) __attribute__((always_inline)) {
     (void)hh;
     const bool ok = c * CK + srow < N;
-    if (PREMAP) premap4(x, gq, bq, p.ln_eps);
+    if (PREMAP) premap4(x, gq, bq, p.ln_eps, p.pn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = ok ? x[i] : 0.f;
     lds_st_f4(&sh.qd[srow][4 * sq], x[0], x[1], x[2], x[3]);
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256, OP16_OCC) void onepass16_kernel(const Args16 p
     const bool ok = c * CK + srow < N;
     float x[4];
     unpack4(lds_u2(slot + RK + srow * DH + 4 * sq), x);
-    if (PREMAP) premap4(x, gk, bk, p.ln_eps);
+    if (PREMAP) premap4(x, gk, bk, p.ln_eps, p.pn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = ok ? x[i] : 0.f;
@@ -666,6 +667,7 @@ hipError_t launch_onepass16(const FwdLaunch& a, size_t workspace_bytes, hipStrea
   p.ca = a.ca; p.cb = a.cb; p.cc = a.cc; p.G = a.G;
   p.gamma_q = a.gamma_q; p.beta_q = a.beta_q; p.gamma_k = a.gamma_k; p.beta_k = a.beta_k;
   p.ln_eps = a.ln_eps;
+  p.pn = premap_norm(a.premap_kind, DH);
   p.state_in = a.state_in; p.state_out = a.state_out;
   p.blocksum = reinterpret_cast<float*>(a.workspace);
   p.y = reinterpret_cast<uint16_t*>(a.y);

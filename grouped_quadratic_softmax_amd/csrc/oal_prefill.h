@@ -214,16 +214,16 @@ __device__ __forceinline__ void load_vals(const float* p, float* out) {
   }
 }
 
-// LayerNorm + affine of a row split over 4 consecutive lanes, each holding
-// n values at dimension offset d0 (ReBased pre-map, biased variance).
+// Pre-map (normalisation of kind pn, then the affine) of a row split over 4
+// consecutive lanes, each holding n values at dimension offset d0.
 template <int DH, int n>
 __device__ __forceinline__ void premap4(float* x, int d0, const float* __restrict__ gamma,
-                                        const float* __restrict__ beta, float eps) {
+                                        const float* __restrict__ beta, float eps, PremapNorm pn) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < n; ++i) s += x[i];
   s = quad_sum(s);
-  const float mu = s * (1.f / DH);
+  const float mu = s * pn.mean_w;
   float v2 = 0.f;
 #pragma unroll
   for (int i = 0; i < n; ++i) {
@@ -231,7 +231,7 @@ __device__ __forceinline__ void premap4(float* x, int d0, const float* __restric
     v2 += t * t;
   }
   v2 = quad_sum(v2);
-  const float inv = 1.f / sqrtf(v2 * (1.f / DH) + eps);
+  const float inv = 1.f / sqrtf(v2 * pn.var_w + eps);
 #pragma unroll
   for (int i = 0; i < n; ++i) x[i] = gamma[d0 + i] * (x[i] - mu) * inv + beta[d0 + i];
 }
@@ -301,7 +301,8 @@ template <typename T, int DH, bool PREMAP>
 __global__ __launch_bounds__(256) void chunk_exp_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                         const float* __restrict__ gamma_k,
                                                         const float* __restrict__ beta_k, float ln_eps,
-                                                        int2* __restrict__ kvexp, int Hkv, int N, int nchunks) {
+                                                        PremapNorm pn, int2* __restrict__ kvexp, int Hkv, int N,
+                                                        int nchunks) {
   constexpr int QD = DH / 4, QV = DV / 4;
   __shared__ float wm[2][4];
   const int c = blockIdx.x, bh = blockIdx.y;
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(256) void chunk_exp_kernel(const T* __restrict__ k,
     load_vals<QV>(v + ((long)bh * N + row) * DV + sq * QV, vx);
   }
   if (PREMAP) {
-    premap4<DH, QD>(kx, sq * QD, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
+    premap4<DH, QD>(kx, sq * QD, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps, pn);
     if (!valid)
 #pragma unroll
       for (int i = 0; i < QD; ++i) kx[i] = 0.f;
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(256) void chunk_exp_kernel(const T* __restrict__ k,
 template <typename T, int DH, bool PREMAP, int NCW>
 __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gamma_k,
-    const float* __restrict__ beta_k, float ln_eps, const float* __restrict__ state_in,
+    const float* __restrict__ beta_k, float ln_eps, PremapNorm pn, const float* __restrict__ state_in,
     float* __restrict__ state_out, typename Cx<T>::E* __restrict__ snap, int* __restrict__ sexp,
     float* __restrict__ sconst, const int2* __restrict__ kvexp, int Hkv, int N, int nchunks) {
   typedef typename Cx<T>::E E;
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
         for (int e = 0; e < 8; ++e) s += x[e];
       }
       s += __shfl_xor(s, 32);
-      const float mu = s * (1.f / DH);
+      const float mu = s * pn.mean_w;
       float q2 = 0.f;
 #pragma unroll
       for (int i = 0; i < KUL; ++i) {
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
       }
       q2 += __shfl_xor(q2, 32);
       r.mu = mu;
-      r.inv = valid ? 1.f / sqrtf(q2 * (1.f / DH) + ln_eps) : 0.f;
+      r.inv = valid ? 1.f / sqrtf(q2 * pn.var_w + ln_eps) : 0.f;
     }
     float m = 0.f;
 #pragma unroll
@@ -839,7 +840,7 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ ca, const float* __restrict__ cb, const float* __restrict__ cc, int G,
     const float* __restrict__ gamma_q, const float* __restrict__ beta_q, const float* __restrict__ gamma_k,
-    const float* __restrict__ beta_k, float ln_eps, const int32_t* __restrict__ group_of_dim,
+    const float* __restrict__ beta_k, float ln_eps, PremapNorm pn, const int32_t* __restrict__ group_of_dim,
     const typename Cx<T>::E* __restrict__ snap, const int* __restrict__ sexp, const float* __restrict__ sconst,
     int has_state_in, T* __restrict__ y, int Hq, int Hkv, int N, int nchunks, int RG) {
   typedef typename Cx<T>::E E;
@@ -1006,7 +1007,7 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
         for (int i = 0; i < 16; ++i) vTi[(sq * 16 + i) * VP + srow] = T(0);
       }
       if (PREMAP) {
-        premap4<DH, QD>(kx, sq * QD, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps);
+        premap4<DH, QD>(kx, sq * QD, gamma_k + kvh * DH, beta_k + kvh * DH, ln_eps, pn);
         if (srow >= nvalid)
 #pragma unroll
           for (int i = 0; i < QD; ++i) kx[i] = 0.f;
@@ -1139,7 +1140,7 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
 #pragma unroll
         for (int i = 0; i < QD; ++i) qx[i] = 0.f;
       }
-      if (PREMAP) premap4<DH, QD>(qx, sq * QD, gamma_q + h * DH, beta_q + h * DH, ln_eps);
+      if (PREMAP) premap4<DH, QD>(qx, sq * QD, gamma_q + h * DH, beta_q + h * DH, ln_eps, pn);
       float mq = 0.f;
 #pragma unroll
       for (int i = 0; i < QD; ++i) mq = fmaxf(mq, fabsf(qx[i]));
@@ -1528,6 +1529,7 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
   const int BH = a.B * a.Hkv;
   constexpr int KB = n_kblocks(DH);
   const FwdWs<T, DH> w = fwd_ws<T, DH>(a.B, a.Hq, a.Hkv, a.N);
+  const PremapNorm pn = premap_norm(a.premap_kind, DH);
   unsigned char* ws = reinterpret_cast<unsigned char*>(a.workspace);
   E* snap = reinterpret_cast<E*>(ws);
   int* sexp = reinterpret_cast<int*>(ws + w.exp_off);
@@ -1542,10 +1544,10 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
       const dim3 egrid(nchunks, BH);
       if (a.premap)
         hipLaunchKernelGGL((chunk_exp_kernel<T, DH, true>), egrid, dim3(256), 0, stream, kk, vv, a.gamma_k, a.beta_k,
-                           a.ln_eps, kvexp, a.Hkv, a.N, nchunks);
+                           a.ln_eps, pn, kvexp, a.Hkv, a.N, nchunks);
       else
         hipLaunchKernelGGL((chunk_exp_kernel<T, DH, false>), egrid, dim3(256), 0, stream, kk, vv, nullptr, nullptr,
-                           0.f, kvexp, a.Hkv, a.N, nchunks);
+                           0.f, pn, kvexp, a.Hkv, a.N, nchunks);
       hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
     }
@@ -1556,7 +1558,7 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
     dim3 grid((KB + 1 + ncw - 1) / ncw, BH);  // K-blocks + the constant row
 #define OAL_SCAN(PM, NC)                                                                                       \
     hipLaunchKernelGGL((scan_kernel<T, DH, PM, NC>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv,            \
-                       PM ? a.gamma_k : nullptr, PM ? a.beta_k : nullptr, PM ? a.ln_eps : 0.f, a.state_in,     \
+                       PM ? a.gamma_k : nullptr, PM ? a.beta_k : nullptr, PM ? a.ln_eps : 0.f, pn, a.state_in, \
                        a.state_out, snap, sexp, sconst, kvexp, a.Hkv, a.N, nchunks)
     if (a.premap) {
       if (four) OAL_SCAN(true, 4);
@@ -1583,7 +1585,7 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);                  \
     if (e2 != hipSuccess) return e2;                                                                            \
     hipLaunchKernelGGL(fn, grid, dim3(64 * NWV), shm, stream, qq, kk, vv, a.ca, a.cb, a.cc, a.G, a.gamma_q,             \
-                       a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, a.group_of_dim, snap, sexp, sconst, has_in, yy, \
+                       a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, pn, a.group_of_dim, snap, sexp, sconst, has_in, yy, \
                        a.Hq, a.Hkv, a.N, nchunks, rg);                                                          \
   } while (0)
 #define OAL_OUT_NG(RM, PM)                 \

@@ -198,20 +198,21 @@ __device__ __forceinline__ float row_sum(float s) {
   return s;
 }
 
-// ReBased pre-map of a row split over TPR consecutive lanes (n values each).
+// Pre-map (normalisation of kind pn, then the affine) of a row split over
+// TPR consecutive lanes (n values each).
 template <int DH, int TPR, int n>
 __device__ __forceinline__ void premap_row(float (&x)[n], int d0, const float* __restrict__ gamma,
-                                           const float* __restrict__ beta, float eps, bool valid) {
+                                           const float* __restrict__ beta, float eps, PremapNorm pn, bool valid) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < n; ++i) s += x[i];
   s = row_sum<TPR>(s);
-  const float mu = s * (1.f / DH);
+  const float mu = s * pn.mean_w;
   float v2 = 0.f;
 #pragma unroll
   for (int i = 0; i < n; ++i) v2 += (x[i] - mu) * (x[i] - mu);
   v2 = row_sum<TPR>(v2);
-  const float inv = 1.f / sqrtf(v2 * (1.f / DH) + eps);
+  const float inv = 1.f / sqrtf(v2 * pn.var_w + eps);
 #pragma unroll
   for (int i = 0; i < n; ++i) x[i] = valid ? gamma[d0 + i] * (x[i] - mu) * inv + beta[d0 + i] : 0.f;
 }
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void small_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ group_of_dim, const float* __restrict__ ca, const float* __restrict__ cb,
     const float* __restrict__ cc, int G, const float* __restrict__ gamma_q, const float* __restrict__ beta_q,
-    const float* __restrict__ gamma_k, const float* __restrict__ beta_k, float ln_eps,
+    const float* __restrict__ gamma_k, const float* __restrict__ beta_k, float ln_eps, PremapNorm pn,
     const float* __restrict__ state_in, float* __restrict__ state_out, float* __restrict__ segsum,
     T* __restrict__ y, int Hq, int Hkv, int N, int seg_chunks) {
   typedef SmallLds<T, DH, DIAG> L;
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void small_fwd_kernel(
       float kx[QD];
 #pragma unroll
       for (int i = 0; i < QD; ++i) kx[i] = cur.k.get(i, cur.ok);
-      if (PREMAP) premap_row<DH, TPR, QD>(kx, kvh * DH + sq * QD, gamma_k, beta_k, ln_eps, okrow);
+      if (PREMAP) premap_row<DH, TPR, QD>(kx, kvh * DH + sq * QD, gamma_k, beta_k, ln_eps, pn, okrow);
       feats(kx, OUT ? kf : nullptr, kft, nullptr);  // kernel 1 needs only the transposed tile
       if (sq == 0) {
         const E one = to_e(okrow ? 1.f : 0.f, E());
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(256, 2) void small_fwd_kernel(
 #pragma unroll
             for (int i = 0; i < QD; ++i) qx[i] = qr.get(i, okrow);
           }
-          if (PREMAP) premap_row<DH, TPR, QD>(qx, h * DH + sq * QD, gamma_q, beta_q, ln_eps, okrow);
+          if (PREMAP) premap_row<DH, TPR, QD>(qx, h * DH + sq * QD, gamma_q, beta_q, ln_eps, pn, okrow);
           feats(qx, qf, nullptr, coefq[hh]);
           if (sq == 0) qf[srow * FPP + SP::CF] = to_e(okrow ? coefq[hh][SP::CF] : 0.f, E());
         }
@@ -644,6 +645,7 @@ static hipError_t launch_small_t(const FwdLaunch& a, size_t workspace_bytes, hip
   const T* vv = reinterpret_cast<const T*>(a.v);
   T* yy = reinterpret_cast<T*>(a.y);
   float* segsum = reinterpret_cast<float*>(a.workspace);
+  const PremapNorm pn = premap_norm(a.premap_kind, DH);
 #define OAL_SMALL(PM)                                                                                         \
   do {                                                                                                        \
     auto f1 = small_fwd_kernel<T, DH, DIAG, PM, false>;                                                       \
@@ -656,10 +658,10 @@ static hipError_t launch_small_t(const FwdLaunch& a, size_t workspace_bytes, hip
     if (e != hipSuccess) return e;                                                                            \
     if (nseg_used > 1)                                                                                        \
       hipLaunchKernelGGL(f1, dim3(nseg_used - 1, BH), dim3(256), shm, stream, qq, kk, vv, a.group_of_dim,     \
-                         a.ca, a.cb, a.cc, a.G, a.gamma_q, a.beta_q, a.gamma_k, a.beta_k, a.ln_eps,           \
+                         a.ca, a.cb, a.cc, a.G, a.gamma_q, a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, pn,       \
                          a.state_in, a.state_out, segsum, yy, a.Hq, a.Hkv, a.N, seg_chunks);                  \
     hipLaunchKernelGGL(f2, dim3(nseg_used, BH), dim3(256), shm, stream, qq, kk, vv, a.group_of_dim, a.ca,     \
-                       a.cb, a.cc, a.G, a.gamma_q, a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, a.state_in,       \
+                       a.cb, a.cc, a.G, a.gamma_q, a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, pn, a.state_in,   \
                        a.state_out, segsum, yy, a.Hq, a.Hkv, a.N, seg_chunks);                                \
   } while (0)
   if (a.premap) OAL_SMALL(true);

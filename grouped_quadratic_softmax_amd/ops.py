@@ -80,18 +80,25 @@ class Coeffs:
                            self.c.data_ptr(), 1 if self.diagonal else 0)
 
 
-class Prep:
-    """ReBased pre-map parameters (device float32)."""
+_PREMAP_KINDS = {"layernorm": 0, "l2": 1}
 
-    def __init__(self, gamma_q, beta_q, gamma_k, beta_k, ln_eps=1e-5, device="cuda"):
+
+class Prep:
+    """Pre-map parameters (device float32): gamma * norm(x) + beta on q and k,
+    norm = LayerNorm (kind "layernorm", the ReBased map) or the unit l2 norm
+    (kind "l2", the TaylorShift-style map)."""
+
+    def __init__(self, gamma_q, beta_q, gamma_k, beta_k, ln_eps=1e-5, device="cuda", kind="layernorm"):
+        _need(kind in _PREMAP_KINDS, f"pre-map kind must be one of {sorted(_PREMAP_KINDS)}")
         conv = lambda x: torch.as_tensor(np.asarray(x, dtype=np.float32)).contiguous().to(device)
         self.gamma_q, self.beta_q = conv(gamma_q), conv(beta_q)
         self.gamma_k, self.beta_k = conv(gamma_k), conv(beta_k)
         self.ln_eps = float(ln_eps)
+        self.kind = kind
 
     def struct(self):
         return L.OalPrep(self.gamma_q.data_ptr(), self.beta_q.data_ptr(), self.gamma_k.data_ptr(),
-                         self.beta_k.data_ptr(), self.ln_eps)
+                         self.beta_k.data_ptr(), self.ln_eps, _PREMAP_KINDS[self.kind])
 
 
 def coeffs_from_factor(eps: float, Lf) -> tuple:

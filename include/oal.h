@@ -109,17 +109,28 @@ typedef struct oal_coeffs {
   int32_t diagonal;            /* 0: grouped kernel; nonzero: dimension-wise form */
 } oal_coeffs;
 
-/* Optional ReBased pre-map x -> gamma * LayerNorm(x) + beta applied to q
- * and k before the kernel ("Linear Transformers with Learnable Kernel
- * Functions", section on letting training place the parabola).  LayerNorm
- * uses the mean and biased variance over d_h and no affine of its own.
- * Device pointers; pass NULL for the whole struct to disable. */
+/* Optional pre-map x -> gamma * norm(x) + beta applied to q and k before
+ * the kernel, per head over d_h.  norm is chosen by `kind`:
+ *  OAL_PREMAP_LAYERNORM (0): LayerNorm with the mean and biased variance and
+ *    no affine of its own, eps added to the variance -- the ReBased map
+ *    ("Linear Transformers with Learnable Kernel Functions", section on
+ *    letting training place the parabola);
+ *  OAL_PREMAP_L2 (1): x / sqrt(sum_r x_r^2 + eps), the unit vector -- the
+ *    TaylorShift-style map ("Not All Dimensions Are Equal...", App. F.1,
+ *    the TaylorShift baseline: with gamma = tau sqrt(d_h) on queries,
+ *    gamma = 1 on keys, beta = 0 and a = 1, b = 1, c = 1/2 the kernel is
+ *    1 + s + s^2/2 of s = tau qhat . khat).
+ * Device pointers; pass NULL for the whole struct to disable.  Any other
+ * kind: OAL_ERR_INVALID_ARG. */
+#define OAL_PREMAP_LAYERNORM 0
+#define OAL_PREMAP_L2 1
 typedef struct oal_prep {
   const float* gamma_q; /* [Hq, d_h] */
   const float* beta_q;  /* [Hq, d_h] */
   const float* gamma_k; /* [Hkv, d_h] */
   const float* beta_k;  /* [Hkv, d_h] */
-  float ln_eps;         /* added to the variance, e.g. 1e-5 */
+  float ln_eps;         /* added inside the root, e.g. 1e-5 */
+  int32_t kind;         /* OAL_PREMAP_LAYERNORM or OAL_PREMAP_L2 */
 } oal_prep;
 
 /* Library version string. */

@@ -72,13 +72,34 @@ def gpu_prep(wl):
     if wl.premap is None:
         return None
     p = wl.premap
-    return oal.Prep(p["gamma_q"], p["beta_q"], p["gamma_k"], p["beta_k"], p["ln_eps"])
+    return oal.Prep(p["gamma_q"], p["beta_q"], p["gamma_k"], p["beta_k"], p["ln_eps"], kind=p.get("kind", "layernorm"))
 
 
 def oracle_prep(wl):
     if wl.premap is None:
         return None
-    return {k: (np.asarray(v, np.float64) if not isinstance(v, float) else v) for k, v in wl.premap.items()}
+    return {k: (np.asarray(v, np.float64) if not isinstance(v, (float, str)) else v) for k, v in wl.premap.items()}
+
+
+def with_l2_premap(wl, seed, tau=None):
+    """Give workload wl the TaylorShift-style pre-map (unit l2 norm, then the
+    affine).  tau given: that baseline's parameters, gamma_q = tau sqrt(d_h),
+    gamma_k = 1, beta = 0 (tau per query head); else seeded gamma ~ 1 +
+    N(0, 0.1^2) and beta ~ N(0, 0.1^2) per head and dimension."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, d = wl.n_q_heads, wl.n_kv_heads, wl.d_h
+    if tau is not None:
+        tq = np.broadcast_to(np.asarray(tau, np.float64), (Hq,))
+        p = {"gamma_q": np.repeat((tq * np.sqrt(d))[:, None], d, 1), "beta_q": np.zeros((Hq, d)),
+             "gamma_k": np.ones((Hkv, d)), "beta_k": np.zeros((Hkv, d))}
+    else:
+        p = {"gamma_q": 1 + 0.1 * rng.standard_normal((Hq, d)), "beta_q": 0.1 * rng.standard_normal((Hq, d)),
+             "gamma_k": 1 + 0.1 * rng.standard_normal((Hkv, d)), "beta_k": 0.1 * rng.standard_normal((Hkv, d))}
+    p = {k: v.astype(np.float32).astype(np.float64) for k, v in p.items()}
+    p["ln_eps"] = 1e-6
+    p["kind"] = "l2"
+    wl.premap = p
+    return wl
 
 
 def rel_err(y, ref):

@@ -6,7 +6,7 @@ import pytest
 import oracle as O
 import synthetic as S
 from helpers import (TOL, diag_form_mask, gpu_coeffs, gpu_prep, log, oracle_coeffs, oracle_prep, rel_err,
-                     require_gpu, to_dev, to_np)
+                     require_gpu, to_dev, to_np, with_l2_premap)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,6 +81,11 @@ def test_decode_d16_taylor():
 @pytest.mark.parametrize("reading", ["d", "e"])
 def test_decode_rebased_premap(reading):
     wl = S.make(4, batch=3, n_q_heads=2, n_kv_heads=2, seq_len=25, rebased_reading=reading)
+    _decode_case(wl, np.array([3, 10, 24]))
+
+
+def test_decode_taylorshift_premap():
+    wl = with_l2_premap(S.make(2, batch=3, n_q_heads=4, n_kv_heads=2, seq_len=25), seed=56)
     _decode_case(wl, np.array([3, 10, 24]))
 
 

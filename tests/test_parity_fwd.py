@@ -11,7 +11,7 @@ import pytest
 import oracle as O
 import synthetic as S
 from helpers import (TOL, diag_form_mask, gpu_coeffs, gpu_prep, log, oracle_coeffs, oracle_prep, rel_err,
-                     require_gpu, sample_rows, to_dev, to_np)
+                     require_gpu, sample_rows, to_dev, to_np, with_l2_premap)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,6 +205,32 @@ def test_dimensionwise_form_rejects_two_stage_calls():
         plan.outputs()
     assert info.value.status == -2  # OAL_ERR_UNSUPPORTED
     plan.run()  # one oal_fwd call
+
+
+def test_taylorshift_premap_gqa_bf16():
+    """The unit-l2-norm pre-map with per-dimension gamma and beta on the
+    chunk path (grouped-query heads, d_h = 64, four groups)."""
+    _run_case(with_l2_premap(S.make(2, batch=2, seq_len=150), seed=51))
+
+
+def test_taylorshift_premap_fp32():
+    _run_case(with_l2_premap(S.make(2, batch=1, seq_len=130, dtype="f32"), seed=52))
+
+
+def test_taylorshift_based_d16():
+    """The TaylorShift baseline itself ([OAL] App. F.1): unit vectors, s = tau
+    qhat.khat with a temperature per head, kernel 1 + s + s^2/2 (the Based
+    coefficients), here at d_h = 16 (the pre-map takes the CTA build)."""
+    wl = S.make(3, batch=2, n_q_heads=4, n_kv_heads=4, seq_len=333)
+    _run_case(with_l2_premap(wl, seed=53, tau=[0.5, 1.0, 1.7, 3.0]))
+
+
+def test_taylorshift_premap_dimensionwise():
+    """The unit-l2-norm pre-map on the dimension-wise form: heads with their
+    own keys (the one-launch kernel, two chained groups) and grouped-query
+    heads (the small-space kernel)."""
+    _run_case(with_l2_premap(S.make(4, batch=2, n_q_heads=3, n_kv_heads=3, seq_len=777), seed=54))
+    _run_case(with_l2_premap(S.make(4, batch=1, n_q_heads=4, n_kv_heads=2, seq_len=150), seed=55))
 
 
 def test_c4_rebased_squared_dot_premap():
