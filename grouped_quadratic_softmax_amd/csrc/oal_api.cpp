@@ -130,7 +130,7 @@ size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeff
   if (coeffs == nullptr || check_dims(dims, true) != OAL_OK) return 0;
   const bool diagonal = coeffs->diagonal != 0;
   if (oal::onepass16_supported(dims->d_h, dims->dtype, diagonal, dims->n_groups, dims->n_q_heads,
-                               dims->n_kv_heads))
+                               dims->n_kv_heads, false))
     return oal::onepass16_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->seq_len);
   if (!oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads))
     return diagonal ? 0 : oal_fwd_workspace_bytes(dims);
@@ -158,9 +158,9 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
     small = want_states && oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads);
     // one-call prefill at d_h = 16 with the state on chip
     onepass = want_states && oal::onepass16_supported(dims->d_h, dims->dtype, diagonal, dims->n_groups,
-                                                      dims->n_q_heads, dims->n_kv_heads);
+                                                      dims->n_q_heads, dims->n_kv_heads, prep != nullptr);
     if (diagonal && !small) return OAL_ERR_UNSUPPORTED;  // no separate stages for this form
-    if (!small && dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
+    if (!small && !onepass && dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
   }
   if ((st = check_prep(prep)) != OAL_OK) return st;
   if (dims->batch == 0) return OAL_OK;

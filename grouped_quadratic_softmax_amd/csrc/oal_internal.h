@@ -64,8 +64,10 @@ size_t small_workspace_bytes_for(int B, int Hq, int Hkv, int N, int d_h, bool di
 hipError_t launch_fwd_small(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 // One-pass prefill at d_h = 16 with bf16 activations: the state stays in MFMA
 // accumulators; sequences are cut into segments whose starting states come
-// from block sums in the workspace (one segment without a workspace).
-bool onepass16_supported(int d_h, int dtype, bool diagonal, int G, int Hq, int Hkv);
+// from block sums in the workspace (one segment without a workspace).  Up
+// to eight groups, or up to d_h groups for heads with their own keys and no
+// pre-map.
+bool onepass16_supported(int d_h, int dtype, bool diagonal, int G, int Hq, int Hkv, bool premap);
 size_t onepass16_workspace_bytes(int B, int Hq, int Hkv, int N);
 hipError_t launch_onepass16(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 // dimension-wise form at d_h = 64, bf16, heads with their own keys: one wave

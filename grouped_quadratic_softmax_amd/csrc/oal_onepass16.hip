@@ -640,8 +640,11 @@ Plan16 plan16(int BH, int nchunks, size_t workspace_bytes) {
 
 }  // namespace
 
-bool onepass16_supported(int d_h, int dtype, bool diagonal, int G, int Hq, int Hkv) {
-  return d_h == 16 && dtype == 1 && !diagonal && G >= 1 && G <= 8 && Hq / Hkv <= RMAX;
+// Up to eight groups in either build; more (up to one per dimension, the
+// dimension-aware kernel with any symmetric c) in the one-wave build only.
+bool onepass16_supported(int d_h, int dtype, bool diagonal, int G, int Hq, int Hkv, bool premap) {
+  if (d_h != 16 || dtype != 1 || diagonal || G < 1 || Hq / Hkv > RMAX) return false;
+  return G <= 8 || (G <= DH && onepass16w_supported(Hq, Hkv, premap));
 }
 
 // The workspace that lets either build run at full parallelism (the

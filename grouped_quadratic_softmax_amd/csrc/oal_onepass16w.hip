@@ -469,38 +469,41 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
       auto tile = [&](auto TC) __attribute__((always_inline)) {
         constexpr int T = decltype(TC)::value;
         if (16 * T >= nvalid) return;
-        // query row 16 T + l, dims rotated by 4 lg
+        // row 16 t + l of a tile (q or k), dims rotated by 4 lg, and the
+        // monomials of its features in K-block kb, rows 4 lg + j % 4 of tiles
+        // 2 kb + j / 4 (tile 8: pair (l, l + 8) in rows l < 8 (lane rows 0,
+        // 1), linear term above; tile 9: linear term in rows l < 8, the
+        // constant and zero rows above)
+        auto load_row = [&](const uint16_t* tile, int t, float (&R)[16], uint2 (&w)[4]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            w[i] = lds_u2(&tile[(16 * t + l) * DH + 4 * ((lg + i) & 3)]);
+            float x[4];
+            unpack4(w[i], x);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) R[4 * i + jj] = x[jj];
+          }
+        };
+        auto monomials = [&](const float (&R)[16], int kb, float (&f)[8]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int m = 2 * kb + j / 4, jj = j % 4;
+            const float p8 = lg < 2 ? R[jj + 8] : 1.f, b9 = lg < 2 ? R[jj] : 1.f;
+            if (m < 8) f[j] = R[jj] * R[(jj - m + 16) & 15];
+            else if (m == 8) f[j] = R[jj] * p8;
+            else f[j] = b9;
+          }
+        };
         uint2 qw[4];
         float Qr[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qw[i] = lds_u2(&sh.q[(16 * T + l) * DH + 4 * ((lg + i) & 3)]);
-          float x[4];
-          unpack4(qw[i], x);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) Qr[4 * i + jj] = x[jj];
-        }
-        // tile 8: pair (l, l + 8) in rows l < 8 (lane rows 0, 1), linear term
-        // above; tile 9: linear term in rows l < 8, the constant and zeros above
-        float p8[4], b9[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          p8[jj] = lg < 2 ? Qr[jj + 8] : 1.f;
-          b9[jj] = lg < 2 ? Qr[jj] : 1.f;
-        }
+        load_row(sh.q, T, Qr, qw);
         f32x4 Y[4], Dn = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int n = 0; n < 4; ++n) Y[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           float f[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int m = 2 * kb + j / 4, jj = j % 4;
-            if (m < 8) f[j] = Qr[jj] * Qr[(jj - m + 16) & 15];
-            else if (m == 8) f[j] = Qr[jj] * p8[jj];
-            else f[j] = b9[jj];
-          }
+          monomials(Qr, kb, f);
           const bf16x8 Bq = frag8(f);
 #pragma unroll
           for (int n = 0; n < 4; ++n) Y[n] = mma32(As[kb][n], Bq, Y[n]);
@@ -510,13 +513,38 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
         const bf16x4s Bqs = __builtin_bit_cast(bf16x4s, qw[0]);  // dims 4 lg .. 4 lg + 3 of the query
         float pk[T + 1][4];
 #pragma unroll
-        for (int kt = 0; kt <= T; ++kt) {
-          const uint2 kw = lds_u2(&sh.k[(16 * kt + l) * DH + 4 * lg]);
-          f32x4 sg[NG];
+        for (int kt = 0; kt <= T && NG > 8; ++kt) {
+          // more than eight groups (up to one per dimension, with any
+          // symmetric c): kappa = sum_f coef_f phi_f(k) phi_f(q) over the
+          // packed features, coefficient-weighted key features against the
+          // query features, five K-blocks on MFMA
+          float Kr[16];
+          uint2 kw4[4];
+          load_row(sh.k, kt, Kr, kw4);
+          f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int g = 0; g < NG; ++g) {
+          for (int kb = 0; kb < NKB; ++kb) {
+            const float4 c0 = lds_f4(&tb.coefq[32 * kb + 4 * lg]), c1 = lds_f4(&tb.coefq[32 * kb + 16 + 4 * lg]);
+            const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            float fk[8], fq[8];
+            monomials(Kr, kb, fk);
+            monomials(Qr, kb, fq);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) fk[j] *= cf[j];
+            sc = mma32(frag8(fk), frag8(fq), sc);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[kt][e] = (kt < T || 4 * lg + e <= l) ? sc[e] : 0.f;  // causal mask
+        }
+#pragma unroll
+        for (int kt = 0; kt <= T && NG <= 8; ++kt) {
+          const uint2 kw = lds_u2(&sh.k[(16 * kt + l) * DH + 4 * lg]);
+          constexpr int NGG = NG <= 8 ? NG : 1;
+          f32x4 sg[NGG];
+#pragma unroll
+          for (int g = 0; g < NGG; ++g) {
             uint2 km = kw;
-            if (NG > 1) {
+            if (NGG > 1) {
               const uint2 mk = tb.gmask[g][lg];
               km = make_uint2(kw.x & mk.x, kw.y & mk.y);
             }
@@ -527,10 +555,10 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
             // kappa = a + sum_g s_g (b_g + sum_{h >= g} c'_gh s_h), c'_gh = 2 sym(c)_gh off the diagonal
             float kap = tb.poly[0];
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
+            for (int g = 0; g < NGG; ++g) {
               float inner = tb.poly[1 + g];
 #pragma unroll
-              for (int h2 = g; h2 < NG; ++h2) inner += (h2 == g ? 1.f : 2.f) * tb.poly[9 + 8 * g + h2] * sg[h2][e];
+              for (int h2 = g; h2 < NGG; ++h2) inner += (h2 == g ? 1.f : 2.f) * tb.poly[9 + 8 * g + h2] * sg[h2][e];
               kap += sg[g][e] * inner;
             }
             if (kt == T) kap = 4 * lg + e <= l ? kap : 0.f;  // causal mask inside the diagonal tile
@@ -679,7 +707,7 @@ hipError_t launch_onepass16w(const FwdLaunch& a, size_t workspace_bytes, hipStre
     p.pub = reinterpret_cast<float4*>(reinterpret_cast<char*>(a.workspace) + ctl_bytes_w(BH));
     p.tag = chained_launch_tag();
   }
-  const int NG = a.G <= 1 ? 1 : a.G <= 2 ? 2 : a.G <= 4 ? 4 : 8;
+  const int NG = a.G <= 1 ? 1 : a.G <= 2 ? 2 : a.G <= 4 ? 4 : a.G <= 8 ? 8 : 16;
   const long per_slot = (long)BH * kQuads * kWave;  // float4 per slot of segment sums
 #define OAL_OP16W(G_)                                                                                  \
   do {                                                                                                 \
@@ -698,7 +726,8 @@ hipError_t launch_onepass16w(const FwdLaunch& a, size_t workspace_bytes, hipStre
     case 1: OAL_OP16W(1); break;
     case 2: OAL_OP16W(2); break;
     case 4: OAL_OP16W(4); break;
-    default: OAL_OP16W(8); break;
+    case 8: OAL_OP16W(8); break;
+    default: OAL_OP16W(16); break;
   }
 #undef OAL_OP16W
   return hipGetLastError();

@@ -136,6 +136,10 @@ def test_fwd_validation_errors(L, no_device):
     assert _fwd(L, _dims(L, G=0)) == E
     assert _fwd(L, _dims(L, G=65)) == E
     assert _fwd(L, _dims(L, G=9)) == U
+    # more than eight groups: only the one-wave d_h = 16 build (heads with
+    # their own keys, bf16, no pre-map) takes them
+    assert _fwd(L, _dims(L, d=16, Hq=4, Hkv=2, G=9)) == U
+    assert _fwd(L, _dims(L, d=16, G=9, dt=0)) == U
     assert _fwd(L, _dims(L), coeffs=False) == E
     assert _fwd(L, _dims(L), q=None) == E
     assert _fwd(L, _dims(L), y=None) == E

@@ -89,6 +89,17 @@ def test_decode_taylorshift_premap():
     _decode_case(wl, np.array([3, 10, 24]))
 
 
+def test_decode_dimension_aware_general_c():
+    """d_h = 16, one group per dimension with a general symmetric C."""
+    rng = np.random.default_rng(1616)
+    wl = S.make(3, batch=3, n_q_heads=2, n_kv_heads=2, seq_len=30)
+    groups = np.stack([rng.permutation(16) for _ in range(2)]).astype(np.int32)
+    a, b, c = O.coeffs_from_factor(1e-3, rng.standard_normal((2, 17, 17)) * 0.5)
+    wl.coeff = {"kind": "abc", "a": a, "b": b, "c": c}
+    wl.n_groups = 16
+    _decode_case(wl, np.array([0, 11, 29]), groups=groups)
+
+
 def test_decode_eight_groups():
     wl = S.make(5, n_q_heads=4, n_kv_heads=4, seq_len=33, batch=3)
     groups = np.stack([np.arange(64) % 8 for _ in range(4)]).astype(np.int32)

@@ -450,6 +450,36 @@ def test_d16_workspace_sizes_stages_and_state(dtype, heads):
                 assert (np.abs(to_np(got)[bi, kh] - ref_s) <= bound).all(), (bi, kh)
 
 
+@pytest.mark.parametrize("G,N", [(16, 777), (16, 64), (12, 130), (9, 1500)])
+def test_d16_dimension_aware_general_c(G, N):
+    """The dimension-aware kernel with a general symmetric C ([Slides]
+    "Relax sharing ...", Eq. (3): b_r and C_rt per dimension), here G = 16 =
+    d_h singleton groups in a random order, and 9-12 uneven groups: more
+    than eight groups take the within-chunk scores in the packed feature
+    space (the one-wave build, heads with their own keys).  C = M[1:, 1:] of
+    a PSD M = L L^T ([OAL] Eq. (7)), so every weight is positive."""
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    rng = np.random.default_rng(1600 + G + N)
+    wl = S.make(3, batch=2, n_q_heads=3, n_kv_heads=3, seq_len=N)
+    groups = np.stack([rng.permutation(np.arange(16) % G) for _ in range(3)]).astype(np.int32)
+    a, b, c = O.coeffs_from_factor(1e-3, rng.standard_normal((3, G + 1, G + 1)) * 0.5)
+    co = oal.Coeffs(groups, a.astype(np.float32), b.astype(np.float32), c.astype(np.float32))
+    q, k, v = to_dev(wl.q, "bf16"), to_dev(wl.k, "bf16"), to_dev(wl.v, "bf16")
+    y, st = oal.fwd(q, k, v, co, return_state=True)
+    ref = O.attention_direct(wl.q, wl.k, wl.v, groups, a, b, c)
+    err = rel_err(to_np(y), ref)
+    log(f"[fwd]   d16 dimension-aware G={G} N={N}: max rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    u = 2.0 ** -9
+    for bi in range(wl.batch):
+        for kh in range(wl.n_kv_heads):
+            ref_s = O.abi_state_from_matrix(O.state_from_prefix(wl.k[bi, kh], wl.v[bi, kh]))
+            absum = O.abi_state_from_matrix(O.state_from_prefix(np.abs(wl.k[bi, kh]), np.abs(wl.v[bi, kh])))
+            bound = (2 * u + N * 2.0 ** -24) * absum + 2.0 ** -24 * absum.max()
+            assert (np.abs(to_np(st)[bi, kh] - ref_s) <= bound).all(), (bi, kh)
+
+
 def test_d16_chained_back_to_back():
     """d_h = 16, a KV head per query head, two chained groups of segments:
     two calls with different inputs on one workspace, each against the
