@@ -59,6 +59,8 @@ _SIGS = {
     "oal_fwd_workspace_bytes": ([_P], ctypes.c_size_t),
     "oal_fwd_workspace_bytes_for": ([_P, _P], ctypes.c_size_t),
     "oal_fwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "oal_fwd_varlen_workspace_bytes_for": ([_P, _P], ctypes.c_size_t),
+    "oal_fwd_varlen": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_fwd_states": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_fwd_outputs": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_decode_workspace_bytes": ([_P], ctypes.c_size_t),

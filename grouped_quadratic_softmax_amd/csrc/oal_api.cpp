@@ -55,6 +55,23 @@ int check_prep(const oal_prep* p) {
   return OAL_OK;
 }
 
+// Which prefill build serves a call: the one-call small-space path (the
+// dimension-wise form), the one-call path at d_h = 16, or the chunk path.
+// Calls with per-sequence lengths take the one-launch builds only (heads
+// with their own keys), else the chunk path.
+struct FwdPath {
+  bool small = false, onepass = false;
+};
+FwdPath fwd_path(const oal_dims* dims, bool diagonal, bool premap, bool varlen) {
+  FwdPath p;
+  const int d = dims->d_h, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads;
+  p.small = oal::small_path_supported(d, diagonal, Hq, Hkv) &&
+            (!varlen || oal::dimw_supported(d, dims->dtype, diagonal, Hq, Hkv));
+  p.onepass = oal::onepass16_supported(d, dims->dtype, diagonal, dims->n_groups, Hq, Hkv, premap) &&
+              (!varlen || oal::onepass16w_supported(Hq, Hkv, premap));
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,17 +143,26 @@ size_t oal_fwd_workspace_bytes(const oal_dims* dims) {
                                  dims->dtype);
 }
 
-size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs) {
+namespace {
+size_t workspace_for_path(const oal_dims* dims, const oal_coeffs* coeffs, bool varlen) {
   if (coeffs == nullptr || check_dims(dims, true) != OAL_OK) return 0;
   const bool diagonal = coeffs->diagonal != 0;
-  if (oal::onepass16_supported(dims->d_h, dims->dtype, diagonal, dims->n_groups, dims->n_q_heads,
-                               dims->n_kv_heads, false))
+  const FwdPath path = fwd_path(dims, diagonal, false, varlen);
+  if (path.onepass)
     return oal::onepass16_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->seq_len);
-  if (!oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads))
+  if (!path.small)
     return diagonal ? 0 : oal_fwd_workspace_bytes(dims);
   return oal::small_workspace_bytes_for(dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->seq_len, dims->d_h,
-                                       diagonal,
-                                    dims->dtype);
+                                       diagonal, dims->dtype);
+}
+}  // namespace
+
+size_t oal_fwd_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs) {
+  return workspace_for_path(dims, coeffs, false);
+}
+
+size_t oal_fwd_varlen_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs) {
+  return workspace_for_path(dims, coeffs, true);
 }
 
 namespace {
@@ -145,7 +171,7 @@ namespace {
 // stages: bit 0 = chunk states, bit 1 = outputs.
 int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v, const oal_coeffs* coeffs,
                const oal_prep* prep, const float* state_in, float* state_out, void* y, void* workspace,
-               size_t workspace_bytes, void* stream, int stages) {
+               size_t workspace_bytes, void* stream, int stages, const int32_t* seq_lens = nullptr) {
   const bool want_states = stages & 1, want_out = stages & 2;
   int st = check_dims(dims, true);
   if (st != OAL_OK) return st;
@@ -154,11 +180,9 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
     if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
     if ((st = check_coeff_ptrs(coeffs)) != OAL_OK) return st;
     diagonal = coeffs->diagonal != 0;
-    // one-call prefill of a small feature space (the dimension-wise form)
-    small = want_states && oal::small_path_supported(dims->d_h, diagonal, dims->n_q_heads, dims->n_kv_heads);
-    // one-call prefill at d_h = 16 with the state on chip
-    onepass = want_states && oal::onepass16_supported(dims->d_h, dims->dtype, diagonal, dims->n_groups,
-                                                      dims->n_q_heads, dims->n_kv_heads, prep != nullptr);
+    const FwdPath path = fwd_path(dims, diagonal, prep != nullptr, seq_lens != nullptr);
+    small = want_states && path.small;
+    onepass = want_states && path.onepass;
     if (diagonal && !small) return OAL_ERR_UNSUPPORTED;  // no separate stages for this form
     if (!small && !onepass && dims->n_groups > 8) return OAL_ERR_UNSUPPORTED;
   }
@@ -197,6 +221,7 @@ int fwd_stages(const oal_dims* dims, const void* q, const void* k, const void* v
   }
   a.state_in = state_in; a.state_out = state_out; a.y = y; a.workspace = workspace;
   a.diagonal = diagonal;
+  a.seq_lens = seq_lens;
   if (onepass)
     return oal::launch_onepass16(a, workspace ? workspace_bytes : 0, (hipStream_t)stream) == hipSuccess
                ? OAL_OK
@@ -214,6 +239,14 @@ int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v, c
             const oal_prep* prep, const float* state_in, float* state_out, void* y, void* workspace,
             size_t workspace_bytes, void* stream) {
   return fwd_stages(dims, q, k, v, coeffs, prep, state_in, state_out, y, workspace, workspace_bytes, stream, 3);
+}
+
+int oal_fwd_varlen(const oal_dims* dims, const int32_t* seq_lens, const void* q, const void* k, const void* v,
+                   const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, float* state_out,
+                   void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (seq_lens == nullptr) return OAL_ERR_INVALID_ARG;
+  return fwd_stages(dims, q, k, v, coeffs, prep, state_in, state_out, y, workspace, workspace_bytes, stream, 3,
+                    seq_lens);
 }
 
 int oal_fwd_states(const oal_dims* dims, const void* k, const void* v, const oal_prep* prep,

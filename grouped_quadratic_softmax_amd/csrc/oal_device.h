@@ -135,6 +135,12 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 // sum / max over aligned groups of 4 lanes, in every lane of the group
+// Length of sequence b: its entry of seq_lens clamped to [0, N], or N
+// (padded layout: rows past a sequence's length are not part of it).
+__device__ __forceinline__ int seq_len_of(const int32_t* seq_lens, int b, int N) {
+  return seq_lens == nullptr ? N : min(max(seq_lens[b], 0), N);
+}
+
 // Normalisation of the pre-map gamma * norm(x) + beta over d_h:
 //   mu = mean_w * sum_r x_r,  norm(x) = (x - mu) / sqrt(var_w * sum_r (x_r - mu)^2 + eps)
 // LayerNorm (kind 0): mean_w = var_w = 1 / d_h; unit l2 norm (kind 1):

@@ -20,6 +20,7 @@ struct FwdLaunch {
   const float *gamma_q, *beta_q, *gamma_k, *beta_k;
   float ln_eps;
   int premap_kind = 0;  // OAL_PREMAP_LAYERNORM or OAL_PREMAP_L2
+  const int32_t* seq_lens = nullptr;  // [B] device lengths within the padded N (null: all N)
   const float* state_in;
   float* state_out;
   void* y;

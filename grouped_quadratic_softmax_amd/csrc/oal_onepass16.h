@@ -157,6 +157,7 @@ struct Args16 {
   float4* pub;      // [BH][quads x 64 lanes]: the first groups' totals
   uint64_t tag;     // unique to the launch
   int nwg, nseg, BH;
+  const int32_t* seq_lens;  // [B] lengths within the padded N (null: all N)
 };
 
 // Key features of tile M for the eight tokens t0 .. t0 + 7 whose k_l this

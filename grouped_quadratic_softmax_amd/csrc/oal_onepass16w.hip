@@ -120,12 +120,14 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
     bh = blockIdx.y;
   }
   const int BH = MODE == kChainedW ? p.BH : gridDim.y;
-  const int N = p.N;
+  const int N = seq_len_of(p.seq_lens, bh / p.Hkv, p.N);  // rows of this sequence (row stride p.N)
   const int nchunks = (N + CK - 1) / CK;
   const int c_begin = seg * p.seg_chunks, c_end = min(c_begin + p.seg_chunks, nchunks);
   const bool live = c_begin < c_end;          // empty segments past the end
-  const bool last = live && c_end == nchunks;  // the segment that ends the sequence
-  const long rowbase = (long)bh * N;  // rows of q, k, v and y of this (sequence, head)
+  // the segment that ends the sequence (of an empty sequence: segment 0,
+  // which then only writes the final state)
+  const bool last = nchunks == 0 ? seg == 0 : live && c_end == nchunks;
+  const long rowbase = (long)bh * p.N;  // rows of q, k, v and y of this (sequence, head)
   constexpr long SF = D16 * (DV + 1);
 
   // ---- per-head tables (outputs), spread over the workgroup's threads ----
@@ -699,7 +701,7 @@ hipError_t launch_onepass16w(const FwdLaunch& a, size_t workspace_bytes, hipStre
   p.state_in = a.state_in; p.state_out = a.state_out;
   p.blocksum = reinterpret_cast<float*>(a.workspace);
   p.y = reinterpret_cast<uint16_t*>(a.y);
-  p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;
+  p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N; p.seq_lens = a.seq_lens;
   p.seg_chunks = pl.seg_chunks; p.blk_chunks = pl.seg_chunks; p.nblk = pl.nseg - 1;
   p.nwg = pl.nwg; p.nseg = pl.nseg; p.BH = BH;
   if (pl.nwg > 1) {

@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void chunk_exp_kernel(const T* __restrict__ k,
                                                         const float* __restrict__ gamma_k,
                                                         const float* __restrict__ beta_k, float ln_eps,
                                                         PremapNorm pn, int2* __restrict__ kvexp, int Hkv, int N,
-                                                        int nchunks) {
+                                                        int nchunks, const int32_t* __restrict__ seq_lens) {
   constexpr int QD = DH / 4, QV = DV / 4;
   __shared__ float wm[2][4];
   const int c = blockIdx.x, bh = blockIdx.y;
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void chunk_exp_kernel(const T* __restrict__ k,
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int srow = tid / 4, sq = tid % 4;  // token of the chunk, quarter of its dimensions
   const int row = c * C + srow;
-  const bool valid = row < N;
+  const bool valid = row < seq_len_of(seq_lens, bh / Hkv, N);  // rows of the sequence (stride N)
   float kx[QD], vx[QV];
 #pragma unroll
   for (int i = 0; i < QD; ++i) kx[i] = 0.f;
@@ -350,7 +350,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ gamma_k,
     const float* __restrict__ beta_k, float ln_eps, PremapNorm pn, const float* __restrict__ state_in,
     float* __restrict__ state_out, typename Cx<T>::E* __restrict__ snap, int* __restrict__ sexp,
-    float* __restrict__ sconst, const int2* __restrict__ kvexp, int Hkv, int N, int nchunks) {
+    float* __restrict__ sconst, const int2* __restrict__ kvexp, int Hkv, int NS, int nchunks,
+    const int32_t* __restrict__ seq_lens) {
   typedef typename Cx<T>::E E;
   typedef typename Cx<T>::Frag F;
   constexpr int KB = n_kblocks(DH);
@@ -376,6 +377,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
 
   const int bh = blockIdx.y, BH = gridDim.y;
   const int kvh = bh % Hkv;
+  // rows of this sequence (its own length with seq_lens; the row stride is NS)
+  const int N = seq_len_of(seq_lens, bh / Hkv, NS);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int lg = lane / 16, l16 = lane % 16;
   const bool loader = wave >= kScanCompute;
@@ -427,8 +430,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     for (int n = 0; n < 5; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const long sbase = (long)bh * SF;
-  const T* kp = k + (long)bh * N * DH;
-  const T* vp = v + (long)bh * N * DV;
+  const T* kp = k + (long)bh * NS * DH;
+  const T* vp = v + (long)bh * NS * DV;
 
   // ---- loader helpers ----
   struct RawSet {
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
 #pragma unroll
       for (int i = 0; i < TPL; ++i) {
         const int row = c * C + TPL * tg + i;
-        const long rr = row < N ? row : N - 1;
+        const long rr = row < N ? row : max(N - 1, 0);
         if (ulive) {
           ld8(r.u[i], kload ? kp + rr * DH + 8 * lu : vp + rr * DV + 8 * lu);
         } else {
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
       return r;
     }
     const int row = c * C + ltok;
-    const long rr = row < N ? row : N - 1;
+    const long rr = row < N ? row : max(N - 1, 0);
 #pragma unroll
     for (int i = 0; i < UL; ++i) {
       const int unit = lhalf + 2 * i;
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void scan_kernel(
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kScanCompute; ++w) m_in = fmaxf(m_in, wm_in[w]);
-    beta = exp_above((float)N + m_in) - 15;
+    beta = exp_above((float)NS + m_in) - 15;
     const float sb = pow2(-beta);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -842,7 +845,8 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
     const float* __restrict__ gamma_q, const float* __restrict__ beta_q, const float* __restrict__ gamma_k,
     const float* __restrict__ beta_k, float ln_eps, PremapNorm pn, const int32_t* __restrict__ group_of_dim,
     const typename Cx<T>::E* __restrict__ snap, const int* __restrict__ sexp, const float* __restrict__ sconst,
-    int has_state_in, T* __restrict__ y, int Hq, int Hkv, int N, int nchunks, int RG) {
+    int has_state_in, T* __restrict__ y, int Hq, int Hkv, int NS, int nchunks, int RG,
+    const int32_t* __restrict__ seq_lens) {
   typedef typename Cx<T>::E E;
   typedef typename Cx<T>::Frag F;
   typedef Frag<IsBf16<T>::value> PF;  // P . V operands (bf16 or fp32)
@@ -879,6 +883,10 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
   const int c = blockIdx.x, bh = blockIdx.y, BH = gridDim.y;
   const int b = bh / Hkv, kvh = bh % Hkv;
   const int R = Hq / Hkv;
+  // rows of this sequence (its own length with seq_lens; the row stride is NS):
+  // chunks past its end have nothing to do
+  const int N = seq_len_of(seq_lens, b, NS);
+  if (c * C >= N) return;
   // Builds with eight head slots, and the eight-group builds with one slot
   // (held to two waves per SIMD) or four, run short of registers (measured
   // gains: one slot 899 -> 830 us on the 32k-token prefill, four slots
@@ -977,8 +985,8 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
   // ---- chunk-wide prologue: K (scores), V (P . V), snapshot scales ----
   {
     float kx[QD];
-    const T* kp = k + ((long)bh * N + j0) * DH;
-    const T* vp = v + ((long)bh * N + j0) * DV;
+    const T* kp = k + ((long)bh * NS + j0) * DH;
+    const T* vp = v + ((long)bh * NS + j0) * DV;
 #pragma unroll
     for (int i = 0; i < QD; ++i) kx[i] = 0.f;
     if (stager) {
@@ -1135,7 +1143,7 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
       const int h = kvh * R + h0 + (live ? it : 0);
       float qx[QD];
       if (live && srow < nvalid) {
-        load_vals<QD>(q + ((long)(b * Hq + h) * N + j0 + srow) * DH + sq * QD, qx);
+        load_vals<QD>(q + ((long)(b * Hq + h) * NS + j0 + srow) * DH + sq * QD, qx);
       } else {
 #pragma unroll
         for (int i = 0; i < QD; ++i) qx[i] = 0.f;
@@ -1468,7 +1476,7 @@ __global__ __launch_bounds__(64 * NW, (RMAX == 1 && IsBf16<T>::value) ? 2 : 1) v
       }
       {
         constexpr int VPR = DV * sizeof(T) / 16;  // 16-byte vectors per row
-        T* yp = y + ((long)(b * Hq + h) * N + j0 + 16 * rt) * DV;
+        T* yp = y + ((long)(b * Hq + h) * NS + j0 + 16 * rt) * DV;
 #pragma unroll
         for (int u = 0; u < 16 * VPR / 64; ++u) {
           const int vi = lane + 64 * u, r = vi / VPR, cv = vi % VPR;
@@ -1544,10 +1552,10 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
       const dim3 egrid(nchunks, BH);
       if (a.premap)
         hipLaunchKernelGGL((chunk_exp_kernel<T, DH, true>), egrid, dim3(256), 0, stream, kk, vv, a.gamma_k, a.beta_k,
-                           a.ln_eps, pn, kvexp, a.Hkv, a.N, nchunks);
+                           a.ln_eps, pn, kvexp, a.Hkv, a.N, nchunks, a.seq_lens);
       else
         hipLaunchKernelGGL((chunk_exp_kernel<T, DH, false>), egrid, dim3(256), 0, stream, kk, vv, nullptr, nullptr,
-                           0.f, pn, kvexp, a.Hkv, a.N, nchunks);
+                           0.f, pn, kvexp, a.Hkv, a.N, nchunks, a.seq_lens);
       hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
     }
@@ -1559,7 +1567,7 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
 #define OAL_SCAN(PM, NC)                                                                                       \
     hipLaunchKernelGGL((scan_kernel<T, DH, PM, NC>), grid, dim3(64 * kScanWaves), 0, stream, kk, vv,            \
                        PM ? a.gamma_k : nullptr, PM ? a.beta_k : nullptr, PM ? a.ln_eps : 0.f, pn, a.state_in, \
-                       a.state_out, snap, sexp, sconst, kvexp, a.Hkv, a.N, nchunks)
+                       a.state_out, snap, sexp, sconst, kvexp, a.Hkv, a.N, nchunks, a.seq_lens)
     if (a.premap) {
       if (four) OAL_SCAN(true, 4);
       else OAL_SCAN(true, 8);
@@ -1586,7 +1594,7 @@ hipError_t launch_fwd_t(const FwdLaunch& a, int stages, hipStream_t stream) {
     if (e2 != hipSuccess) return e2;                                                                            \
     hipLaunchKernelGGL(fn, grid, dim3(64 * NWV), shm, stream, qq, kk, vv, a.ca, a.cb, a.cc, a.G, a.gamma_q,             \
                        a.beta_q, a.gamma_k, a.beta_k, a.ln_eps, pn, a.group_of_dim, snap, sexp, sconst, has_in, yy, \
-                       a.Hq, a.Hkv, a.N, nchunks, rg);                                                          \
+                       a.Hq, a.Hkv, a.N, nchunks, rg, a.seq_lens);                                              \
   } while (0)
 #define OAL_OUT_NG(RM, PM)                 \
   do {                                     \

@@ -132,19 +132,22 @@ def fwd_workspace_bytes(B, Hq, Hkv, N, d_h, d_v, G, dtype) -> int:
     return int(L.lib().oal_fwd_workspace_bytes(ctypes.byref(dims)))
 
 
-def fwd_workspace_bytes_for(q, k, v, coeffs: Coeffs) -> int:
-    """Workspace oal_fwd uses at full parallelism for these tensors and
-    coefficients (oal_fwd_workspace_bytes_for)."""
+def fwd_workspace_bytes_for(q, k, v, coeffs: Coeffs, varlen=False) -> int:
+    """Workspace oal_fwd (varlen: oal_fwd_varlen) uses at full parallelism
+    for these tensors and coefficients."""
     B, Hq, N, d = q.shape
     dims = _dims(B, Hq, k.shape[1], N, d, v.shape[3], coeffs.n_groups, q.dtype)
     cs = coeffs.struct()
-    return int(L.lib().oal_fwd_workspace_bytes_for(ctypes.byref(dims), ctypes.byref(cs)))
+    fn = L.lib().oal_fwd_varlen_workspace_bytes_for if varlen else L.lib().oal_fwd_workspace_bytes_for
+    return int(fn(ctypes.byref(dims), ctypes.byref(cs)))
 
 
 def fwd(q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None, return_state=False,
-        y=None, state_out=None, workspace=None):
+        y=None, state_out=None, workspace=None, seq_lens=None):
     """Causal OAL prefill.  q [B, Hq, N, d], k [B, Hkv, N, d], v [B, Hkv, N, 64].
 
+    seq_lens: optional device int32 [B]; sequence b then uses its first
+    seq_lens[b] rows (oal_fwd_varlen: the other rows of y are not written).
     Returns y (and the final state [B, Hkv, state_floats] when return_state).
     """
     _dev(q, "q", ndim=4)
@@ -166,16 +169,23 @@ def fwd(q, k, v, coeffs: Coeffs, prep: Optional[Prep] = None, state_in=None, ret
     if return_state and state_out is None:
         state_out = torch.empty((B, Hkv, sf), dtype=torch.float32, device=q.device)
     cs = coeffs.struct()
+    if seq_lens is not None:
+        _dev(seq_lens, "seq_lens", torch.int32, 1)
+        _need(seq_lens.numel() == B, "seq_lens must hold one length per sequence")
     if workspace is None:  # a caller's workspace is passed as given
-        nbytes = int(L.lib().oal_fwd_workspace_bytes_for(ctypes.byref(dims), ctypes.byref(cs)))
+        size_fn = (L.lib().oal_fwd_varlen_workspace_bytes_for if seq_lens is not None
+                   else L.lib().oal_fwd_workspace_bytes_for)
+        nbytes = int(size_fn(ctypes.byref(dims), ctypes.byref(cs)))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     else:
         _dev(workspace, "workspace", torch.uint8)
     ps = prep.struct() if prep is not None else None
-    st = L.lib().oal_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
-                         ctypes.byref(ps) if ps is not None else None, _ptr(state_in), _ptr(state_out),
-                         _ptr(y), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
-    L.check(st, "oal_fwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs), ctypes.byref(ps) if ps is not None else None,
+            _ptr(state_in), _ptr(state_out), _ptr(y), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
+    if seq_lens is None:
+        L.check(L.lib().oal_fwd(ctypes.byref(dims), *args), "oal_fwd")
+    else:
+        L.check(L.lib().oal_fwd_varlen(ctypes.byref(dims), _ptr(seq_lens), *args), "oal_fwd_varlen")
     return (y, state_out) if return_state else y
 
 

@@ -199,6 +199,27 @@ int oal_fwd(const oal_dims* dims, const void* q, const void* k, const void* v,
             const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, float* state_out,
             void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Causal prefill of sequences of different lengths in the padded layout
+ * ("Not All Dimensions Are Equal...", sec. 3.1, Eq. (2): prompts of length
+ * N_p; here the prefill of such a batch): sequence b of q, k, v, y holds
+ * seq_lens[b] valid rows (device int32 [batch]; values are clamped to
+ * [0, seq_len]) at the start of its seq_len-row slot.
+ *   y:         rows below seq_lens[b] as oal_fwd would write them for a
+ *              sequence of that length; the other rows are not written.
+ *   state_out: the states after seq_lens[b] tokens (state_in, or zero, for
+ *              an empty sequence).
+ * Heads with their own keys take the one-launch builds (d_h = 16 bf16 and
+ * the dimension-wise form at d_h = 64 bf16); the other grouped forms take
+ * the chunk path, whose workspace is oal_fwd_workspace_bytes(dims); the
+ * dimension-wise form with grouped-query heads returns OAL_ERR_UNSUPPORTED.
+ * Workspace: oal_fwd_varlen_workspace_bytes_for(dims, coeffs).  Other
+ * arguments and errors as for oal_fwd; seq_lens == NULL:
+ * OAL_ERR_INVALID_ARG. */
+size_t oal_fwd_varlen_workspace_bytes_for(const oal_dims* dims, const oal_coeffs* coeffs);
+int oal_fwd_varlen(const oal_dims* dims, const int32_t* seq_lens, const void* q, const void* k, const void* v,
+                   const oal_coeffs* coeffs, const oal_prep* prep, const float* state_in, float* state_out,
+                   void* y, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The two stages of oal_fwd, for callers that schedule or time them
  * separately.  oal_fwd(...) is exactly oal_fwd_states(...) followed by
  * oal_fwd_outputs(...) on the same stream with the same workspace (the

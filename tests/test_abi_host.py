@@ -153,6 +153,12 @@ def test_fwd_validation_errors(L, no_device):
     assert _fwd(L, _dims(L), state_out=_mis(4)) == E
     bad_prep = L.OalPrep(0x1000, 0, 0x1000, 0x1000, 1e-5)
     assert _fwd(L, _dims(L), prep=bad_prep) == E
+    # per-sequence lengths: a null length array is refused before any launch
+    lib = L.lib()
+    cs = L.OalCoeffs(0x1000, 0x1000, 0x1000, 0x1000)
+    assert lib.oal_fwd_varlen(ctypes.byref(_dims(L)), None, FAKE, FAKE, FAKE, ctypes.byref(cs), None, None, None,
+                              FAKE, FAKE, ctypes.c_size_t(need), None) == E
+    assert lib.oal_fwd_varlen_workspace_bytes_for(ctypes.byref(_dims(L)), ctypes.byref(cs)) == need
     for kind in (-1, 2):  # pre-map kinds: 0 LayerNorm, 1 unit l2 norm
         assert _fwd(L, _dims(L), prep=L.OalPrep(0x1000, 0x1000, 0x1000, 0x1000, 1e-5, kind)) == E
     assert _fwd(L, _dims(L, B=0)) == L.OAL_OK                     # empty batch: nothing enqueued
