@@ -58,6 +58,7 @@ __all__ = [
     "kappa_from_scores",
     "kappa",
     "attention_direct",
+    "attention_backward",
     "feature_count",
     "packed_pairs",
     "phi_k_packed",
@@ -226,6 +227,60 @@ def attention_direct(Q, K, V, group_of_dim, a, b, c, premap_params=None, rows=No
 # --------------------------------------------------------------------------
 # feature-space (HD state) forms
 # --------------------------------------------------------------------------
+
+def attention_backward(Q, K, V, dY, group_of_dim, a, b, c):
+    """Gradients of sum(dY * y) for the causal normalised attention of
+    ``attention_direct`` (no pre-map), by the chain rule on its definition.
+
+    The backward pass the calibration of [OAL] App. B (Eq. (20), the
+    output-matching fit of L) and the joint adaptation of App. F.2 need:
+        y_i = num_i / den_i,  num_i = sum_{j<=i} kappa_ij v_j,  den_i = sum_{j<=i} kappa_ij
+        dnum_i = dY_i / den_i,  dden_i = -(dY_i . y_i) / den_i
+        dkappa_ij = [j <= i] (dnum_i . v_j + dden_i)
+        dV_j = sum_i kappa_ij dnum_i
+        dkappa/ds_g = b_g + sum_h (c_gh + c_hg) s_h
+        dQ_ir = sum_j dkappa_ij (dkappa/ds_g(r))_ij k_jr / sqrt(d)   (dK likewise with q_ir)
+        da = sum dkappa,  db_g = sum dkappa s_g,  dc_gh = sum dkappa s_g s_h
+    (the coefficient gradients summed over the batch).  Q, K, V, dY as in
+    ``attention_direct`` (dY: [B, Hq, N, dv]).  Returns dQ, dK, dV (fp64, the
+    input shapes), da [Hq], db [Hq, G], dc [Hq, G, G].
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    dY = np.asarray(dY, np.float64)
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    G = len(b[0])
+    da, db, dc = np.zeros(Hq), np.zeros((Hq, G)), np.zeros((Hq, G, G))
+    causal = np.tril(np.ones((N, N)))
+    for bi in range(B):
+        for h in range(Hq):
+            kh = _kv_head(h, Hq, Hkv)
+            q, k, v = Q[bi, h], K[bi, kh], V[bi, kh]
+            gd = np.asarray(group_of_dim[h])
+            s = group_scores(q, k, gd, G)
+            w = kappa_from_scores(s, a[h], b[h], c[h]) * causal
+            num, den = w @ v, w.sum(axis=1)
+            y = num / den[:, None]
+            dnum = dY[bi, h] / den[:, None]
+            dden = -(dY[bi, h] * y).sum(axis=1) / den
+            dk = (dnum @ v.T + dden[:, None]) * causal
+            dV[bi, kh] += w.T @ dnum
+            cs = np.asarray(c[h], np.float64)
+            for g in range(G):
+                dks = float(b[h][g]) + sum((cs[g, hh] + cs[hh, g]) * s[hh] for hh in range(G))
+                m = dk * dks
+                dims = np.nonzero(gd == g)[0]
+                dQ[bi, h][:, dims] += (m @ k[:, dims]) / math.sqrt(d)
+                dK[bi, kh][:, dims] += (m.T @ q[:, dims]) / math.sqrt(d)
+                db[h, g] += (dk * s[g]).sum()
+                for hh in range(G):
+                    dc[h, g, hh] += (dk * s[g] * s[hh]).sum()
+            da[h] += dk.sum()
+    return dQ, dK, dV, da, db, dc
+
 
 def feature_count(d):
     """Packed feature count 1 + d + d(d+1)/2 ([OAL] App. D)."""

@@ -430,6 +430,51 @@ def test_taylorshift_through_the_grouped_kernel():
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------- backward
+
+def test_attention_backward_against_finite_differences():
+    """The oracle's analytic gradients of sum(dY * y) against central finite
+    differences of the forward definition (attention_direct) in fp64, on a
+    tiny grouped-query case with uneven groups: every element of Q, K, V and
+    of a, b, c."""
+    rng = np.random.default_rng(61)
+    B, Hq, Hkv, N, d, dv, G = 1, 2, 1, 5, 4, 3, 2
+    Q, K, V = _rand(rng, B, Hq, N, d), _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, dv)
+    dY = _rand(rng, B, Hq, N, dv)
+    groups = np.array([[0, 1, 1, 0], [1, 0, 0, 1]])
+    a, b, c = O.coeffs_from_factor(0.1, rng.standard_normal((Hq, G + 1, G + 1)) * 0.7)
+    c = c + 0.05 * rng.standard_normal(c.shape)  # not symmetric: every ordered entry is its own parameter
+
+    def loss(Q_, K_, V_, a_, b_, c_):
+        return float((dY * O.attention_direct(Q_, K_, V_, groups, a_, b_, c_)).sum())
+
+    got = O.attention_backward(Q, K, V, dY, groups, a, b, c)
+    args = [Q, K, V, a, b, c]
+    h = 1e-6
+    for which, g in enumerate(got):
+        x = args[which]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            up = [np.array(t, dtype=np.float64, copy=True) for t in args]
+            dn = [np.array(t, dtype=np.float64, copy=True) for t in args]
+            up[which][idx] += h
+            dn[which][idx] -= h
+            fd[idx] = (loss(*up) - loss(*dn)) / (2 * h)
+        scale = max(np.abs(fd).max(), 1e-3)
+        assert np.abs(g - fd).max() <= 1e-6 * scale, (which, np.abs(g - fd).max(), scale)
+
+
+def test_attention_backward_closed_form_single_key():
+    """N = 1: y = v (any kernel), so dV = dY and every other gradient is 0."""
+    rng = np.random.default_rng(62)
+    Q, K, V, dY = _rand(rng, 1, 1, 1, 4), _rand(rng, 1, 1, 1, 4), _rand(rng, 1, 1, 1, 3), _rand(rng, 1, 1, 1, 3)
+    a, b, c = O.coeffs_from_factor(0.1, rng.standard_normal((1, 3, 3)))
+    dQ, dK, dV, da, db, dc = O.attention_backward(Q, K, V, dY, np.array([[0, 0, 1, 1]]), a, b, c)
+    assert np.allclose(dV, dY, rtol=1e-14)
+    for g in (dQ, dK, da, db, dc):
+        assert np.abs(g).max() <= 1e-14
+
+
 # ---------------------------------------------------------------- contribution score
 
 def test_chi_bruteforce_equals_separable_varlen_gqa():
