@@ -13,6 +13,8 @@ from .ops import (  # noqa: F401
     PrefillPlan,
     Prep,
     StepPlan,
+    bwd,
+    bwd_workspace_bytes,
     coeffs_from_factor,
     contrib,
     decode_step,

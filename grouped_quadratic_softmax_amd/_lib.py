@@ -68,6 +68,8 @@ _SIGS = {
     "oal_decode_step_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "oal_contrib_workspace_bytes": ([_P], ctypes.c_size_t),
     "oal_contrib": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "oal_bwd_workspace_bytes": ([_P], ctypes.c_size_t),
+    "oal_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_group_dims": ([ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
     "oal_group_dims_budget": ([ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_double, _P], ctypes.c_int),
     # include/oal_ceilings.h

@@ -337,4 +337,39 @@ int oal_contrib(const oal_dims* dims, const void* q, const void* k, const int32_
   return oal::launch_contrib(a, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
 }
 
+size_t oal_bwd_workspace_bytes(const oal_dims* dims) {
+  if (check_dims(dims, true) != OAL_OK || check_coeff_dims(dims) != OAL_OK) return 0;
+  if (!oal::bwd16_supported(dims->d_h, dims->d_v, dims->dtype, false, dims->n_groups, dims->n_q_heads,
+                            dims->n_kv_heads))
+    return 0;
+  return oal::bwd16_workspace_bytes(dims->batch, dims->n_q_heads, dims->seq_len);
+}
+
+int oal_bwd(const oal_dims* dims, const void* q, const void* k, const void* v, const void* dy,
+            const oal_coeffs* coeffs, float* dq, float* dk, float* dv, float* da, float* db, float* dc,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(dims, true);
+  if (st != OAL_OK) return st;
+  if ((st = check_coeff_dims(dims)) != OAL_OK) return st;
+  if ((st = check_coeff_ptrs(coeffs)) != OAL_OK) return st;
+  if (!oal::bwd16_supported(dims->d_h, dims->d_v, dims->dtype, coeffs->diagonal != 0, dims->n_groups,
+                            dims->n_q_heads, dims->n_kv_heads))
+    return OAL_ERR_UNSUPPORTED;
+  if (da == nullptr || db == nullptr || dc == nullptr) return OAL_ERR_INVALID_ARG;
+  const bool work = dims->batch > 0 && dims->seq_len > 0;
+  if (work && (q == nullptr || k == nullptr || v == nullptr || dy == nullptr || dq == nullptr ||
+               dk == nullptr || dv == nullptr))
+    return OAL_ERR_INVALID_ARG;
+  if (!all_aligned16({q, k, v, dy, dq, dk, dv, workspace})) return OAL_ERR_INVALID_ARG;
+  const size_t need = oal_bwd_workspace_bytes(dims);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return OAL_ERR_WORKSPACE;
+  oal::BwdLaunch a{};
+  a.B = dims->batch; a.H = dims->n_q_heads; a.N = dims->seq_len; a.G = dims->n_groups; a.dtype = dims->dtype;
+  a.q = q; a.k = k; a.v = v; a.dy = dy;
+  a.group_of_dim = coeffs->group_of_dim; a.ca = coeffs->a; a.cb = coeffs->b; a.cc = coeffs->c;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.da = da; a.db = db; a.dc = dc;
+  a.workspace = workspace;
+  return oal::launch_bwd16(a, (hipStream_t)stream) == hipSuccess ? OAL_OK : OAL_ERR_HIP;
+}
+
 }  // extern "C"

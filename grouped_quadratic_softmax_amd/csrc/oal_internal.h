@@ -92,6 +92,18 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 // the decode step's scratch array of the current device (see oal_decode_step_noalloc)
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 hipError_t decode_scratch(void** ptr);
+// Backward pass at d_h = 16, d_v = 64, heads with their own keys, no pre-map
+struct BwdLaunch {
+  int B, H, N, G, dtype;
+  const void *q, *k, *v, *dy;
+  const int32_t* group_of_dim;
+  const float *ca, *cb, *cc;
+  float *dq, *dk, *dv, *da, *db, *dc;
+  void* workspace;
+};
+bool bwd16_supported(int d_h, int d_v, int dtype, bool diagonal, int G, int Hq, int Hkv);
+size_t bwd16_workspace_bytes(int B, int H, int N);
+hipError_t launch_bwd16(const BwdLaunch& a, hipStream_t stream);
 size_t contrib_workspace_bytes(int P, int Hq, int Hkv, int N, int d_h);
 hipError_t launch_contrib(const ContribLaunch& a, hipStream_t stream);
 

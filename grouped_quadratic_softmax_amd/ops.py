@@ -63,12 +63,14 @@ class Coeffs:
         L.check(L.lib().oal_check_coeffs(ctypes.byref(dims), g.ctypes.data_as(ctypes.c_void_p),
                                          c.ctypes.data_as(ctypes.c_void_p)), "oal_check_coeffs")
         self.n_heads, self.d_h, self.n_groups = Hq, d, G
+        # c without off-diagonal entries: the grouped kernel equals the
+        # dimension-wise form read from the same coefficients
+        self.offdiag_zero = not np.any(c * (1.0 - np.eye(G, dtype=np.float32)))
         if diagonal is None:
             # the dimension-wise form is exact when every group is one
             # dimension and c is diagonal; it is required beyond 8 groups
             singletons = G == d and all(np.array_equal(np.sort(row), np.arange(d)) for row in g)
-            offdiag = c * (1.0 - np.eye(G, dtype=np.float32))
-            diagonal = bool(singletons and not np.any(offdiag))
+            diagonal = bool(singletons and self.offdiag_zero)
         self.diagonal = bool(diagonal)
         self.group_of_dim = torch.from_numpy(g).to(device)
         self.a = torch.from_numpy(a).to(device)
@@ -242,6 +244,45 @@ def contrib(q, k, seq_lens=None, per_prompt=False, workspace=None):
                              _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream())
     L.check(st, "oal_contrib")
     return (chi, chip) if per_prompt else chi
+
+
+def bwd_workspace_bytes(B, H, N, d_h, d_v, G, dtype) -> int:
+    dims = _dims(B, H, H, N, d_h, d_v, G, dtype)
+    return int(L.lib().oal_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def bwd(q, k, v, dy, coeffs: Coeffs, workspace=None):
+    """Gradients of sum(dy * y) for y = fwd(q, k, v, coeffs) (oal_bwd).
+
+    q, k [B, H, N, 16], v, dy [B, H, N, 64], one dtype.  Returns dq, dk, dv
+    (float32, the input shapes) and da [H], db [H, G], dc [H, G, G] (float32,
+    summed over the batch)."""
+    _dev(q, "q", ndim=4)
+    _need(q.dtype in _DT, "q must be float32 or bfloat16")
+    _dev(k, "k", q.dtype, 4)
+    _dev(v, "v", q.dtype, 4)
+    _dev(dy, "dy", q.dtype, 4)
+    B, H, N, d = q.shape
+    dv = v.shape[3]
+    _need(k.shape == q.shape and v.shape == (B, H, N, dv) and dy.shape == v.shape, "k/v/dy shapes")
+    _need(coeffs.n_heads == H and coeffs.d_h == d, "coefficients do not match q")
+    G = coeffs.n_groups
+    dims = _dims(B, H, H, N, d, dv, G, q.dtype)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dvv = torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32)
+    da, db, dc = torch.empty((H,), **f32), torch.empty((H, G), **f32), torch.empty((H, G, G), **f32)
+    nbytes = int(L.lib().oal_bwd_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    cs = coeffs.struct()
+    if coeffs.diagonal:  # the backward takes the grouped kernel, which is the same kernel here
+        _need(coeffs.offdiag_zero, "bwd: the dimension-wise form with off-diagonal c entries has no backward")
+        cs.diagonal = 0
+    st = L.lib().oal_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(dy), ctypes.byref(cs), _ptr(dq),
+                         _ptr(dk), _ptr(dvv), _ptr(da), _ptr(db), _ptr(dc), _ptr(workspace),
+                         ctypes.c_size_t(workspace.numel()), _stream())
+    L.check(st, "oal_bwd")
+    return dq, dk, dvv, da, db, dc
 
 
 class PrefillPlan:

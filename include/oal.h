@@ -290,6 +290,37 @@ int oal_contrib(const oal_dims* dims, const void* q, const void* k, const int32_
                 float* chi_per_prompt, float* chi_mean, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/* Bytes of device workspace oal_bwd needs for `dims` (0 if invalid or
+ * unsupported). */
+size_t oal_bwd_workspace_bytes(const oal_dims* dims);
+
+/* Backward pass of the causal attention of oal_fwd (no pre-map, no initial
+ * state): the gradients of L = sum(dy * y) with respect to q, k, v and the
+ * coefficients, which the output-matching calibration of the paper (App. B,
+ * Eq. (20)) and the joint adaptation of the coefficients (App. F.2) take.
+ * With y_i = num_i / den_i (num_i = sum_{j<=i} kappa_ij v_j, den_i =
+ * sum_{j<=i} kappa_ij), dkappa_ij = (dy_i . v_j - dy_i . y_i) / den_i for
+ * j <= i, and the chain rule through kappa (header comment) gives
+ *   dq_i = sum_j dkappa_ij dkappa/dq_i,  dk_j = sum_i dkappa_ij dkappa/dk_j,
+ *   dv_j = sum_{i>=j} kappa_ij dy_i / den_i,
+ *   da = sum dkappa,  db_g = sum dkappa s_g,  dc_gh = sum dkappa s_g s_h.
+ *   q, k [B, H, N, d_h], v, dy [B, H, N, d_v] in `dtype` (the same for all
+ *   four); dq, dk [B, H, N, d_h], dv [B, H, N, d_v] float32, overwritten;
+ *   da [H], db [H, G], dc [H, G, G] float32, summed over the batch and
+ *   overwritten (zeros when B or N is 0: the one case where a zero-length
+ *   call still enqueues work).
+ *   workspace: at least oal_bwd_workspace_bytes(dims) (the recomputed
+ *              dL/d[num, den] rows and per-sequence coefficient sums);
+ *              contents undefined afterwards.
+ * Supports d_h = 16, d_v = 64, heads with their own keys (Hq == Hkv), any
+ * G <= 16, the grouped kernel (coeffs->diagonal == 0); others return
+ * OAL_ERR_UNSUPPORTED.  Recomputes the forward pass in float32; the result is
+ * deterministic.  Calls that share a workspace must be ordered on one
+ * stream. */
+int oal_bwd(const oal_dims* dims, const void* q, const void* k, const void* v, const void* dy,
+            const oal_coeffs* coeffs, float* dq, float* dk, float* dv, float* da, float* db, float* dc,
+            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- dimension grouping (host functions; every pointer below is HOST) ---- */
 
 /* Settings of the outlier-aware grouping (paper, App. B, "Grouping

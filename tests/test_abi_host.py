@@ -211,6 +211,37 @@ def test_decode_and_contrib_validation(L, no_device):
         L.OAL_ERR_WORKSPACE
 
 
+def _bwd(L, dims, coeffs=True, diagonal=0, ws=(FAKE, 1 << 40), dq=FAKE, da=FAKE, dy=FAKE):
+    lib = L.lib()
+    cs = L.OalCoeffs(0x1000, 0x1000, 0x1000, 0x1000, diagonal) if coeffs else None
+    return lib.oal_bwd(ctypes.byref(dims) if dims is not None else None, FAKE, FAKE, FAKE, dy,
+                       ctypes.byref(cs) if cs is not None else None, dq, FAKE, FAKE, da, FAKE, FAKE, ws[0],
+                       ctypes.c_size_t(ws[1]), None)
+
+
+def test_bwd_validation_errors(L, no_device):
+    E, U, W = L.OAL_ERR_INVALID_ARG, L.OAL_ERR_UNSUPPORTED, L.OAL_ERR_WORKSPACE
+    ok = _dims(L, B=2, d=16, Hq=4, Hkv=4, G=16, N=300)
+    assert _bwd(L, None) == E
+    assert _bwd(L, _dims(L, d=16, G=17)) == E                  # G > d_h
+    assert _bwd(L, _dims(L, d=64, Hq=4, Hkv=4)) == U           # only d_h = 16
+    assert _bwd(L, _dims(L, d=16, Hq=4, Hkv=2)) == U           # heads with their own keys only
+    assert _bwd(L, ok, diagonal=1) == U                        # the grouped kernel only
+    assert _bwd(L, ok, coeffs=False) == E
+    assert _bwd(L, ok, dy=None) == E
+    assert _bwd(L, ok, dq=None) == E
+    assert _bwd(L, ok, da=None) == E
+    assert _bwd(L, ok, dy=_mis(4)) == E                        # 16-byte alignment
+    need = L.lib().oal_bwd_workspace_bytes(ctypes.byref(ok))
+    # recomputed dL/d[num, den] rows plus per-sequence coefficient sums (153 features at d_h = 16)
+    rows = 2 * 4 * 300 * 65 * 4
+    assert need == (rows + 255) // 256 * 256 + 2 * 4 * 153 * 4
+    assert _bwd(L, ok, ws=(None, 0)) == W
+    assert _bwd(L, ok, ws=(FAKE, need - 1)) == W
+    assert L.lib().oal_bwd_workspace_bytes(ctypes.byref(_dims(L, d=32, Hq=4, Hkv=4))) == 0
+    assert L.lib().oal_bwd_workspace_bytes(None) == 0
+
+
 def test_binding_refuses_cpu_tensors(L):
     import torch
     import grouped_quadratic_softmax_amd as oal
