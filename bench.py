@@ -15,8 +15,8 @@ own stream; `roofline_decode` is the batched decode step of 256 sequences x
 16 heads with fp32 states (HBM-bound); `ceilings` are the in-place stream and
 MFMA-chain probes measured in the same run; `cpu_baseline` is the fp64
 oracle on the host.  Secondary lines (under "secondary") time the other
-workloads' hot kernels: the Qwen-shaped GQA layer, the ReBased prefill and the
-32k-token prefill.
+workloads' hot kernels: the Qwen-shaped GQA layer, the ReBased prefill, the
+32k-token prefill, and the backward pass of the timed prefill.
 """
 
 from __future__ import annotations
@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 matrix cores (256 CUs x 2.4 GHz x 256 flops per cycle)
 COPY_BYTES = 1 << 30        # calibration copy for the HBM byte counters
 STREAM_BYTES = 2 << 30      # in-place stream probe (read and written once each)
 METRIC = "causal OAL attention tokens/s at 1 GPU; % bf16 MFMA peak (prefill), % HBM BW (decode)"
@@ -71,6 +72,22 @@ def coeffs_for(wl, groups=None):
     else:
         a, b, c = wl.coeff["a"], wl.coeff["b"], wl.coeff["c"]
     return oal.Coeffs(wl.group_of_dim if groups is None else groups, a, b, c)
+
+
+def bwd_flops_per_token(d, N, C=32):
+    """Algorithmic flops per (token, head) of the backward pass in the packed
+    feature space (D features, d_v + 1 columns with the normaliser), counted
+    from its definition (2 flops per multiply-add): the six state products
+    of D x (d_v + 1) per token (the readout it recomputes against S, S g, the
+    state update, R u, R^T m(k) and the R update), and per causal pair within
+    a C-token chunk (C / 2 pairs per token on average): kappa twice (2 D
+    each), dkappa twice (2 (d_v + 1) each), the readout's pair term (d_v + 1),
+    the dq and dk pair terms (2 D each) and dv's (d_v).  The segment sums
+    that let segments run in parallel are not counted."""
+    D = feature_count(d)
+    state = 6 * 2 * D * (DV + 1)
+    pair = 2 * (2 * D) + 2 * (2 * (DV + 1)) + 2 * (DV + 1) + 2 * (2 * D) + 2 * DV
+    return state + pair * min(C, N) / 2
 
 
 def time_events(fn, steps, warmup):
@@ -294,6 +311,25 @@ def run_secondary(args):
     out["c5_long_prefill"] = {"ms": ms, "tokens_per_s": tok / (ms * 1e-3),
                               "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     del pre, q, k, v
+    # the backward pass of the Based prefill (B=8, H=16, N=8192, d_h=16):
+    # fp32 matrix-core products over the packed features
+    wl = S.make(3)
+    q, k, v = device_inputs(wl)
+    dy = torch.randn(v.shape, generator=torch.Generator(device="cuda").manual_seed(2102), device="cuda").to(v.dtype)
+    co = coeffs_for(wl)
+    B_, H_, N_ = wl.batch, wl.n_q_heads, wl.seq_len
+    f32 = dict(dtype=torch.float32, device="cuda")
+    outs = (torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32),
+            torch.empty((H_,), **f32), torch.empty((H_, 1), **f32), torch.empty((H_, 1, 1), **f32))
+    ws = torch.empty(max(oal.bwd_workspace_bytes(B_, H_, N_, 16, DV, 1, q.dtype), 1), dtype=torch.uint8,
+                     device="cuda")
+    ms = time_events(lambda: oal.bwd(q, k, v, dy, co, workspace=ws, out=outs), steps, warm)
+    flops = B_ * H_ * N_ * bwd_flops_per_token(16, N_)
+    out["f2_based_backward"] = {"ms": ms, "tokens_per_s": B_ * N_ / (ms * 1e-3),
+                                "fp32_mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+                                "kernels": "bwd16_segsum_kernel x2, bwd16_fwd_kernel, bwd16_rev_kernel, "
+                                           "bwd16_coef_kernel (fp32 MFMA)"}
+    del q, k, v, dy, outs, ws
     return out
 
 
@@ -312,7 +348,8 @@ def run_pmc_target(args):
     1 GiB (fp32), whose FETCH_SIZE and WRITE_SIZE readings calibrate the
     counters against a known byte count; ``mfma``: the bf16 MFMA chain probe,
     whose MFMA counters calibrate the busy fraction of the prefill kernels;
-    ``stream``: the in-place stream probe over 2 GiB."""
+    ``stream``: the in-place stream probe over 2 GiB; ``bwd``: the backward
+    pass of the timed workload's prefill (B=8, H=16, N=8192, d_h=16)."""
     import ctypes
     import torch
     import grouped_quadratic_softmax_amd as oal
@@ -362,6 +399,18 @@ def run_pmc_target(args):
         groups = oal.groups_from_contribution(chi, wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"])
         pre = oal.PrefillPlan(q, k, v, coeffs_for(wl, groups), staged=False)
         repeat(pre.run)
+        return
+    if t == "bwd":
+        wl = S.make(3)
+        q, k, v = device_inputs(wl)
+        dy = torch.randn(v.shape, generator=torch.Generator(device="cuda").manual_seed(2102),
+                         device="cuda").to(v.dtype)
+        co = coeffs_for(wl)
+        f32 = dict(dtype=torch.float32, device="cuda")
+        H_ = wl.n_q_heads
+        outs = (torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32),
+                torch.empty((H_,), **f32), torch.empty((H_, 1), **f32), torch.empty((H_, 1, 1), **f32))
+        repeat(lambda: oal.bwd(q, k, v, dy, co, out=outs))
         return
     if t in ("based16", "rebased"):
         wl = S.make(3 if t == "based16" else 4)
@@ -426,7 +475,7 @@ def main():
     ap.add_argument("--no-overlap", action="store_true",
                     help="run chi, prefill and decode back to back on one stream")
     ap.add_argument("--pmc-target", default=None,
-                    choices=("based16", "decode", "readout", "states", "rebased", "long", "copy", "mfma", "stream"),
+                    choices=("based16", "decode", "readout", "states", "rebased", "long", "copy", "mfma", "stream", "bwd"),
                     help="only launch this kernel --steps times (for rocprofv3 counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

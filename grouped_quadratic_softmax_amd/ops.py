@@ -251,12 +251,13 @@ def bwd_workspace_bytes(B, H, N, d_h, d_v, G, dtype) -> int:
     return int(L.lib().oal_bwd_workspace_bytes(ctypes.byref(dims)))
 
 
-def bwd(q, k, v, dy, coeffs: Coeffs, workspace=None):
+def bwd(q, k, v, dy, coeffs: Coeffs, workspace=None, out=None):
     """Gradients of sum(dy * y) for y = fwd(q, k, v, coeffs) (oal_bwd).
 
     q, k [B, H, N, 16], v, dy [B, H, N, 64], one dtype.  Returns dq, dk, dv
     (float32, the input shapes) and da [H], db [H, G], dc [H, G, G] (float32,
-    summed over the batch)."""
+    summed over the batch), written into `out` (those six tensors) when
+    given."""
     _dev(q, "q", ndim=4)
     _need(q.dtype in _DT, "q must be float32 or bfloat16")
     _dev(k, "k", q.dtype, 4)
@@ -269,8 +270,14 @@ def bwd(q, k, v, dy, coeffs: Coeffs, workspace=None):
     G = coeffs.n_groups
     dims = _dims(B, H, H, N, d, dv, G, q.dtype)
     f32 = dict(dtype=torch.float32, device=q.device)
-    dq, dk, dvv = torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32)
-    da, db, dc = torch.empty((H,), **f32), torch.empty((H, G), **f32), torch.empty((H, G, G), **f32)
+    shapes = (q.shape, k.shape, v.shape, (H,), (H, G), (H, G, G))
+    if out is None:
+        out = tuple(torch.empty(sh, **f32) for sh in shapes)
+    _need(len(out) == 6, "out must hold dq, dk, dv, da, db, dc")
+    for t, sh, name in zip(out, shapes, ("dq", "dk", "dv", "da", "db", "dc")):
+        _dev(t, name, torch.float32)
+        _need(tuple(t.shape) == tuple(sh), f"{name} shape")
+    dq, dk, dvv, da, db, dc = out
     nbytes = int(L.lib().oal_bwd_workspace_bytes(ctypes.byref(dims)))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
