@@ -74,6 +74,11 @@ __all__ = [
     "group_dims_bootstrap",
     "group_dims_budget",
     "groups_sorted_split",
+    "softmax_attention",
+    "factor_grad",
+    "adam_clip_step",
+    "validation_errors",
+    "calibrate",
 ]
 
 
@@ -645,3 +650,162 @@ def groups_sorted_split(chi, bulk_sizes, n_tail):
             pos += 1
         out.append(gid)
     return np.array(out, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# output-matching calibration of the factors ([OAL] App. B, Eq. (20) and
+# "Coefficient-calibration settings")
+# --------------------------------------------------------------------------
+
+def softmax_attention(Q, K, V):
+    """Causal softmax attention, the calibration target y^softmax of [OAL]
+    Eq. (20): y_i = sum_{j<=i} w_ij v_j with w_ij proportional to
+    exp(q_i . k_j / sqrt(d_h)) over the causal prefix.  fp64; shapes as in
+    ``attention_direct`` (query head h reads KV head h // (Hq / Hkv))."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    out = np.zeros((B, Hq, N, V.shape[3]))
+    mask = np.tril(np.ones((N, N), bool))
+    for bi in range(B):
+        for h in range(Hq):
+            kh = _kv_head(h, Hq, Hkv)
+            s = (Q[bi, h] @ K[bi, kh].T) / math.sqrt(d)
+            s = np.where(mask, s, -np.inf)
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            out[bi, h] = (w @ V[bi, kh]) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+def factor_grad(L, da, db, dc):
+    """Gradient with respect to the factor L (lower triangle, [G+1, G+1]) of
+    an objective that depends on L only through (a, b, c) =
+    ``coeffs_from_factor(eps, L)``, given its gradients da, db [G], dc [G, G].
+    With M = L L^T, a = eps + M_00, b_g = 2 M_0g, c_gh = M_gh, the objective
+    reads the entries Mbar = [[da, 2 db^T], [0, dc]] of M, and
+    d/dL = (Mbar + Mbar^T) L restricted to the lower triangle."""
+    L = np.tril(np.asarray(L, np.float64))
+    G = len(db)
+    Mbar = np.zeros((G + 1, G + 1))
+    Mbar[0, 0] = da
+    Mbar[0, 1:] = 2.0 * np.asarray(db, np.float64)
+    Mbar[1:, 1:] = np.asarray(dc, np.float64)
+    return np.tril((Mbar + Mbar.T) @ L)
+
+
+def adam_clip_step(theta, grad, m, v, t, lr, clip, beta1=0.9, beta2=0.999, eps=1e-8):
+    """One Adam update of the parameter vector theta (the settings' optimiser:
+    Adam at learning rate lr, gradient norm clipped at clip).  The gradient is
+    first scaled by clip / (||grad|| + 1e-6) when its norm exceeds clip; then
+    the bias-corrected moments of step t (t >= 1) give
+    theta - lr * mhat / (sqrt(vhat) + eps).  Returns (theta, m, v)."""
+    grad = np.asarray(grad, np.float64)
+    norm = float(np.sqrt((grad * grad).sum()))
+    if norm > clip:
+        grad = grad * (clip / (norm + 1e-6))
+    m = beta1 * m + (1.0 - beta1) * grad
+    v = beta2 * v + (1.0 - beta2) * grad * grad
+    mhat = m / (1.0 - beta1 ** t)
+    vhat = v / (1.0 - beta2 ** t)
+    return theta - lr * mhat / (np.sqrt(vhat) + eps), m, v
+
+
+def _tril_index(n):
+    return np.tril_indices(n)
+
+
+def validation_errors(L, eps, group_of_dim, Qv, Kv, Vv, Yv):
+    """Per-head MSE and RelMSE of the OAL outputs with factors L [H, G+1, G+1]
+    against the targets Yv over whole validation sequences ([OAL] metric
+    definitions: the mean over sequences of ||Yhat_b - Y_b||_F^2 / n_b, n_b
+    the scalar output elements, and of ||Yhat_b - Y_b||_F^2 / ||Y_b||_F^2)."""
+    a, b, c = coeffs_from_factor(eps, L)
+    Yh = attention_direct(Qv, Kv, Vv, group_of_dim, a, b, c)
+    err = ((Yh - Yv) ** 2).sum(axis=(2, 3))      # [V, H]
+    n = Yv.shape[2] * Yv.shape[3]
+    mse = (err / n).mean(axis=0)
+    rel = (err / (Yv ** 2).sum(axis=(2, 3))).mean(axis=0)
+    return mse, rel
+
+
+def calibrate(train, val, group_of_dim, eps, inits, plan, lr=0.02, clip=10.0, validate_every=100,
+              patience=400, targets=None):
+    """Output-matching calibration of the factors L of every head ([OAL]
+    App. B, Eq. (20)), following the coefficient-calibration settings: Adam
+    at lr, gradient norm clipped at clip, one training sequence and the
+    sampled causal query positions per update, validation every
+    ``validate_every`` updates, early stop after ``patience`` updates without
+    improvement, the lowest-validation-MSE checkpoint kept per head within
+    each initialisation candidate and the best candidate chosen per head.
+
+    Readings (the settings leave them open): each head is its own objective
+    and optimiser (independent coefficients per head; its gradient norm is
+    clipped alone and it stops alone); an update's objective is the mean over
+    its sampled positions of ||yhat_i - y_i||^2; validation runs on whole
+    sequences, also before the first update (update 0), so the initial
+    factors are a checkpoint; every candidate follows the same plan.
+
+    train, val: (Q, K, V) arrays [T, H, N, d] / [V, H, N, d] (heads with their
+    own keys); inits [n_init, H, G+1, G+1]; plan [U, 1 + P] int: per update,
+    the training sequence and P distinct positions.  targets: optional
+    (Y_train, Y_val) in place of the softmax outputs.  Returns a dict with
+    the chosen factors "L" [H, G+1, G+1], "mse", "relmse", "init" [H], and per
+    candidate "cand_mse" [n_init, H], "cand_L", "updates" [n_init, H] (the
+    updates each head ran)."""
+    Qt, Kt, Vt = (np.asarray(x, np.float64) for x in train)
+    Qv, Kv, Vv = (np.asarray(x, np.float64) for x in val)
+    inits = np.asarray(inits, np.float64)
+    plan = np.asarray(plan)
+    n_init, H, n, _ = inits.shape
+    G = n - 1
+    if targets is None:
+        Yt, Yv = softmax_attention(Qt, Kt, Vt), softmax_attention(Qv, Kv, Vv)
+    else:
+        Yt, Yv = (np.asarray(x, np.float64) for x in targets)
+    ti = _tril_index(n)
+    cand_mse = np.zeros((n_init, H))
+    cand_rel = np.zeros((n_init, H))
+    cand_L = np.zeros((n_init, H, n, n))
+    cand_upd = np.zeros((n_init, H), np.int64)
+    for ci in range(n_init):
+        L = np.stack([np.tril(inits[ci, h]) for h in range(H)])
+        m = np.zeros((H, len(ti[0])))
+        v = np.zeros((H, len(ti[0])))
+        best, best_rel = validation_errors(L, eps, group_of_dim, Qv, Kv, Vv, Yv)
+        best_L = L.copy()
+        last = np.zeros(H, np.int64)
+        active = np.ones(H, bool)
+        done = np.zeros(H, np.int64)
+        for u in range(1, len(plan) + 1):
+            if not active.any():
+                break
+            seq, pos = int(plan[u - 1, 0]), np.asarray(plan[u - 1, 1:])
+            a, b, c = coeffs_from_factor(eps, L)
+            sl = slice(seq, seq + 1)
+            y = attention_direct(Qt[sl], Kt[sl], Vt[sl], group_of_dim, a, b, c)
+            dY = np.zeros_like(y)
+            dY[0][:, pos] = 2.0 * (y[0][:, pos] - Yt[seq][:, pos]) / len(pos)
+            _, _, _, da, db, dc = attention_backward(Qt[sl], Kt[sl], Vt[sl], dY, group_of_dim, a, b, c)
+            for h in range(H):
+                if not active[h]:
+                    continue
+                gL = factor_grad(L[h], da[h], db[h], dc[h])
+                th, m[h], v[h] = adam_clip_step(L[h][ti], gL[ti], m[h], v[h], u, lr, clip)
+                L[h][ti] = th
+                done[h] = u
+            if u % validate_every == 0:
+                mse, rel = validation_errors(L, eps, group_of_dim, Qv, Kv, Vv, Yv)
+                for h in range(H):
+                    if not active[h]:
+                        continue
+                    if mse[h] < best[h]:
+                        best[h], best_rel[h], best_L[h], last[h] = mse[h], rel[h], L[h], u
+                    elif u - last[h] >= patience:
+                        active[h] = False
+        cand_mse[ci], cand_rel[ci], cand_L[ci], cand_upd[ci] = best, best_rel, best_L, done
+    pick = cand_mse.argmin(axis=0)
+    hs = np.arange(H)
+    return {"L": cand_L[pick, hs], "mse": cand_mse[pick, hs], "relmse": cand_rel[pick, hs], "init": pick,
+            "cand_mse": cand_mse, "cand_L": cand_L, "updates": cand_upd}

@@ -615,3 +615,148 @@ def test_groups_sorted_split_properties():
         assert np.array_equal(gp, gid[h][perm])
     with pytest.raises(ValueError):
         O.groups_sorted_split(chi, [10], 2)
+
+
+# ---------------------------------------------------------------- calibration
+
+def test_softmax_attention_bruteforce_and_closed_forms():
+    """The calibration target against pure-Python loops of its definition on
+    a tiny grouped-query case, and closed forms: one key gives y = v; equal
+    keys give the prefix mean of the values."""
+    rng = np.random.default_rng(71)
+    B, Hq, Hkv, N, d, dv = 1, 2, 1, 5, 3, 2
+    Q, K, V = _rand(rng, B, Hq, N, d), _rand(rng, B, Hkv, N, d), _rand(rng, B, Hkv, N, dv)
+    got = O.softmax_attention(Q, K, V)
+    for h in range(Hq):
+        for i in range(N):
+            w = [math.exp(sum(Q[0, h, i, r] * K[0, 0, j, r] for r in range(d)) / math.sqrt(d)) for j in range(i + 1)]
+            for col in range(dv):
+                ref = sum(w[j] * V[0, 0, j, col] for j in range(i + 1)) / sum(w)
+                assert abs(got[0, h, i, col] - ref) <= 1e-13 * max(1.0, abs(ref))
+    one = O.softmax_attention(Q[:, :, :1], K[:, :, :1], V[:, :, :1])
+    assert np.allclose(one[0, 0, 0], V[0, 0, 0], rtol=1e-15)
+    Ke = np.repeat(K[:, :, :1], N, axis=2)
+    eq = O.softmax_attention(Q, Ke, V)
+    for i in range(N):
+        assert np.allclose(eq[0, 1, i], V[0, 0, : i + 1].mean(axis=0), rtol=1e-13)
+
+
+def test_factor_grad_finite_differences():
+    """dJ/dL for J = w_a a + w_b . b + sum w_c * c (non-symmetric weights),
+    (a, b, c) = coeffs_from_factor(eps, L), against central differences in
+    every lower-triangular entry of L."""
+    rng = np.random.default_rng(72)
+    G = 3
+    L = np.tril(rng.standard_normal((G + 1, G + 1)))
+    wa, wb, wc = rng.standard_normal(), rng.standard_normal(G), rng.standard_normal((G, G))
+
+    def J(L_):
+        a, b, c = O.coeffs_from_factor(0.01, L_)
+        return wa * a + (wb * b).sum() + (wc * c).sum()
+
+    g = O.factor_grad(L, wa, wb, wc)
+    h = 1e-6
+    for i in range(G + 1):
+        for j in range(G + 1):
+            if j > i:
+                assert g[i, j] == 0.0
+                continue
+            up, dn = L.copy(), L.copy()
+            up[i, j] += h
+            dn[i, j] -= h
+            fd = (J(up) - J(dn)) / (2 * h)
+            assert abs(g[i, j] - fd) <= 1e-7 * max(1.0, abs(fd)), (i, j)
+
+
+def test_adam_clip_step_closed_forms():
+    """First Adam step: the bias-corrected moments are g and g^2, so each
+    coordinate moves by -lr g / (|g| + eps).  A gradient of norm 100 with the
+    clip at 10 enters the moments scaled by 10 / (100 + 1e-6); a second step
+    follows the moment recursions written out by hand."""
+    g = np.array([3.0, -0.5, 1e-3])
+    th, m, v = O.adam_clip_step(np.zeros(3), g, np.zeros(3), np.zeros(3), 1, 0.02, 10.0)
+    assert np.allclose(th, -0.02 * g / (np.abs(g) + 1e-8), rtol=1e-14)
+    big = np.array([60.0, -80.0, 0.0])
+    th, m, v = O.adam_clip_step(np.zeros(3), big, np.zeros(3), np.zeros(3), 1, 0.02, 10.0)
+    gc = big * (10.0 / (100.0 + 1e-6))
+    assert np.allclose(m, 0.1 * gc, rtol=1e-14) and np.allclose(v, 0.001 * gc * gc, rtol=1e-14)
+    g2 = np.array([1.0, 2.0, -1.0])
+    th2, m2, v2 = O.adam_clip_step(th, g2, m, v, 2, 0.02, 10.0)
+    mm = 0.9 * 0.1 * gc + 0.1 * g2
+    vv = 0.999 * 0.001 * gc * gc + 0.001 * g2 * g2
+    step = (mm / (1 - 0.9 ** 2)) / (np.sqrt(vv / (1 - 0.999 ** 2)) + 1e-8)
+    assert np.allclose(th2, th - 0.02 * step, rtol=1e-13)
+
+
+def _calib_case(rng, T=2, V=1, H=2, N=12, d=4, dv=3, G=2):
+    tr = tuple(_rand(rng, T, H, N, x) for x in (d, d, dv))
+    va = tuple(_rand(rng, V, H, N, x) for x in (d, d, dv))
+    groups = np.array([np.arange(d) % G, (np.arange(d) + 1) % G])[:H]
+    return tr, va, groups
+
+
+def test_calibrate_fixed_point_of_its_own_kernel():
+    """Targets made by the OAL kernel itself at factors L_true: the loss and
+    every gradient are zero there, so Adam does not move (0 / (0 + eps)),
+    the validation error stays 0, no update improves on update 0, and every
+    head stops after exactly `patience` updates."""
+    rng = np.random.default_rng(73)
+    tr, va, groups = _calib_case(rng)
+    Lt = np.stack([np.tril(rng.standard_normal((3, 3))) * 0.7 for _ in range(2)])
+    a, b, c = O.coeffs_from_factor(0.01, Lt)
+    Yt = O.attention_direct(*tr, groups, a, b, c)
+    Yv = O.attention_direct(*va, groups, a, b, c)
+    plan = np.array([[u % 2] + list(rng.choice(12, 4, replace=False)) for u in range(30)])
+    res = O.calibrate(tr, va, groups, 0.01, Lt[None], plan, validate_every=5, patience=10, targets=(Yt, Yv))
+    assert np.array_equal(res["L"], Lt)
+    assert (res["mse"] == 0).all() and (res["updates"] == 10).all()
+
+
+def test_calibrate_selects_best_initial_candidate_at_zero_rate():
+    """With lr = 0 the factors never move: each head's checkpoint is its
+    initial factors, it stops after `patience` updates, and per head the
+    candidate with the lowest initial validation MSE is chosen; the MSE and
+    RelMSE are recomputed here from the metric definitions."""
+    rng = np.random.default_rng(74)
+    tr, va, groups = _calib_case(rng)
+    inits = np.stack([np.stack([np.tril(rng.standard_normal((3, 3))) for _ in range(2)]) for _ in range(3)])
+    plan = np.array([[u % 2] + list(rng.choice(12, 4, replace=False)) for u in range(40)])
+    res = O.calibrate(tr, va, groups, 0.01, inits, plan, lr=0.0, validate_every=5, patience=15)
+    Yv = O.softmax_attention(*va)
+    mse = np.zeros((3, 2))
+    rel = np.zeros((3, 2))
+    for ci in range(3):
+        a, b, c = O.coeffs_from_factor(0.01, inits[ci])
+        Yh = O.attention_direct(*va, groups, a, b, c)
+        for h in range(2):
+            e = ((Yh[0, h] - Yv[0, h]) ** 2).sum()
+            mse[ci, h] = e / Yv[0, h].size
+            rel[ci, h] = e / (Yv[0, h] ** 2).sum()
+    pick = mse.argmin(axis=0)
+    assert np.array_equal(res["init"], pick)
+    assert np.allclose(res["mse"], mse[pick, [0, 1]], rtol=1e-12)
+    assert np.allclose(res["relmse"], rel[pick, [0, 1]], rtol=1e-12)
+    assert (res["updates"] == 15).all()
+    for h in range(2):
+        assert np.array_equal(res["L"][h], np.tril(inits[pick[h], h]))
+
+
+def test_calibrate_lowers_validation_error_from_taylor_start():
+    """From the second-order Taylor factors (a = 1, b_g = 1, c_gh = 1/2,
+    a Cholesky factor of that PSD matrix with a small ridge) on softmax
+    targets, the fit ends with a lower validation MSE for every head than the
+    starting factors, and early stopping ends it before the plan runs out."""
+    rng = np.random.default_rng(75)
+    T, H, N, d, dv, G = 2, 2, 24, 4, 3, 2
+    tr = tuple(rng.standard_normal((T, H, N, x)) for x in (d, d, dv))
+    va = tuple(rng.standard_normal((1, H, N, x)) for x in (d, d, dv))
+    groups = np.array([np.arange(d) % G, (np.arange(d) + 1) % G])
+    M = np.full((G + 1, G + 1), 0.5)
+    M[0, 0] = 1.0
+    L0 = np.linalg.cholesky(M + 1e-3 * np.eye(G + 1))
+    inits = np.stack([np.stack([L0] * H)])
+    plan = np.array([[u % T] + list(rng.choice(N, 8, replace=False)) for u in range(200)])
+    res = O.calibrate(tr, va, groups, 1e-3, inits, plan, validate_every=20, patience=80)
+    start, _ = O.validation_errors(inits[0], 1e-3, groups, *va, O.softmax_attention(*va))
+    assert (res["mse"] < 0.6 * start).all()
+    assert (res["updates"] < 200).all()
