@@ -16,7 +16,8 @@ own stream; `roofline_decode` is the batched decode step of 256 sequences x
 MFMA-chain probes measured in the same run; `cpu_baseline` is the fp64
 oracle on the host.  Secondary lines (under "secondary") time the other
 workloads' hot kernels: the Qwen-shaped GQA layer, the ReBased prefill, the
-32k-token prefill, and the backward pass of the timed prefill.
+32k-token prefill, the backward pass of the timed prefill, and the
+output-matching calibration.
 """
 
 from __future__ import annotations
@@ -330,7 +331,49 @@ def run_secondary(args):
                                 "kernels": "bwd16_segsum_kernel x2, bwd16_fwd_kernel, bwd16_rev_kernel, "
                                            "bwd16_coef_kernel (fp32 MFMA)"}
     del q, k, v, dy, outs, ws
+    out["f3_calibration"] = run_calibration()
     return out
+
+
+def calibration_case():
+    """The calibration run timed here: the Based shape at the settings' scale
+    (8 training and 2 validation sequences of 4096 tokens, 16 heads, d_h = 16,
+    bf16; four groups of four dimensions; 32 positions per update; the
+    Taylor factors as the one candidate)."""
+    import numpy as np
+    import synthetic as S
+    T, V, N, H, G = 8, 2, 4096, 16, 4
+    wl = S.make(3, batch=T + V, seq_len=N)
+    groups = np.repeat(np.arange(G, dtype=np.int32), 16 // G)[None, :].repeat(H, 0)
+    M = np.full((G + 1, G + 1), 0.5)
+    M[0, 0] = 1.0
+    L0 = np.linalg.cholesky(M + 1e-3 * np.eye(G + 1))
+    inits = np.stack([np.stack([L0] * H)])
+    return wl, T, groups, inits
+
+
+def run_calibration(n_updates=100):
+    """oal_calibrate on calibration_case(): one call with no update (targets
+    and the initial validation) and one with n_updates updates and a second
+    validation; the difference over n_updates is the cost of an update."""
+    import numpy as np
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    import synthetic as S
+    wl, T, groups, inits = calibration_case()
+    q, k, v = device_inputs(wl)
+    tr, va = (q[:T], k[:T], v[:T]), (q[T:], k[T:], v[T:])
+    plan = S.calibration_plan(T, wl.seq_len, 32, n_updates)
+    times = []
+    for U in (0, n_updates):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = oal.calibrate(tr, va, groups, inits, plan[:U], validate_every=n_updates, patience=4 * n_updates)
+        times.append(time.perf_counter() - t0)
+    per = (times[1] - times[0]) / n_updates
+    return {"ms_per_update": per * 1e3, "targets_and_validation_ms": times[0] * 1e3,
+            "protocol_3x1000_s": 3 * (times[0] + 1000 * per),
+            "mse_after": float(np.mean(res["mse"])), "shape": "T=8, V=2, N=4096, H=16, d_h=16, G=4, bf16, P=32"}
 
 
 def run_pmc_target(args):
@@ -349,7 +392,9 @@ def run_pmc_target(args):
     counters against a known byte count; ``mfma``: the bf16 MFMA chain probe,
     whose MFMA counters calibrate the busy fraction of the prefill kernels;
     ``stream``: the in-place stream probe over 2 GiB; ``bwd``: the backward
-    pass of the timed workload's prefill (B=8, H=16, N=8192, d_h=16)."""
+    pass of the timed workload's prefill (B=8, H=16, N=8192, d_h=16);
+    ``calib``: one calibration run of ``--steps`` updates on
+    calibration_case()."""
     import ctypes
     import torch
     import grouped_quadratic_softmax_amd as oal
@@ -399,6 +444,15 @@ def run_pmc_target(args):
         groups = oal.groups_from_contribution(chi, wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"])
         pre = oal.PrefillPlan(q, k, v, coeffs_for(wl, groups), staged=False)
         repeat(pre.run)
+        return
+    if t == "calib":
+        import synthetic as S2
+        wl, T, groups, inits = calibration_case()
+        q, k, v = device_inputs(wl)
+        plan = S2.calibration_plan(T, wl.seq_len, 32, args.steps)
+        res = oal.calibrate((q[:T], k[:T], v[:T]), (q[T:], k[T:], v[T:]), groups, inits, plan,
+                            validate_every=max(args.steps, 1))
+        print(json.dumps({"pmc_target": t, "updates": args.steps, "mse": float(res["mse"].mean())}), flush=True)
         return
     if t == "bwd":
         wl = S.make(3)
@@ -475,7 +529,8 @@ def main():
     ap.add_argument("--no-overlap", action="store_true",
                     help="run chi, prefill and decode back to back on one stream")
     ap.add_argument("--pmc-target", default=None,
-                    choices=("based16", "decode", "readout", "states", "rebased", "long", "copy", "mfma", "stream", "bwd"),
+                    choices=("based16", "decode", "readout", "states", "rebased", "long", "copy", "mfma", "stream", "bwd",
+                             "calib"),
                     help="only launch this kernel --steps times (for rocprofv3 counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -14,6 +14,7 @@ from .ops import (  # noqa: F401
     Prep,
     StepPlan,
     bwd,
+    calibrate,
     bwd_workspace_bytes,
     coeffs_from_factor,
     contrib,

@@ -30,6 +30,11 @@ class OalCoeffs(ctypes.Structure):
                 ("c", ctypes.c_void_p), ("diagonal", ctypes.c_int32)]
 
 
+class OalCalibParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("clip", ctypes.c_double), ("eps", ctypes.c_double),
+                ("n_positions", ctypes.c_int32), ("validate_every", ctypes.c_int32), ("patience", ctypes.c_int32)]
+
+
 class OalPrep(ctypes.Structure):
     _fields_ = [("gamma_q", ctypes.c_void_p), ("beta_q", ctypes.c_void_p), ("gamma_k", ctypes.c_void_p),
                 ("beta_k", ctypes.c_void_p), ("ln_eps", ctypes.c_float), ("kind", ctypes.c_int32)]
@@ -70,6 +75,9 @@ _SIGS = {
     "oal_contrib": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_bwd_workspace_bytes": ([_P], ctypes.c_size_t),
     "oal_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "oal_calibrate_workspace_bytes": ([_P, ctypes.c_int32, _P], ctypes.c_size_t),
+    "oal_calibrate": ([_P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
+                       _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "oal_group_dims": ([ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P], ctypes.c_int),
     "oal_group_dims_budget": ([ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_double, _P], ctypes.c_int),
     # include/oal_ceilings.h

@@ -292,6 +292,54 @@ def bwd(q, k, v, dy, coeffs: Coeffs, workspace=None, out=None):
     return dq, dk, dvv, da, db, dc
 
 
+def calibrate(train, val, group_of_dim, inits, plan, lr=0.02, clip=10.0, eps=1e-3, validate_every=100,
+              patience=400, workspace=None):
+    """Output-matching calibration of the factors L of every head
+    (oal_calibrate).  train, val: (q, k, v) device tensors [T, H, N, d] and
+    [V, H, N, d] of one dtype (heads with their own keys); group_of_dim
+    [H, d] ints; inits [n_init, H, G+1, G+1]; plan [U, 1 + P] ints (per
+    update a training sequence and P distinct positions).  Returns a dict of
+    numpy arrays: "L" [H, G+1, G+1], "mse", "relmse", "init" [H],
+    "cand_mse" and "updates" [n_init, H]."""
+    qt, kt, vt = train
+    qv, kv, vv = val
+    for name, t in (("q_train", qt), ("k_train", kt), ("v_train", vt), ("q_val", qv), ("k_val", kv), ("v_val", vv)):
+        _dev(t, name, qt.dtype, 4)
+    _need(qt.dtype in _DT, "activations must be float32 or bfloat16")
+    T, H, N, d = qt.shape
+    _need(kt.shape == qt.shape and vt.shape[:3] == (T, H, N), "training shapes")
+    _need(qv.shape[1:] == qt.shape[1:] and kv.shape == qv.shape and vv.shape[:3] == qv.shape[:3], "validation shapes")
+    dv = vt.shape[3]
+    n_val = qv.shape[0]
+    g = np.ascontiguousarray(np.asarray(group_of_dim, dtype=np.int32))
+    inits = np.ascontiguousarray(np.asarray(inits, dtype=np.float64))
+    plan = np.ascontiguousarray(np.asarray(plan, dtype=np.int32))
+    n_init, Hi, n, _ = inits.shape
+    G = n - 1
+    _need(Hi == H and g.shape == (H, d), "inits and group map must match the heads")
+    _need(plan.ndim == 2 and plan.shape[1] >= 2, "plan must be [updates, 1 + positions]")
+    P = plan.shape[1] - 1
+    dims = _dims(T, H, H, N, d, dv, G, qt.dtype)
+    gd = torch.from_numpy(g).to(qt.device)
+    nbytes = int(L.lib().oal_calibrate_workspace_bytes(ctypes.byref(dims), n_val, _ptr(gd)))
+    _need(nbytes > 0, "calibration not supported for these shapes")
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=qt.device)
+    prm = L.OalCalibParams(float(lr), float(clip), float(eps), P, int(validate_every), int(patience))
+    L_out = np.zeros((H, n, n))
+    mse, rel = np.zeros(H), np.zeros(H)
+    init = np.zeros(H, np.int32)
+    cand = np.zeros((n_init, H))
+    upd = np.zeros((n_init, H), np.int32)
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = L.lib().oal_calibrate(ctypes.byref(dims), _ptr(qt), _ptr(kt), _ptr(vt), n_val, _ptr(qv), _ptr(kv), _ptr(vv),
+                               _ptr(gd), n_init, vp(inits), plan.shape[0], vp(plan), ctypes.byref(prm), vp(L_out),
+                               vp(mse), vp(rel), vp(init), vp(cand), vp(upd), _ptr(workspace),
+                               ctypes.c_size_t(workspace.numel()), _stream())
+    L.check(st, "oal_calibrate")
+    return {"L": L_out, "mse": mse, "relmse": rel, "init": init, "cand_mse": cand, "updates": upd}
+
+
 class PrefillPlan:
     """Pre-marshalled oal_fwd arguments for repeated calls on fixed buffers.
 

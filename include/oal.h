@@ -20,7 +20,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every array argument is a caller-owned DEVICE pointer unless stated
- *    otherwise.  The library never allocates, frees or synchronises, keeps no
+ *    otherwise.  The library never allocates, frees or synchronises (the one
+ *    exception, oal_calibrate, synchronises its stream and says so), keeps no
  *    global mutable state and is safe to call from several host threads.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and is complete when that stream is synchronised.
@@ -320,6 +321,65 @@ size_t oal_bwd_workspace_bytes(const oal_dims* dims);
 int oal_bwd(const oal_dims* dims, const void* q, const void* k, const void* v, const void* dy,
             const oal_coeffs* coeffs, float* dq, float* dk, float* dv, float* da, float* db, float* dc,
             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Settings of the output-matching calibration (paper, App. B,
+ * "Coefficient-calibration settings": Adam at lr 0.02, gradient norm clipped
+ * at 10, 32 causal query positions per update, validation every 100 updates,
+ * early stop after 400 updates without improvement). */
+typedef struct oal_calib_params {
+  double lr;              /* Adam learning rate (betas 0.9, 0.999, epsilon 1e-8) */
+  double clip;            /* per-head gradient norm bound (> 0) */
+  double eps;             /* the kernel's epsilon of Eq. (7): a = eps + M_00 */
+  int32_t n_positions;    /* P: sampled query positions per update (1..N) */
+  int32_t validate_every; /* updates between validations (>= 1) */
+  int32_t patience;       /* a head stops after this many updates without improvement (>= 1) */
+} oal_calib_params;
+
+/* Bytes of device workspace oal_calibrate needs (0 if invalid or
+ * unsupported); group_of_dim: the device group map the call will use. */
+size_t oal_calibrate_workspace_bytes(const oal_dims* dims, int32_t n_val, const int32_t* group_of_dim);
+
+/* Output-matching calibration of the factors L of every head (paper, App. B,
+ * Eq. (20): L* minimises the squared error between the normalised OAL
+ * outputs and the causal softmax outputs, kappa = eps + sbar^T L L^T sbar as
+ * in oal_coeffs_from_factor), by the coefficient-calibration settings.
+ * For each initialisation candidate c: starting from inits[c], for update
+ * u = 1 .. n_updates the plan row u - 1 names a training sequence s and P
+ * distinct positions i_1 .. i_P; each head takes one Adam step on the lower
+ * triangle of its factor against the gradient of
+ *     (1/P) sum_p || yhat_{i_p}(L; s) - y^softmax_{i_p}(s) ||^2,
+ * its norm first scaled down to clip when larger.  Validation (whole
+ * sequences, before the first update and every validate_every updates)
+ * gives each head's MSE = mean over validation sequences of
+ * ||Yhat_b - Y_b||_F^2 / n_b (n_b = N d_v scalar outputs) and RelMSE = mean
+ * of ||Yhat_b - Y_b||_F^2 / ||Y_b||_F^2; a head keeps its lowest-MSE
+ * checkpoint and stops updating once that is patience updates old.  Finally
+ * every head takes the candidate with the lowest checkpoint MSE.  Heads are
+ * independent problems (their own clipping, stopping and selection).
+ *   dims:     batch = T training sequences of seq_len N; heads with their own
+ *             keys; d_h, d_v, G, dtype as oal_bwd supports them (d_h = 16,
+ *             d_v = 64, G <= 16; otherwise OAL_ERR_UNSUPPORTED).
+ *   q/k/v_train [T, H, N, d], q/k/v_val [n_val, H, N, d]: device, dtype.
+ *   group_of_dim: device [H, d_h] (ids in [0, G)).
+ *   inits:    HOST double [n_init, H, G+1, G+1] (lower triangles read).
+ *   plan:     HOST int32 [n_updates, 1 + P]: sequence in [0, T), then P
+ *             distinct positions in [0, N) (OAL_ERR_INVALID_ARG otherwise).
+ *   outputs (HOST): L_out [H, G+1, G+1] (upper triangle zero), mse_out and
+ *             relmse_out [H] of the chosen checkpoints, init_out [H] the
+ *             chosen candidates; optional (NULL to skip) cand_mse_out
+ *             [n_init, H] and updates_out [n_init, H] (updates each head
+ *             ran).
+ *   workspace: oal_calibrate_workspace_bytes(dims, n_val, group_of_dim).
+ * The optimiser runs on the host in fp32; the targets, forward and backward
+ * passes on the device.  Unlike the other entry points this call is
+ * synchronous: it synchronises `stream` after every update and validation
+ * (its next step depends on the gradients), and returns when it is done. */
+int oal_calibrate(const oal_dims* dims, const void* q_train, const void* k_train, const void* v_train, int32_t n_val,
+                  const void* q_val, const void* k_val, const void* v_val, const int32_t* group_of_dim,
+                  int32_t n_init, const double* inits, int32_t n_updates, const int32_t* plan,
+                  const oal_calib_params* params, double* L_out, double* mse_out, double* relmse_out,
+                  int32_t* init_out, double* cand_mse_out, int32_t* updates_out, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /* ---- dimension grouping (host functions; every pointer below is HOST) ---- */
 

@@ -13,4 +13,5 @@ from .workloads import (  # noqa: F401
     bf16_round,
     make,
     decode_prefix_lengths,
+    calibration_plan,
 )

@@ -244,3 +244,16 @@ def decode_prefix_lengths(n_seq: int, max_len: int = 512, seed: int = 1105) -> n
     """Seeded prefix lengths in [1, max_len] for the batched decode workload."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.integers(1, max_len + 1, size=n_seq).astype(np.int32)
+
+
+def calibration_plan(n_train: int, seq_len: int, n_positions: int, n_updates: int, seed: int = 2200) -> np.ndarray:
+    """Seeded sampling plan of a calibration run: per update, one training
+    sequence and n_positions distinct causal query positions (the pages'
+    settings draw one sequence and 32 positions per update).  int32
+    [n_updates, 1 + n_positions]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    plan = np.zeros((n_updates, 1 + n_positions), dtype=np.int32)
+    for u in range(n_updates):
+        plan[u, 0] = rng.integers(0, n_train)
+        plan[u, 1:] = rng.choice(seq_len, size=n_positions, replace=False)
+    return plan

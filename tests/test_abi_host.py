@@ -245,6 +245,37 @@ def test_bwd_validation_errors(L, no_device):
     assert L.lib().oal_bwd_workspace_bytes(None) == 0
 
 
+def test_calibrate_validation_errors(L, no_device):
+    """oal_calibrate refuses bad shapes, settings and plans before any work."""
+    import numpy as np
+    lib = L.lib()
+    E, U, W = L.OAL_ERR_INVALID_ARG, L.OAL_ERR_UNSUPPORTED, L.OAL_ERR_WORKSPACE
+    G, H, N, P = 2, 2, 40, 4
+    ok = _dims(L, B=3, d=16, Hq=H, Hkv=H, G=G, N=N)
+    inits = np.zeros((1, H, G + 1, G + 1))
+    plan = np.array([[0, 1, 2, 3, 4], [2, 39, 0, 5, 7]], dtype=np.int32)
+    outs = [np.zeros(H * (G + 1) ** 2), np.zeros(H), np.zeros(H), np.zeros(H, np.int32)]
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+
+    def call(dims, plan=plan, prm=None, ws=(FAKE, 1 << 40), n_val=1):
+        prm = prm or L.OalCalibParams(0.02, 10.0, 1e-3, P, 100, 400)
+        return lib.oal_calibrate(ctypes.byref(dims), FAKE, FAKE, FAKE, n_val, FAKE, FAKE, FAKE, FAKE, 1, vp(inits),
+                                 len(plan), vp(plan), ctypes.byref(prm), *[vp(o) for o in outs], None, None,
+                                 ws[0], ctypes.c_size_t(ws[1]), None)
+
+    assert call(_dims(L, B=3, d=64, Hq=H, Hkv=H, G=G, N=N)) == U   # the backward pass is d_h = 16 only
+    assert call(_dims(L, B=3, d=16, Hq=4, Hkv=2, G=G, N=N)) == U   # heads with their own keys
+    assert call(ok, n_val=0) == E
+    assert call(ok, prm=L.OalCalibParams(0.02, 0.0, 1e-3, P, 100, 400)) == E   # clip must be > 0
+    assert call(ok, prm=L.OalCalibParams(0.02, 10.0, 1e-3, N + 1, 100, 400)) == E
+    assert call(ok, plan=np.array([[3, 1, 2, 3, 4]], dtype=np.int32)) == E   # sequence out of range
+    assert call(ok, plan=np.array([[0, 1, 2, 2, 4]], dtype=np.int32)) == E   # repeated position
+    assert call(ok, plan=np.array([[0, 1, 2, 3, 40]], dtype=np.int32)) == E  # position out of range
+    assert call(ok, ws=(None, 0)) == W
+    assert lib.oal_calibrate_workspace_bytes(ctypes.byref(ok), 1, FAKE) > 0
+    assert lib.oal_calibrate_workspace_bytes(ctypes.byref(_dims(L, B=3, d=64, Hq=H, Hkv=H, G=G, N=N)), 1, FAKE) == 0
+
+
 def test_binding_refuses_cpu_tensors(L):
     import torch
     import grouped_quadratic_softmax_amd as oal
