@@ -72,6 +72,14 @@ __device__ __forceinline__ f4 mma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Operands along K: a K-block kb of 16 is taken as four steps e = 0..3 in
+// which lane group g = lane / 16 supplies k = 16 kb + 4 g + e, so an operand
+// stored contiguously along K loads as one 16-byte LDS read per four
+// products, and an accumulator tile (lane group g holds rows 4 g .. 4 g + 3)
+// is, unchanged, the B operand of the K-block it covers.
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float el(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+
 // Feature f of the library's packed order as a pair of indices into the
 // augmented row: f = 0 the constant (16, 16), f = 1 + r the linear term
 // (r, 16), then the pairs r <= t row by row; padding features (17, 17).
@@ -315,10 +323,12 @@ __device__ __forceinline__ void kappa_tile(const Rows& s, float (*kap)[KS], int 
     return;
   }
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* a = &s.phq[16 * rb + i16][g];
-  const float* b = &s.mk[16 * cb + i16][g];
-#pragma unroll 8
-  for (int ks = 0; ks < DP / 4; ++ks) acc = mma(a[4 * ks], b[4 * ks], acc);
+#pragma unroll 5
+  for (int kb = 0; kb < NFB; ++kb) {
+    const float4 a = ld4(&s.phq[16 * rb + i16][16 * kb + 4 * g]), b = ld4(&s.mk[16 * cb + i16][16 * kb + 4 * g]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mma(el(a, e), el(b, e), acc);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = 16 * rb + 4 * g + r, j = 16 * cb + i16;
@@ -337,10 +347,12 @@ __device__ __forceinline__ void dkappa_tile(const Rows& s, const float (&gd4)[4]
     return;
   }
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* a = &s.gg[16 * rb + i16][g];
-  const float* b = &s.u[16 * cb + i16][g];
 #pragma unroll
-  for (int ks = 0; ks < DV / 4; ++ks) acc = mma(a[4 * ks], b[4 * ks], acc);
+  for (int kb = 0; kb < DV / 16; ++kb) {
+    const float4 a = ld4(&s.gg[16 * rb + i16][16 * kb + 4 * g]), b = ld4(&s.u[16 * cb + i16][16 * kb + 4 * g]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mma(el(a, e), el(b, e), acc);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = 16 * rb + 4 * g + r, j = 16 * cb + i16;
@@ -531,11 +543,14 @@ __global__ __launch_bounds__(bw::NT, 1) void bwd16_fwd_kernel(const bw::BwdArgs 
     // kappa; num against S before the chunk
     kappa_tile(R, sh.kap, krb, kcb, lane);
     f4 accY[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 8
-    for (int ks = 0; ks < DP / 4; ++ks) {
-      const float b = sh.st[4 * ks + g][16 * w + i16];
-      accY[0] = mma(R.phq[i16][4 * ks + g], b, accY[0]);
-      accY[1] = mma(R.phq[16 + i16][4 * ks + g], b, accY[1]);
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) {  // B: this wave's columns of S, from its accumulators
+      const float4 a0 = ld4(&R.phq[i16][16 * fb + 4 * g]), a1 = ld4(&R.phq[16 + i16][16 * fb + 4 * g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        accY[0] = mma(el(a0, e), accS[fb][e], accY[0]);
+        accY[1] = mma(el(a1, e), accS[fb][e], accY[1]);
+      }
     }
     __syncthreads();
     // num += kappa U over the chunk; den = Phi z + sum_j kappa_ij
@@ -591,11 +606,15 @@ __global__ __launch_bounds__(bw::NT, 1) void bwd16_fwd_kernel(const bw::BwdArgs 
       f4 acc[5];
 #pragma unroll
       for (int m = 0; m < 5; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int ks = 0; ks < DV / 4; ++ks) {
-        const float a = R.gg[16 * prb + i16][4 * ks + g];
 #pragma unroll
-        for (int m = 0; m < 5; ++m) acc[m] = mma(a, sh.st[16 * ((w >> 1) + 2 * m) + i16][4 * ks + g], acc[m]);
+      for (int cb = 0; cb < DV / 16; ++cb) {
+        const float4 a = ld4(&R.gg[16 * prb + i16][16 * cb + 4 * g]);
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+          const float4 b = ld4(&sh.st[16 * ((w >> 1) + 2 * m) + i16][16 * cb + 4 * g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[m] = mma(el(a, e), el(b, e), acc[m]);
+        }
       }
       for (int ks = 0; ks < 4 * (prb + 1); ++ks) {
         const float a = sh.dkap[16 * prb + i16][4 * ks + g];
@@ -723,11 +742,14 @@ __global__ __launch_bounds__(bw::NT, 1) void bwd16_rev_kernel(const bw::BwdArgs 
     // dL/du = M R + kappa^T G (v columns 16 w ..): dv
     {
       f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 8
-      for (int ks = 0; ks < DP / 4; ++ks) {
-        const float b = sh.st[4 * ks + g][16 * w + i16];
-        acc[0] = mma(R.mk[i16][4 * ks + g], b, acc[0]);
-        acc[1] = mma(R.mk[16 + i16][4 * ks + g], b, acc[1]);
+#pragma unroll
+      for (int fb = 0; fb < NFB; ++fb) {  // B: this wave's columns of R, from its accumulators
+        const float4 a0 = ld4(&R.mk[i16][16 * fb + 4 * g]), a1 = ld4(&R.mk[16 + i16][16 * fb + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[0] = mma(el(a0, e), accR[fb][e], acc[0]);
+          acc[1] = mma(el(a1, e), accR[fb][e], acc[1]);
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < C / 4; ++ks) {
@@ -748,11 +770,15 @@ __global__ __launch_bounds__(bw::NT, 1) void bwd16_rev_kernel(const bw::BwdArgs 
     f4 accK[5];
 #pragma unroll
     for (int m = 0; m < 5; ++m) accK[m] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int ks = 0; ks < DV / 4; ++ks) {
-      const float a = R.u[16 * pjb + i16][4 * ks + g];
 #pragma unroll
-      for (int m = 0; m < 5; ++m) accK[m] = mma(a, sh.st[16 * ((w >> 1) + 2 * m) + i16][4 * ks + g], accK[m]);
+    for (int cb = 0; cb < DV / 16; ++cb) {
+      const float4 a = ld4(&R.u[16 * pjb + i16][16 * cb + 4 * g]);
+#pragma unroll
+      for (int m = 0; m < 5; ++m) {
+        const float4 b = ld4(&sh.st[16 * ((w >> 1) + 2 * m) + i16][16 * cb + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accK[m] = mma(el(a, e), el(b, e), accK[m]);
+      }
     }
     for (int ks = 4 * pjb; ks < C / 4; ++ks) {
       const float a = sh.dkap[4 * ks + g][16 * pjb + i16];
