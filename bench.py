@@ -356,6 +356,7 @@ def run_secondary(args):
     flops = B_ * H_ * N_ * bwd_flops_per_token(16, N_)
     out["f2_based_backward"] = {"ms": ms, "tokens_per_s": B_ * N_ / (ms * 1e-3),
                                 "fp32_mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+                                "traffic": load_traffic("bwd16_based_backward"),
                                 "kernels": "bwd16_segsum_kernel x2, bwd16_fwd_kernel, bwd16_rev_kernel, "
                                            "bwd16_coef_kernel (fp32 MFMA)"}
     del q, k, v, dy, outs, ws
