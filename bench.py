@@ -234,9 +234,8 @@ def run_main(args):
                                "bf16; step = chi + prefill(+final state) + 1 decode token/seq",
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {
-            "kernel": "onepass16p_kernel (oal_fwd prefill at d_h=16 in one launch: two waves per segment, each "
-                      "with half the state's feature tiles; segment sums and outputs of four segments per "
-                      "workgroup, two chained workgroups per sequence)",
+            "kernel": "onepass16w_kernel (oal_fwd prefill at d_h=16 in one launch: segment sums and outputs of "
+                      "four segments per workgroup, two chained workgroups per sequence)",
             "bound": "hbm",
             "achieved": gbs,
             "peak": PEAK_HBM_GBS,

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboal.so")
 
 HIP_SOURCES = ["oal_prefill_d64.hip", "oal_prefill_d32.hip", "oal_prefill_d16.hip", "oal_prefill.hip", "oal_small.hip",
-               "oal_onepass16.hip", "oal_onepass16w.hip", "oal_onepass16p.hip", "oal_dimw.hip", "oal_decode.hip", "oal_contrib.hip", "oal_ceilings.hip", "oal_bwd16.hip",
+               "oal_onepass16.hip", "oal_onepass16w.hip", "oal_dimw.hip", "oal_decode.hip", "oal_contrib.hip", "oal_ceilings.hip", "oal_bwd16.hip",
                "oal_calib.hip"]
 HOST_SOURCES = ["oal_api.cpp", "oal_grouping.cpp"]
 

@@ -85,12 +85,6 @@ int device_cus();
 bool onepass16w_supported(int Hq, int Hkv, bool premap);
 size_t onepass16w_workspace_bytes(int B, int Hkv, int N);
 hipError_t launch_onepass16w(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
-// The same with two waves per segment (the state split by feature tiles):
-// heads with their own keys, no pre-map, up to two groups, four or eight
-// segments per sequence.
-bool onepass16p_supported(const FwdLaunch& a, size_t workspace_bytes);
-size_t onepass16p_workspace_bytes(int B, int Hkv, int N);
-hipError_t launch_onepass16p(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream);
 hipError_t launch_state_passthrough(const float* src, float* dst, long n, hipStream_t stream);
 void decode_slicing(int d_h, long states, int& rows, int& nslice, bool diagonal);
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d_h);

@@ -654,13 +654,10 @@ size_t onepass16_workspace_bytes(int B, int Hq, int Hkv, int N) {
   const int nchunks = (N + CK - 1) / CK;
   const Plan16 pl = plan16(BH, nchunks, (size_t)-1);
   const size_t cta = (size_t)pl.nblk * BH * FT * (DV + 1) * sizeof(float);
-  return onepass16w_supported(Hq, Hkv, false)
-             ? std::max({cta, onepass16w_workspace_bytes(B, Hkv, N), onepass16p_workspace_bytes(B, Hkv, N)})
-             : cta;
+  return onepass16w_supported(Hq, Hkv, false) ? std::max(cta, onepass16w_workspace_bytes(B, Hkv, N)) : cta;
 }
 
 hipError_t launch_onepass16(const FwdLaunch& a, size_t workspace_bytes, hipStream_t stream) {
-  if (onepass16p_supported(a, workspace_bytes)) return launch_onepass16p(a, workspace_bytes, stream);
   if (onepass16w_supported(a.Hq, a.Hkv, a.premap)) return launch_onepass16w(a, workspace_bytes, stream);
   const int BH = a.B * a.Hkv;
   const int nchunks = (a.N + CK - 1) / CK;
