@@ -1,0 +1,93 @@
+"""Bit-reproducibility of the GPU paths: the same inputs give the same bits
+on every call.  Every reduction in the kernels runs in a fixed order, so any
+difference between reruns means a race or a violated hardware hazard (an
+operand overwritten while a matrix product still reads it), which tolerance
+checks against the oracle would not catch.  Each path runs at its
+benchmark size and in the launch configuration the benchmark times."""
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from helpers import gpu_coeffs, gpu_prep, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+RERUNS = 4
+
+
+def _dev(wl):
+    import torch
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    return [torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dt).contiguous() for x in (wl.q, wl.k, wl.v)]
+
+
+def _prefill_reruns(wl, groups=None, staged=False):
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    q, k, v = _dev(wl)
+    co = gpu_coeffs(wl, wl.group_of_dim if groups is None else groups)
+    plan = oal.PrefillPlan(q, k, v, co, gpu_prep(wl), staged=staged)
+    plan.run()
+    torch.cuda.synchronize()
+    y0, s0 = plan.y.clone(), plan.state_out.clone()
+    for r in range(RERUNS):
+        plan.run()
+        torch.cuda.synchronize()
+        ny = int((plan.y != y0).sum())
+        ns = int((plan.state_out != s0).sum())
+        log(f"[repro] {wl.name} rerun {r}: {ny} output and {ns} state elements differ")
+        assert ny == 0 and ns == 0
+
+
+@pytest.mark.parametrize("config", [3, 2, 4])
+def test_prefill_reruns_are_bitwise_equal(config):
+    """The Based prefill (one-wave chained build), the Qwen-shaped GQA layer
+    (chunk scan and readout) and the ReBased prefill (dimension-wise build)."""
+    require_gpu()
+    _prefill_reruns(S.make(config))
+
+
+def test_grouped_query_d16_reruns_are_bitwise_equal():
+    """The d_h = 16 CTA build (grouped-query heads, state split over four
+    waves by feature tiles)."""
+    require_gpu()
+    _prefill_reruns(S.make(3, batch=4, n_q_heads=8, n_kv_heads=2, seq_len=4096))
+
+
+def test_long_prefill_reruns_are_bitwise_equal():
+    """The 32k-token multi-head prefill with eight groups from its
+    contribution scores (chunk build)."""
+    require_gpu()
+    import grouped_quadratic_softmax_amd as oal
+    wl = S.make(5)
+    q, k, _ = _dev(wl)
+    chi = oal.contrib(q, k).cpu().numpy()
+    groups = oal.groups_from_contribution(chi, wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"])
+    _prefill_reruns(wl, groups)
+
+
+def test_decode_reruns_are_bitwise_equal():
+    """The batched decode step (256 sequences x 16 heads, fp32 states) from
+    the same state."""
+    require_gpu()
+    import torch
+    import grouped_quadratic_softmax_amd as oal
+    S_, H, d = 256, 16, 64
+    D = oal.feature_count(d)
+    g = torch.Generator(device="cuda").manual_seed(1205)
+    state0 = torch.rand((S_, H, D * 65), generator=g, device="cuda", dtype=torch.float32)
+    mk = lambda: torch.randn((S_, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    qn, kn, vn = mk(), mk(), mk()
+    groups = ((np.arange(d) * 8) // d)[None, :].repeat(H, 0).astype(np.int32)
+    wl = S.make(5, seq_len=8, batch=1)
+    state = state0.clone()
+    dec = oal.DecodePlan(qn, kn, vn, gpu_coeffs(wl, groups), state)
+    outs = []
+    for _ in range(RERUNS):
+        state.copy_(state0)
+        y = dec.run().clone()
+        torch.cuda.synchronize()
+        outs.append((y, state.clone()))
+    for y, st in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(st, outs[0][1])
