@@ -46,7 +46,10 @@
  *    row-major upper-triangle order.  Entries are the raw moments of Eq. (5):
  *    H[f][l] = sum_j phi_f(k_j) v_jl and z[f] = sum_j phi_f(k_j), with
  *    phi = [1, k_r, k_r k_t]; the packed count is the one of the paper's
- *    App. D (139,425 floats at d_h = d_v = 64).
+ *    App. D (139,425 floats at d_h = d_v = 64).  The dimension-wise form
+ *    (oal_coeffs.diagonal) has the features [1, k_r, k_r^2] only: its calls
+ *    read and write the rows of those (constant, linear terms, squares) and
+ *    leave the rows of the pairs r < t as the buffer holds them.
  *  - Supported shapes: d_h in {16, 32, 64}; d_v = 64; prefill: 1 <= G <= 8
  *    with any group map, or any G <= d_h in the dimension-wise form
  *    (oal_coeffs.diagonal); decode and chi: any G <= d_h.  Others return

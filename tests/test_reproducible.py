@@ -28,16 +28,28 @@ def _prefill_reruns(wl, groups=None, staged=False):
     q, k, v = _dev(wl)
     co = gpu_coeffs(wl, wl.group_of_dim if groups is None else groups)
     plan = oal.PrefillPlan(q, k, v, co, gpu_prep(wl), staged=staged)
-    plan.run()
-    torch.cuda.synchronize()
-    y0, s0 = plan.y.clone(), plan.state_out.clone()
-    for r in range(RERUNS):
+    runs = []
+    for _ in range(RERUNS + 1):
         plan.run()
         torch.cuda.synchronize()
-        ny = int((plan.y != y0).sum())
-        ns = int((plan.state_out != s0).sum())
-        log(f"[repro] {wl.name} rerun {r}: {ny} output and {ns} state elements differ")
-        assert ny == 0 and ns == 0
+        # compared as bits: in the dimension-wise form the state rows outside
+        # its features are left as the buffer held them (possibly NaN)
+        runs.append((plan.y.clone().view(torch.int16), plan.state_out.clone().view(torch.int32)))
+    ok = True
+    for r, (y, st) in enumerate(runs[1:], 1):
+        ny, ds = int((y != runs[0][0]).sum()), st != runs[0][1]
+        if ny or ds.any():
+            ok = False
+            heads = sorted(set((ds.nonzero()[:, 0] * st.shape[1] + ds.nonzero()[:, 1]).tolist()))
+            same_as = [j for j in range(1, len(runs)) if j != r and torch.equal(runs[j][1], st)]
+            log(f"[repro] {wl.name} run {r} vs run 0: {ny} output and {int(ds.sum())} state elements differ, "
+                f"states of (b, h) {heads[:8]}; run {r}'s state equals runs {same_as}")
+            nz = ds.nonzero()[:6].tolist()
+            dv = wl.v.shape[-1]
+            log("[repro]   (b, h, feature row, column, run 0, run r): " + "; ".join(
+                f"({b}, {h}, {i // dv}, {i % dv}, {int(runs[0][1][b, h, i]):#x}, {int(st[b, h, i]):#x})"
+                for b, h, i in nz))
+    assert ok
 
 
 @pytest.mark.parametrize("config", [3, 2, 4])
@@ -88,6 +100,6 @@ def test_decode_reruns_are_bitwise_equal():
         state.copy_(state0)
         y = dec.run().clone()
         torch.cuda.synchronize()
-        outs.append((y, state.clone()))
+        outs.append((y.view(torch.int16), state.clone().view(torch.int32)))
     for y, st in outs[1:]:
         assert torch.equal(y, outs[0][0]) and torch.equal(st, outs[0][1])
