@@ -108,27 +108,13 @@ def time_events(fn, steps, warmup):
     return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps  # ms
 
 
-def settle_clocks(ms=40.0):
-    """About `ms` of the MFMA probe's sustained load: the clocks drop within a
-    second of idling and take tens of milliseconds of load to come back, so
-    every timed region below starts from the level a sustained workload runs
-    at (its own setup on the host can idle the GPU for seconds)."""
-    import ctypes
-    import torch
-    from grouped_quadratic_softmax_amd import _lib as L
-    lib = L.lib()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    out = torch.empty(4096 * 256, device="cuda", dtype=torch.float32)
-    for _ in range(max(1, int(ms / 0.5))):  # about 0.5 ms per probe call
-        L.check(lib.oal_ceiling_mfma(ctypes.c_void_p(out.data_ptr()), 4096, 512, stream), "oal_ceiling_mfma")
-    torch.cuda.synchronize()
-
-
 def settle_with(fn, ms=60.0):
-    """Run `fn` back to back, untimed, for about `ms`.  After the ceiling
-    probes (the MFMA chain draws the chip's full power) the clocks take some
-    tens of milliseconds of a lighter load to climb back: without this the
-    first ~60 steps run about 12% slower than every later one."""
+    """Run `fn` back to back, untimed, for about `ms` before it is timed.
+    The clocks drop within a second of idling (host-side setup between the
+    timed regions does that) and after the ceiling probes (the MFMA chain
+    draws the chip's full power) take some tens of milliseconds of load to
+    climb back: without this the first ~60 steps run about 12% slower than
+    every later one."""
     import torch
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -273,7 +259,7 @@ def run_decode(args):
     groups = ((torch.arange(64) * 8) // 64).repeat(H, 1).numpy()
     wl5 = S.make(5, seq_len=8, batch=1)
     dec = oal.DecodePlan(qd, kd, vd, coeffs_for(wl5, groups), state)
-    settle_clocks()
+    settle_with(dec.run)
     ms = time_events(dec.run, max(10, args.steps), 3)
     nbytes = 2 * S_ * H * D * (DV + 1) * 4 + (3 * S_ * H * 64 + S_ * H * 64) * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -299,7 +285,7 @@ def run_secondary(args):
     q, k, v = (t[:, :, :N].contiguous() for t in (q_all, k_all, v_all))
     qn, kn, vn = (t[:, :, N].contiguous() for t in (q_all, k_all, v_all))
     plan = oal.StepPlan(q, k, v, qn, kn, vn, coeffs_for(wl))
-    settle_clocks()
+    settle_with(plan.run)
     step_ms = time_events(plan.run, steps, warm)
     pre = oal.PrefillPlan(q, k, v, coeffs_for(wl))
     st_ms = time_events(pre.states, steps, warm)
@@ -321,7 +307,7 @@ def run_secondary(args):
     g8 = np.repeat(np.arange(8, dtype=np.int32), 8)[None, :].repeat(wl.n_q_heads, 0)
     pre = oal.PrefillPlan(q, k, v, oal.Coeffs(g8, a8, b8, c8))
     pre.states()
-    settle_clocks()
+    settle_with(pre.outputs)
     ms = time_events(pre.outputs, steps, warm)
     out["c2_gqa_g8_readout"] = {"ms": ms, "mfma_frac": rd_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     del pre, q, k, v, q_all, k_all, v_all
@@ -332,7 +318,7 @@ def run_secondary(args):
     p = wl.premap
     pre = oal.PrefillPlan(q, k, v, coeffs_for(wl),
                           oal.Prep(p["gamma_q"], p["beta_q"], p["gamma_k"], p["beta_k"], p["ln_eps"]))
-    settle_clocks()
+    settle_with(pre.run)
     ms = time_events(pre.run, steps, warm)
     tok = wl.batch * wl.seq_len
     io = tok * wl.n_q_heads * (2 * 64 * 2) + tok * wl.n_kv_heads * (2 * 64 * 2)
@@ -347,7 +333,7 @@ def run_secondary(args):
     chi = oal.contrib(q, k).cpu().numpy()
     groups = oal.groups_from_contribution(chi, wl.group_budget["bulk_sizes"], wl.group_budget["n_tail"])
     pre = oal.PrefillPlan(q, k, v, coeffs_for(wl, groups))
-    settle_clocks()
+    settle_with(pre.run)
     ms = time_events(pre.run, steps, warm)
     tok = wl.batch * wl.seq_len
     flops = tok * 2 * wl.n_q_heads * 2 * D * (DV + 1)
@@ -366,7 +352,7 @@ def run_secondary(args):
             torch.empty((H_,), **f32), torch.empty((H_, 1), **f32), torch.empty((H_, 1, 1), **f32))
     ws = torch.empty(max(oal.bwd_workspace_bytes(B_, H_, N_, 16, DV, 1, q.dtype), 1), dtype=torch.uint8,
                      device="cuda")
-    settle_clocks()
+    settle_with(lambda: oal.bwd(q, k, v, dy, co, workspace=ws, out=outs))
     ms = time_events(lambda: oal.bwd(q, k, v, dy, co, workspace=ws, out=outs), steps, warm)
     flops = B_ * H_ * N_ * bwd_flops_per_token(16, N_)
     out["f2_based_backward"] = {"ms": ms, "tokens_per_s": B_ * N_ / (ms * 1e-3),
