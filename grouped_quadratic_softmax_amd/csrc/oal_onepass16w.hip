@@ -468,9 +468,10 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
     {
       const int nvalid = min(CK, N - c * CK);
       const bool badh = tb.bad != 0 || lost;
-      auto tile = [&](auto TC) __attribute__((always_inline)) {
+      auto tile = [&](auto TC, auto FC) __attribute__((always_inline)) {
         constexpr int T = decltype(TC)::value;
-        if (16 * T >= nvalid) return;
+        constexpr bool full = decltype(FC)::value;  // a whole chunk: no row test
+        if (!full && 16 * T >= nvalid) return;
         // row 16 t + l of a tile (q or k), dims rotated by 4 lg, and the
         // monomials of its features in K-block kb, rows 4 lg + j % 4 of tiles
         // 2 kb + j / 4 (tile 8: pair (l, l + 8) in rows l < 8 (lane rows 0,
@@ -596,11 +597,21 @@ __global__ __launch_bounds__(MODE == kChainedW ? 4 * kWave : kWave, 1) void onep
           }
         }
       };
-      tile(std::integral_constant<int, 0>{});
-      tile(std::integral_constant<int, 1>{});
-      if (c + 1 < c_end) fetch(c + 1, pre, true);
-      tile(std::integral_constant<int, 2>{});
-      tile(std::integral_constant<int, 3>{});
+      // the chunk after this one (the last chunk reloads itself, unused)
+      const int cn = c + 1 < c_end ? c + 1 : c;
+      if (nvalid == CK) {
+        tile(std::integral_constant<int, 0>{}, std::true_type{});
+        tile(std::integral_constant<int, 1>{}, std::true_type{});
+        fetch(cn, pre, true);
+        tile(std::integral_constant<int, 2>{}, std::true_type{});
+        tile(std::integral_constant<int, 3>{}, std::true_type{});
+      } else {
+        tile(std::integral_constant<int, 0>{}, std::false_type{});
+        tile(std::integral_constant<int, 1>{}, std::false_type{});
+        fetch(cn, pre, true);
+        tile(std::integral_constant<int, 2>{}, std::false_type{});
+        tile(std::integral_constant<int, 3>{}, std::false_type{});
+      }
     }
 
     update_chunk(std::true_type{});
