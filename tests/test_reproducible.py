@@ -67,6 +67,13 @@ def test_grouped_query_d16_reruns_are_bitwise_equal():
     _prefill_reruns(S.make(3, batch=4, n_q_heads=8, n_kv_heads=2, seq_len=4096))
 
 
+def test_dimension_wise_grouped_query_reruns_are_bitwise_equal():
+    """The dimension-wise form with grouped-query heads (the small-feature
+    CTA kernel)."""
+    require_gpu()
+    _prefill_reruns(S.make(4, batch=4, n_q_heads=8, n_kv_heads=2, seq_len=2048))
+
+
 def test_long_prefill_reruns_are_bitwise_equal():
     """The 32k-token multi-head prefill with eight groups from its
     contribution scores (chunk build)."""
